@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert layer on one MI355X.
+
+One step = one forward pass of the whole layer over one batch of synthetic tokens already resident
+in HBM: router logits -> top-k/renormalise -> permute -> grouped GEMM + SwiGLU -> grouped GEMM ->
+unpermute/combine, each a call into libmoe_rocm.so on the current stream.
+
+Prints ONE JSON line. `value` is tokens/s of the layer. The timed region is bracketed by
+torch.cuda.synchronize(); HIP events between the calls give each step's per-kernel durations,
+from which the roofline of the dominant kernel (the gate_up grouped GEMM) is computed.
+The CPU baseline is the oracle (C, fp64, OpenMP) timed on a bounded sample of the same tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+METRIC = "MoE layer tokens/s at 1 GPU; grouped-GEMM MFMA util %; permute/combine HBM GB/s"
+KERNEL_SOURCES = ["mixture_experts_layer_renorm_amd/csrc/grouped_gemm.hip",
+                  "mixture_experts_layer_renorm_amd/csrc/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_gemm_gate_up_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def dev(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(wl, d, budget_s: float):
+    """The oracle as it stands on a bounded sample of the workload's tokens: router logits, top-k,
+    then the per-token layer, in chunks until the time budget is used."""
+    import oracle
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    chunk = 32
+    done = 0
+    t0 = time.perf_counter()
+    while done < wl.T and time.perf_counter() - t0 < budget_s:
+        sel = np.arange(done, min(wl.T, done + chunk))
+        xs = d["x"][sel]
+        logits = d["logits"][sel] if "logits" in d else oracle.router_logits(xs, d["w_gate"])
+        idx, w = oracle.router_topk(logits, wl.k, True)
+        oracle.moe_forward_tokens(xs, idx, w, d["gate_up"], d["down"], d.get("shared_gate_up"),
+                                  d.get("shared_down"))
+        done += len(sel)
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of {wl.T} tokens of {wl.name} (router logits + top-k + per-token "
+                      f"SwiGLU experts + combine, fp64), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(the layer's multi-GPU sharding is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_layer_renorm_amd as moe
+    from inputs.workloads import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.load_library()
+    wl = WORKLOADS[args.workload]
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    N = T * k
+    t_gen = time.perf_counter()
+    d = workload_inputs(wl.name)
+    print(f"[bench] {wl.name}: inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    x = dev(d["x"], torch)
+    gate_up = dev(d["gate_up"], torch)
+    down = dev(d["down"], torch)
+    w_gate = dev(d["w_gate"], torch) if "w_gate" in d else None
+    given_logits = dev(d["logits"], torch) if "logits" in d else None
+    tdt = x.dtype
+    bufs = moe.LayerBuffers(T, H, I, E, k, tdt, x.device, logits=given_logits is None)
+    stream = torch.cuda.current_stream()
+
+    names = ["router_logits", "router_topk", "permute", "gemm_gate_up", "gemm_down", "combine"]
+
+    def step(evs=None):
+        def mark(i):
+            if evs is not None:
+                evs[i].record(stream)
+        mark(0)
+        logits = given_logits
+        if logits is None:
+            logits = moe.moe_router_logits(x, w_gate, bufs.logits)
+        mark(1)
+        moe.moe_router_topk(logits, k, True, bufs.topk_idx, bufs.topk_w)
+        mark(2)
+        moe.moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace)
+        mark(3)
+        moe.moe_grouped_gemm_swiglu(bufs.x_perm, gate_up, bufs.plan.offsets, bufs.h)
+        mark(4)
+        moe.moe_grouped_gemm_down(bufs.h, down, bufs.plan.offsets, bufs.y)
+        mark(5)
+        moe.moe_unpermute_combine(bufs.y, bufs.plan.row_of_slot, bufs.topk_w, None, bufs.out)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = np.zeros(6)
+    total_ev = 0.0
+    for evs in events:
+        for i in range(6):
+            seg[i] += evs[i].elapsed_time(evs[i + 1])
+        total_ev += evs[0].elapsed_time(evs[6])
+    seg /= args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, total_ev / args.steps)
+    tokens_per_s = T / (ms_per_step / 1e3)
+
+    counts = bufs.plan.counts.cpu().numpy()
+    n_active = int((counts > 0).sum())
+    b = 2 if tdt == torch.bfloat16 else 4
+    # algorithmic work of each call (what the method must read, write and compute)
+    gu_flops = 2.0 * N * H * 2 * I
+    gu_bytes = n_active * H * 2 * I * b + N * H * b + N * I * b
+    dn_flops = 2.0 * N * I * H
+    dn_bytes = n_active * I * H * b + N * I * b + N * H * b
+    perm_bytes = T * H * b + N * H * b + T * k * 4 * 3 + E * 4 * 2
+    comb_bytes = N * H * b + T * H * b + T * k * 8
+    t_gu, t_dn = seg[3] * 1e-3, seg[4] * 1e-3
+    peak_tf = PEAK_BF16_TFLOPS if tdt == torch.bfloat16 else PEAK_F32_TFLOPS
+    ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if gu_flops / gu_bytes < ridge:
+        roof = {"bound": "hbm", "achieved": round(gu_bytes / t_gu / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gu_flops / t_gu / 1e12, 1), "peak": peak_tf, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = load_traffic(wl.name)
+    roof["kernel"] = "grouped_gemm_bf16_kernel<0> (gate_up + SwiGLU)"
+    roof["algorithmic_bytes"] = gu_bytes
+    roof["algorithmic_flops"] = gu_flops
+    roof["avg_launch_us"] = round(seg[3] * 1e3, 2)
+
+    breakdown = {n: round(seg[i] * 1e3, 2) for i, n in enumerate(names)}
+    if given_logits is not None:
+        breakdown["router_logits"] = 0.0
+    perf = {
+        "kernel_us": breakdown,
+        "grouped_gemm_mfma_util_pct": round(100 * (gu_flops + dn_flops) / (t_gu + t_dn) / (peak_tf * 1e12), 2),
+        "gemm_gate_up_tflops": round(gu_flops / t_gu / 1e12, 1),
+        "gemm_down_tflops": round(dn_flops / t_dn / 1e12, 1),
+        "gemm_gate_up_hbm_gbs": round(gu_bytes / t_gu / 1e9, 1),
+        "gemm_down_hbm_gbs": round(dn_bytes / t_dn / 1e9, 1),
+        "permute_hbm_gbs": round(perm_bytes / (seg[2] * 1e-3) / 1e9, 1),
+        "combine_hbm_gbs": round(comb_bytes / (seg[5] * 1e-3) / 1e9, 1),
+        "active_experts": n_active,
+    }
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if tdt == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "k": k, "renorm": True,
+                   "router": "logits given" if given_logits is not None else "x @ W_g"},
+        "roofline": roof, "perf": perf,
+    }
+    if args.cpu_seconds > 0:
+        print(f"[bench] timing the oracle on the CPU for ~{args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, d, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * moe_rocm.h — C ABI of the MI355X (gfx950) MoE expert layer with renormalised top-k routing.
+ *
+ * The layer (one GPU, forward):
+ *   moe_router_logits -> moe_router_topk -> moe_permute -> moe_grouped_swiglu_ffn -> moe_unpermute_combine
+ *
+ * Sources for what each call computes (web pages on the fused MoE layer):
+ *   [MM]  MindSpeed-MM issue 625, "InternVL3.5 pure FSDP2" practice doc: section 8.2/8.3 (router is
+ *         gate -> FP32 softmax -> top-k -> weight normalisation; experts run permute -> grouped_matmul
+ *         -> SwiGLU -> grouped_matmul -> unpermute), section 2 (fused weights gate_up [E*H, 2*I],
+ *         down [E*I, H]); optimisation doc section 2.1 (experts grouped into one call).
+ *   [DS]  "DeepSeek MoE: EP and FSDP" guide (gsyq.cn): Expert Parallelism section (gate scores,
+ *         expert choice, dispatch, expert compute, gate-weighted sum of the outputs), VeOmni section
+ *         (per-expert token counts; permuted rows expert-major, tokens ascending inside an expert),
+ *         Automodel/DeepEP section (fp32 top-k weights; the dispatch "handle" reused by combine).
+ *   [FT]  LLaMA-Factory "FSDPTurbo EP/EFSDP" design note, section 3 (the fused dispatcher's device
+ *         permute / grouped matmul / unpermute; empty experts must be handled).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host". The caller allocates and owns every buffer;
+ *     the library never allocates, frees, synchronises or copies to the host on these paths.
+ *   - Every call only enqueues kernels on `stream` (0 = the null stream) and returns; results are
+ *     ready when the stream reaches them.
+ *   - Tensors are contiguous and row-major. bf16 data is raw bfloat16 (16-bit) storage.
+ *     Routing weights are always fp32; indices and row maps are int32.
+ *   - Sizes: T, H, I, N >= 0 (a zero size enqueues nothing); 1 <= E <= 1024; 1 <= k <= min(E, 32).
+ *     The bf16 grouped FFN needs H and I to be multiples of 8 and 16-byte aligned buffers.
+ *   - Results are bitwise deterministic run to run (no floating-point atomics).
+ *   - Errors: a moe_status is returned; arguments are checked on the host before any launch and a
+ *     failed check enqueues nothing. moe_last_error() gives the calling thread's last message.
+ *     A launch failure reports MOE_ERR_HIP. Nothing aborts and nothing falls back silently.
+ *     Device-side values (indices, offsets) are not checked on the host; the kernels stay in bounds
+ *     for any values (see each call).
+ */
+#ifndef MOE_ROCM_H
+#define MOE_ROCM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned buffer */
+  MOE_ERR_UNSUPPORTED = 2, /* legal request this build does not implement (e.g. H % 8 != 0 in bf16) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Message for the calling thread's last non-OK status ("" if none). Never NULL. */
+const char* moe_last_error(void);
+
+/* Version of this ABI (incremented on incompatible change). */
+int moe_abi_version(void);
+
+/* ---- (1) router logits -------------------------------------------------------------------------
+ * [MM 8.2/8.3] the gate: logits = x @ w_gate, consumed by the FP32 softmax.
+ * logits[t, e] = acc after `acc = fmaf(x[t,h], w_gate[h,e], acc)` for h = 0..H-1 from acc = 0 (fp32,
+ * IEEE fused multiply-add, hidden dimension ascending) — a fixed order so that the top-k decision is
+ * reproducible bit for bit.
+ *   x      [T, H]  dt       w_gate [H, E] dt       logits [T, E] fp32 (output)                       */
+moe_status moe_router_logits(const void* x, const void* w_gate, moe_dtype dt, int T, int H, int E,
+                             float* logits, hipStream_t stream);
+
+/* ---- (2) softmax -> top-k -> renormalise ---------------------------------------------------------
+ * [MM 8.2/8.3] FP32 softmax, top-k, weight normalisation; [DS Automodel] fp32 top-k weights.
+ * Selection: the k largest logits (softmax is monotone), ties to the lower expert index; slot j holds
+ * the j-th largest. With m = max_e logits[t, e]:
+ *   renorm = 1:  topk_w[t, j] = exp(l_j - m) / sum_{i selected} exp(l_i - m)   (sums to 1)
+ *   renorm = 0:  topk_w[t, j] = exp(l_j - m) / sum_{all e} exp(l_e - m)        (raw probability)
+ *   logits [T, E] fp32 (finite)     topk_idx [T, k] int32 (out)     topk_w [T, k] fp32 (out)        */
+moe_status moe_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                           float* topk_w, hipStream_t stream);
+
+/* ---- (3) permute ----------------------------------------------------------------------------------
+ * [DS VeOmni] group the N = T*k rows by expert: counts[e] = #slots choosing e, offsets = exclusive
+ * scan (offsets[E] = number of valid slots), rows ordered by (expert, token) ascending:
+ *   row_of_slot[t*k + j] = row of slot j of token t,  slot_of_row[row] = t*k + j,
+ *   x_perm[row, :] = x[t, :]  (bit copy).
+ * Slots whose index is outside [0, E) get no row: row_of_slot = -1, they are not counted.
+ *   x [T, H] dt; topk_idx [T, k] int32; x_perm [T*k, H] dt (out); counts [E], offsets [E+1],
+ *   row_of_slot [T*k], slot_of_row [T*k] int32 (out); workspace: device scratch of at least
+ *   moe_permute_workspace_bytes(T, k, E) bytes (contents need no initialisation).
+ * The (counts, offsets, row_of_slot) triple is the layout handle that the FFN and combine take.  */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t* topk_idx, int k, int E,
+                       void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                       int32_t* slot_of_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- (4) grouped SwiGLU expert FFN -----------------------------------------------------------------
+ * [MM 2, 8.3; opt. 2.1] for each expert e with rows [offsets[e], offsets[e+1]) of x_perm:
+ *   g = x_perm[r] @ gate_up[e*H:(e+1)*H, 0:I],  u = x_perm[r] @ gate_up[e*H:(e+1)*H, I:2I],
+ *   h[r] = silu(g) * u  (silu(z) = z / (1 + exp(-z))),   y[r] = h[r] @ down[e*I:(e+1)*I, :].
+ * fp32 accumulation; in bf16, h is stored as bf16 between the two matmuls and y is rounded once.
+ * Experts with no rows cost nothing. Rows outside [offsets[0], offsets[E]) are left untouched.
+ *   x_perm [N, H] dt; gate_up [E*H, 2*I] dt; down [E*I, H] dt; expert_offsets [E+1] int32 (device,
+ *   non-decreasing, offsets[E] <= N); h [N, I] dt (out, scratch for the caller); gu_saved [N, 2*I] dt
+ *   (out, optional: the pre-activations g | u, kept for a backward pass; may be NULL); y [N, H] dt (out).
+ * A shared expert is the same call with E = 1 and expert_offsets = {0, T}.                        */
+moe_status moe_grouped_swiglu_ffn(const void* x_perm, const void* gate_up, const void* down, moe_dtype dt,
+                                  int N, int H, int I, int E, const int32_t* expert_offsets, void* h,
+                                  void* gu_saved, void* y, hipStream_t stream);
+
+/* The two halves of moe_grouped_swiglu_ffn, same arguments and rules:
+ *   moe_grouped_gemm_swiglu: the first grouped matmul with SwiGLU fused in its epilogue -> h (+ gu_saved);
+ *   moe_grouped_gemm_down:   the second grouped matmul h @ down_e -> y.
+ * moe_grouped_swiglu_ffn(...) == moe_grouped_gemm_swiglu(...) then moe_grouped_gemm_down(...).        */
+moe_status moe_grouped_gemm_swiglu(const void* x_perm, const void* gate_up, moe_dtype dt, int N, int H, int I,
+                                   int E, const int32_t* expert_offsets, void* h, void* gu_saved,
+                                   hipStream_t stream);
+moe_status moe_grouped_gemm_down(const void* h, const void* down, moe_dtype dt, int N, int H, int I, int E,
+                                 const int32_t* expert_offsets, void* y, hipStream_t stream);
+
+/* ---- (5) unpermute + gate-weighted combine ---------------------------------------------------------
+ * [DS Expert Parallelism] weighted sum of the expert outputs by the gate weights; [MM 8.3] unpermute.
+ *   out[t] = residual[t] + sum_{j<k} topk_w[t, j] * y[row_of_slot[t*k + j]]   (fp32, j ascending,
+ *   rounded once to dt; slots with row_of_slot < 0 are skipped; residual may be NULL).
+ *   y [N, H] dt with N > every row_of_slot entry; topk_w [T, k] fp32; residual, out [T, H] dt.   */
+moe_status moe_unpermute_combine(const void* y, moe_dtype dt, int T, int H, int k, const int32_t* row_of_slot,
+                                 const float* topk_w, const void* residual, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_ROCM_H */

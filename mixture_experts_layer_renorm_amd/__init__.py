@@ -1,0 +1,260 @@
+"""MI355X (gfx950) MoE expert layer with renormalised top-k routing — Python binding.
+
+Thin ctypes marshalling over the C ABI of libmoe_rocm.so (declared in include/moe_rocm.h). Every
+step of the layer runs in the library's HIP kernels; PyTorch only provides device memory and the
+current stream. There is no fallback: if the library is missing or a call fails, this raises.
+
+The functions carry the ABI's names and take torch tensors on the GPU. Output tensors may be
+passed in (they are then written in place) or are allocated here with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_rocm.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "moe_rocm.h")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmoe_rocm.so (built in-tree by build.py). Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run mixture_experts_layer_renorm_amd/build.py "
+                              "(or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "moe_last_error": (ctypes.c_char_p, []),
+            "moe_abi_version": (I, []),
+            "moe_router_logits": (I, [P, P, I, I, I, I, P, P]),
+            "moe_router_topk": (I, [P, I, I, I, I, P, P, P]),
+            "moe_permute_workspace_bytes": (Z, [I, I, I]),
+            "moe_permute": (I, [P, I, I, I, P, I, I, P, P, P, P, P, P, Z, P]),
+            "moe_grouped_swiglu_ffn": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P]),
+            "moe_grouped_gemm_swiglu": (I, [P, P, I, I, I, I, I, P, P, P, P]),
+            "moe_grouped_gemm_down": (I, [P, P, I, I, I, I, I, P, P, P]),
+            "moe_unpermute_combine": (I, [P, I, I, I, I, P, P, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/moe_rocm.h."""
+    with open(HEADER) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(moe_\w+)\s*\(", src, re.M)))
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, load_library().moe_last_error().decode() or what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t, what, dtype=None, shape=None):
+    if t is None or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous CUDA tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+# ---- the ABI calls ----------------------------------------------------------------------------
+def moe_router_logits(x, w_gate, logits=None, stream=None):
+    T, H = x.shape
+    E = w_gate.shape[1]
+    _need(x, "x"), _need(w_gate, "w_gate", x.dtype, (H, E))
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _need(logits, "logits", torch.float32, (T, E))
+    _check(load_library().moe_router_logits(_ptr(x), _ptr(w_gate), _dt(x), T, H, E, _ptr(logits), _stream(stream)),
+           "moe_router_logits")
+    return logits
+
+
+def moe_router_topk(logits, k, renorm=True, topk_idx=None, topk_w=None, stream=None):
+    T, E = logits.shape
+    _need(logits, "logits", torch.float32)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k)), _need(topk_w, "topk_w", torch.float32, (T, k))
+    _check(load_library().moe_router_topk(_ptr(logits), T, E, k, int(bool(renorm)), _ptr(topk_idx), _ptr(topk_w),
+                                          _stream(stream)), "moe_router_topk")
+    return topk_idx, topk_w
+
+
+def moe_permute_workspace_bytes(T, k, E):
+    return int(load_library().moe_permute_workspace_bytes(T, k, E))
+
+
+class Plan:
+    """The permute's layout handle: counts, offsets, row_of_slot, slot_of_row (all int32, device)."""
+
+    def __init__(self, counts, offsets, row_of_slot, slot_of_row):
+        self.counts, self.offsets, self.row_of_slot, self.slot_of_row = counts, offsets, row_of_slot, slot_of_row
+
+
+def moe_permute(x, topk_idx, E, x_perm=None, plan=None, workspace=None, stream=None):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    _need(x, "x"), _need(topk_idx, "topk_idx", torch.int32, (T, k))
+    dev = x.device
+    N = T * k
+    if x_perm is None:
+        x_perm = torch.empty((N, H), dtype=x.dtype, device=dev)
+    if plan is None:
+        plan = Plan(torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+                    torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev))
+    ws_bytes = moe_permute_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(load_library().moe_permute(_ptr(x), _dt(x), T, H, _ptr(topk_idx), k, E, _ptr(x_perm), _ptr(plan.counts),
+                                      _ptr(plan.offsets), _ptr(plan.row_of_slot), _ptr(plan.slot_of_row),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_permute")
+    return x_perm, plan
+
+
+def moe_grouped_swiglu_ffn(x_perm, gate_up, down, expert_offsets, h=None, y=None, gu_saved=None, stream=None):
+    N, H = x_perm.shape
+    I = down.shape[0] // (gate_up.shape[0] // H)
+    E = gate_up.shape[0] // H
+    _need(x_perm, "x_perm"), _need(gate_up, "gate_up", x_perm.dtype, (E * H, 2 * I))
+    _need(down, "down", x_perm.dtype, (E * I, H)), _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    if h is None:
+        h = torch.empty((N, I), dtype=x_perm.dtype, device=x_perm.device)
+    if y is None:
+        y = torch.empty((N, H), dtype=x_perm.dtype, device=x_perm.device)
+    _need(h, "h", x_perm.dtype, (N, I)), _need(y, "y", x_perm.dtype, (N, H))
+    if gu_saved is not None:
+        _need(gu_saved, "gu_saved", x_perm.dtype, (N, 2 * I))
+    _check(load_library().moe_grouped_swiglu_ffn(_ptr(x_perm), _ptr(gate_up), _ptr(down), _dt(x_perm), N, H, I, E,
+                                                 _ptr(expert_offsets), _ptr(h), _ptr(gu_saved), _ptr(y),
+                                                 _stream(stream)), "moe_grouped_swiglu_ffn")
+    return y, h
+
+
+def moe_grouped_gemm_swiglu(x_perm, gate_up, expert_offsets, h=None, gu_saved=None, stream=None):
+    N, H = x_perm.shape
+    E = gate_up.shape[0] // H
+    I = gate_up.shape[1] // 2
+    _need(x_perm, "x_perm"), _need(gate_up, "gate_up", x_perm.dtype, (E * H, 2 * I))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    if h is None:
+        h = torch.empty((N, I), dtype=x_perm.dtype, device=x_perm.device)
+    _need(h, "h", x_perm.dtype, (N, I))
+    if gu_saved is not None:
+        _need(gu_saved, "gu_saved", x_perm.dtype, (N, 2 * I))
+    _check(load_library().moe_grouped_gemm_swiglu(_ptr(x_perm), _ptr(gate_up), _dt(x_perm), N, H, I, E,
+                                                  _ptr(expert_offsets), _ptr(h), _ptr(gu_saved), _stream(stream)),
+           "moe_grouped_gemm_swiglu")
+    return h
+
+
+def moe_grouped_gemm_down(h, down, expert_offsets, y=None, stream=None):
+    N, I = h.shape
+    E = expert_offsets.shape[0] - 1
+    H = down.shape[1]
+    _need(h, "h"), _need(down, "down", h.dtype, (E * I, H)), _need(expert_offsets, "expert_offsets", torch.int32)
+    if y is None:
+        y = torch.empty((N, H), dtype=h.dtype, device=h.device)
+    _need(y, "y", h.dtype, (N, H))
+    _check(load_library().moe_grouped_gemm_down(_ptr(h), _ptr(down), _dt(h), N, H, I, E, _ptr(expert_offsets),
+                                                _ptr(y), _stream(stream)), "moe_grouped_gemm_down")
+    return y
+
+
+def moe_unpermute_combine(y, row_of_slot, topk_w, residual=None, out=None, stream=None):
+    T, k = topk_w.shape
+    H = y.shape[1]
+    _need(y, "y"), _need(row_of_slot, "row_of_slot", torch.int32), _need(topk_w, "topk_w", torch.float32)
+    if row_of_slot.numel() != T * k:
+        raise ValueError("row_of_slot must hold T*k entries")
+    if residual is not None:
+        _need(residual, "residual", y.dtype, (T, H))
+    if out is None:
+        out = torch.empty((T, H), dtype=y.dtype, device=y.device)
+    _need(out, "out", y.dtype, (T, H))
+    _check(load_library().moe_unpermute_combine(_ptr(y), _dt(y), T, H, k, _ptr(row_of_slot), _ptr(topk_w),
+                                                _ptr(residual), _ptr(out), _stream(stream)), "moe_unpermute_combine")
+    return out
+
+
+# ---- the layer: the five calls in order on one stream ---------------------------------------------
+class LayerBuffers:
+    """Device buffers of one layer call, allocated once and reused (no allocation in the timed path)."""
+
+    def __init__(self, T, H, I, E, k, dtype, device, logits=True, gu_saved=False):
+        N = T * k
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device) if logits else None
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.x_perm = torch.empty((N, H), dtype=dtype, device=device)
+        self.plan = Plan(torch.empty(E, dtype=torch.int32, device=device),
+                         torch.empty(E + 1, dtype=torch.int32, device=device),
+                         torch.empty(N, dtype=torch.int32, device=device),
+                         torch.empty(N, dtype=torch.int32, device=device))
+        self.workspace = torch.empty(max(moe_permute_workspace_bytes(T, k, E), 1), dtype=torch.uint8, device=device)
+        self.h = torch.empty((N, I), dtype=dtype, device=device)
+        self.gu_saved = torch.empty((N, 2 * I), dtype=dtype, device=device) if gu_saved else None
+        self.y = torch.empty((N, H), dtype=dtype, device=device)
+        self.out = torch.empty((T, H), dtype=dtype, device=device)
+
+
+def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True, residual=None, bufs=None,
+                      stream=None):
+    """Router (logits unless given) -> top-k -> permute -> grouped SwiGLU FFN -> combine."""
+    T, H = x.shape
+    E = gate_up.shape[0] // H
+    I = gate_up.shape[1] // 2
+    if bufs is None:
+        bufs = LayerBuffers(T, H, I, E, k, x.dtype, x.device, logits=logits is None)
+    if logits is None:
+        logits = moe_router_logits(x, w_gate, bufs.logits, stream)
+    moe_router_topk(logits, k, renorm, bufs.topk_idx, bufs.topk_w, stream)
+    moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace, stream)
+    moe_grouped_swiglu_ffn(bufs.x_perm, gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, bufs.gu_saved, stream)
+    moe_unpermute_combine(bufs.y, bufs.plan.row_of_slot, bufs.topk_w, residual, bufs.out, stream)
+    return bufs.out, bufs

@@ -1,0 +1,170 @@
+// C ABI of the MoE layer library: host-side validation, then the kernel launchers.
+#include "moe_rocm.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool bad_dt(moe_dtype dt) { return dt != MOE_F32 && dt != MOE_BF16; }
+bool misaligned16(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_abi_version(void) { return 1; }
+
+moe_status moe_router_logits(const void* x, const void* w_gate, moe_dtype dt, int T, int H, int E, float* logits,
+                             hipStream_t stream) {
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "moe_router_logits: unknown dtype %d", (int)dt);
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_ARG, "moe_router_logits: T=%d H=%d must be >= 0", T, H);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "moe_router_logits: E=%d outside [1, %d]", E, kMaxE);
+  if (T == 0) return ok();
+  REQUIRE(x && w_gate && logits, MOE_ERR_INVALID_ARG, "moe_router_logits: null pointer");
+  return hip_status(moe::launch_router_logits(x, w_gate, (int)dt, T, H, E, logits, stream), "moe_router_logits");
+}
+
+moe_status moe_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx, float* topk_w,
+                           hipStream_t stream) {
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "moe_router_topk: T=%d must be >= 0", T);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "moe_router_topk: E=%d outside [1, %d]", E, kMaxE);
+  REQUIRE(k >= 1 && k <= E && k <= kMaxK, MOE_ERR_INVALID_ARG, "moe_router_topk: k=%d outside [1, min(E=%d, %d)]", k,
+          E, kMaxK);
+  REQUIRE(renorm == 0 || renorm == 1, MOE_ERR_INVALID_ARG, "moe_router_topk: renorm=%d must be 0 or 1", renorm);
+  if (T == 0) return ok();
+  REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG, "moe_router_topk: null pointer");
+  return hip_status(moe::launch_router_topk(logits, T, E, k, renorm, topk_idx, topk_w, stream), "moe_router_topk");
+}
+
+size_t moe_permute_workspace_bytes(int T, int k, int E) {
+  (void)k;
+  if (T <= 0 || E <= 0) return 0;
+  return moe::permute_workspace_bytes(T, E);
+}
+
+moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
+                       int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "moe_permute: unknown dtype %d", (int)dt);
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_ARG, "moe_permute: T=%d H=%d must be >= 0", T, H);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "moe_permute: E=%d outside [1, %d]", E, kMaxE);
+  REQUIRE(k >= 1 && k <= E && k <= kMaxK, MOE_ERR_INVALID_ARG, "moe_permute: k=%d outside [1, min(E=%d, %d)]", k, E,
+          kMaxK);
+  REQUIRE((int64_t)T * k <= 0x7fffffffLL, MOE_ERR_INVALID_ARG, "moe_permute: T*k overflows int32");
+  REQUIRE(counts && offsets, MOE_ERR_INVALID_ARG, "moe_permute: null counts/offsets");
+  if (T == 0) {
+    // nothing routed: counts = 0, offsets = 0 are still produced (a fill kernel, safe in a captured graph)
+    hipError_t e = moe::launch_fill_i32(counts, E, 0, stream);
+    if (e == hipSuccess) e = moe::launch_fill_i32(offsets, E + 1, 0, stream);
+    return hip_status(e, "moe_permute");
+  }
+  REQUIRE(x && topk_idx && x_perm && row_of_slot && slot_of_row, MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+  const size_t need = moe::permute_workspace_bytes(T, E);
+  REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "moe_permute: workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
+  return hip_status(moe::launch_permute(x, (int)dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot,
+                                        slot_of_row, (int32_t*)workspace, stream),
+                    "moe_permute");
+}
+
+namespace {
+moe_status check_ffn(const char* fn, moe_dtype dt, int N, int H, int I, int E) {
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  REQUIRE(N >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_ARG, "%s: N=%d H=%d I=%d out of range", fn, N, H, I);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (dt == MOE_BF16)
+    REQUIRE(H % 8 == 0 && I % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: bf16 needs H and I multiples of 8 (H=%d I=%d)", fn, H,
+            I);
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_grouped_gemm_swiglu(const void* x_perm, const void* gate_up, moe_dtype dt, int N, int H, int I, int E,
+                                   const int32_t* expert_offsets, void* h, void* gu_saved, hipStream_t stream) {
+  const char* fn = "moe_grouped_gemm_swiglu";
+  moe_status st = check_ffn(fn, dt, N, H, I, E);
+  if (st != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE(x_perm && gate_up && expert_offsets && h, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (dt == MOE_BF16)
+    REQUIRE(!misaligned16(x_perm) && !misaligned16(gate_up) && !misaligned16(h) && !misaligned16(gu_saved),
+            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
+  return hip_status(moe::launch_gemm_gate_up(x_perm, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream),
+                    fn);
+}
+
+moe_status moe_grouped_gemm_down(const void* h, const void* down, moe_dtype dt, int N, int H, int I, int E,
+                                 const int32_t* expert_offsets, void* y, hipStream_t stream) {
+  const char* fn = "moe_grouped_gemm_down";
+  moe_status st = check_ffn(fn, dt, N, H, I, E);
+  if (st != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE(h && down && expert_offsets && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (dt == MOE_BF16)
+    REQUIRE(!misaligned16(h) && !misaligned16(down) && !misaligned16(y), MOE_ERR_INVALID_ARG,
+            "%s: bf16 buffers must be 16-byte aligned", fn);
+  return hip_status(moe::launch_gemm_down(h, down, (int)dt, N, H, I, E, expert_offsets, y, stream), fn);
+}
+
+moe_status moe_grouped_swiglu_ffn(const void* x_perm, const void* gate_up, const void* down, moe_dtype dt, int N, int H,
+                                  int I, int E, const int32_t* expert_offsets, void* h, void* gu_saved, void* y,
+                                  hipStream_t stream) {
+  const char* fn = "moe_grouped_swiglu_ffn";
+  moe_status st = check_ffn(fn, dt, N, H, I, E);
+  if (st != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE(x_perm && gate_up && down && expert_offsets && h && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (dt == MOE_BF16)
+    REQUIRE(!misaligned16(x_perm) && !misaligned16(gate_up) && !misaligned16(down) && !misaligned16(h) &&
+                !misaligned16(y) && !misaligned16(gu_saved),
+            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
+  hipError_t e = moe::launch_gemm_gate_up(x_perm, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream);
+  if (e == hipSuccess) e = moe::launch_gemm_down(h, down, (int)dt, N, H, I, E, expert_offsets, y, stream);
+  return hip_status(e, fn);
+}
+
+moe_status moe_unpermute_combine(const void* y, moe_dtype dt, int T, int H, int k, const int32_t* row_of_slot,
+                                 const float* topk_w, const void* residual, void* out, hipStream_t stream) {
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "moe_unpermute_combine: unknown dtype %d", (int)dt);
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_ARG, "moe_unpermute_combine: T=%d H=%d must be >= 0", T, H);
+  REQUIRE(k >= 1 && k <= kMaxK, MOE_ERR_INVALID_ARG, "moe_unpermute_combine: k=%d outside [1, %d]", k, kMaxK);
+  if (T == 0 || H == 0) return ok();
+  REQUIRE(y && row_of_slot && topk_w && out, MOE_ERR_INVALID_ARG, "moe_unpermute_combine: null pointer");
+  return hip_status(moe::launch_combine(y, (int)dt, T, H, k, row_of_slot, topk_w, residual, out, stream),
+                    "moe_unpermute_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Kernel launchers behind the C ABI. Each enqueues on the given stream and returns
+// hipGetLastError() after the launch. Arguments are validated by the ABI layer beforehand.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum { kF32 = 0, kBF16 = 1 };
+
+inline size_t dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
+
+// router.hip
+hipError_t launch_router_logits(const void* x, const void* w_gate, int dt, int T, int H, int E, float* logits,
+                                hipStream_t s);
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w,
+                              hipStream_t s);
+
+// permute.hip
+constexpr int kPermuteChunk = 256;  // tokens per plan chunk
+inline int permute_nchunks(int T) { return (T + kPermuteChunk - 1) / kPermuteChunk; }
+inline size_t permute_workspace_bytes(int T, int E) { return (size_t)permute_nchunks(T) * (size_t)E * sizeof(int32_t); }
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
+                          int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,
+                          int32_t* chunk_counts, hipStream_t s);
+
+// grouped_gemm.hip
+hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, int N, int H, int I, int E,
+                               const int32_t* offsets, void* h, void* gu_saved, hipStream_t s);
+hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int H, int I, int E, const int32_t* offsets,
+                            void* y, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void* y, int dt, int T, int H, int k, const int32_t* row_of_slot, const float* topk_w,
+                          const void* residual, void* out, hipStream_t s);
+
+}  // namespace moe

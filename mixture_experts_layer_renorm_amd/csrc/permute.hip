@@ -1,0 +1,167 @@
+// Token permute: group the T*k (token, slot) rows by expert.
+//
+// Row order follows the VeOmni walk-through of the "DeepSeek MoE: EP and FSDP" guide (gsyq.cn):
+// the permuted buffer holds expert 0's rows first, then expert 1's, and inside an expert the
+// tokens stay in ascending order; per-expert counts come from summing the routing mask.
+//
+// Three kernels, no host synchronisation and no atomics that decide an order:
+//  1. count : per chunk of 256 tokens, an LDS histogram of the chunk's expert choices.
+//  2. plan  : per chunk, global bases = exclusive scan over experts of the totals + the counts of
+//             earlier chunks; in-chunk ranks from per-expert token bitmaps (popcount of the
+//             tokens before this one). Writes counts, offsets, row_of_slot, slot_of_row.
+//  3. scatter: one wave per token copies x[t] (read once) to its k rows of x_perm.
+// Slots whose expert index is outside [0, E) get no row (row_of_slot = -1).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int kPlanThreads = 256;
+constexpr int kMaxE = 1024;
+constexpr int kMaskWords = kPermuteChunk / 32;
+
+__global__ __launch_bounds__(kPlanThreads) void permute_count_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                                     int E, int32_t* __restrict__ chunk_counts) {
+  __shared__ int cnt[kMaxE];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) cnt[e] = 0;
+  __syncthreads();
+  const int64_t s0 = (int64_t)c * kPermuteChunk * k;
+  const int64_t s1 = (int64_t)min(T, (c + 1) * kPermuteChunk) * k;
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += kPlanThreads) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) chunk_counts[(int64_t)c * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(kPlanThreads) void permute_plan_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, const int32_t* __restrict__ chunk_counts, int nchunks,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of_slot,
+    int32_t* __restrict__ slot_of_row) {
+  __shared__ int scan[kMaxE + 1];
+  __shared__ int base[kMaxE];
+  __shared__ uint32_t mask[kMaxE * kMaskWords];
+  __shared__ int wave_tot[kPlanThreads / kWave];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
+    int tot = 0, before = 0;
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int v = chunk_counts[(int64_t)cc * E + e];
+      tot += v;
+      if (cc < c) before += v;
+    }
+    scan[e] = tot;
+    base[e] = before;
+  }
+  for (int i = threadIdx.x; i < E * kMaskWords; i += kPlanThreads) mask[i] = 0u;
+  __syncthreads();
+  if (c == 0)
+    for (int e = threadIdx.x; e < E; e += kPlanThreads) counts[e] = scan[e];
+  block_exclusive_scan<kPlanThreads>(scan, E, wave_tot);
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
+    base[e] += scan[e];
+    if (c == 0) offsets[e] = scan[e];
+  }
+  if (c == 0 && threadIdx.x == 0) offsets[E] = scan[E];
+
+  const int t0 = c * kPermuteChunk;
+  const int64_t s0 = (int64_t)t0 * k;
+  const int64_t s1 = (int64_t)min(T, t0 + kPermuteChunk) * k;
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += kPlanThreads) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) {
+      const int tl = (int)(s / k) - t0;
+      atomicOr(&mask[e * kMaskWords + (tl >> 5)], 1u << (tl & 31));
+    }
+  }
+  __syncthreads();
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += kPlanThreads) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) {
+      const int tl = (int)(s / k) - t0;
+      const uint32_t* m = mask + e * kMaskWords;
+      int rank = 0;
+      for (int w = 0; w < (tl >> 5); ++w) rank += __popc(m[w]);
+      rank += __popc(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
+      const int row = base[e] + rank;
+      row_of_slot[s] = row;
+      slot_of_row[row] = (int32_t)s;
+    } else {
+      row_of_slot[s] = -1;
+    }
+  }
+}
+
+// One wave per token; 16-byte vectors when rows allow it, 2-byte units otherwise.
+constexpr int kScatterWaves = 4;
+constexpr int kMaxK = 32;
+
+__global__ __launch_bounds__(kScatterWaves * kWave) void permute_scatter_kernel(
+    const uint8_t* __restrict__ x, int T, int64_t row_bytes, int k, const int32_t* __restrict__ row_of_slot,
+    uint8_t* __restrict__ x_perm, int vec16) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * kScatterWaves + (int)(threadIdx.x / kWave);
+  if (t >= T) return;
+  const int my_row = lane < k ? row_of_slot[(int64_t)t * k + lane] : -1;
+  const uint8_t* src = x + (int64_t)t * row_bytes;
+  if (vec16) {
+    const int64_t nvec = row_bytes >> 4;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    for (int64_t v0 = 0; v0 < nvec; v0 += 4 * kWave) {
+      uint4 buf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + u * kWave + lane;
+        if (v < nvec) buf[u] = s4[v];
+      }
+      for (int j = 0; j < k; ++j) {
+        const int r = __shfl(my_row, j, kWave);
+        if (r < 0) continue;
+        uint4* d4 = reinterpret_cast<uint4*>(x_perm + (int64_t)r * row_bytes);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t v = v0 + u * kWave + lane;
+          if (v < nvec) d4[v] = buf[u];
+        }
+      }
+    }
+  } else {
+    const int64_t n16 = row_bytes >> 1;
+    const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
+    for (int64_t i = lane; i < n16; i += kWave) {
+      const uint16_t v = s2[i];
+      for (int j = 0; j < k; ++j) {
+        const int r = __shfl(my_row, j, kWave);
+        if (r >= 0) reinterpret_cast<uint16_t*>(x_perm + (int64_t)r * row_bytes)[i] = v;
+      }
+    }
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
+                          int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,
+                          int32_t* chunk_counts, hipStream_t s) {
+  const int nchunks = permute_nchunks(T);
+  const int64_t row_bytes = (int64_t)H * (int64_t)dtype_bytes(dt);
+  const int vec16 = (row_bytes % 16 == 0) && (((uintptr_t)x | (uintptr_t)x_perm) % 16 == 0);
+  hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(kPlanThreads), 0, s, topk_idx, T, k, E, chunk_counts);
+  hipLaunchKernelGGL(permute_plan_kernel, dim3(nchunks), dim3(kPlanThreads), 0, s, topk_idx, T, k, E, chunk_counts,
+                     nchunks, counts, offsets, row_of_slot, slot_of_row);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3((T + kScatterWaves - 1) / kScatterWaves), dim3(kScatterWaves * kWave),
+                     0, s, (const uint8_t*)x, T, row_bytes, k, row_of_slot, (uint8_t*)x_perm, vec16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

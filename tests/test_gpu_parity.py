@@ -1,0 +1,142 @@
+"""GPU parity: every kernel of the layer, called through the C ABI, against the CPU oracle.
+
+Integer results (indices, counts, offsets, row maps, permuted rows) must match bit for bit; the
+router logits too (both sides run the same fp32 FMA chain). Floating-point outputs must satisfy
+max|gpu - ref| / max|ref| <= 1e-2 in bf16 and <= 1e-5 in fp32. Inputs are seeded and synthetic."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_renorm_amd as moe
+import oracle
+from inputs import make_layer_inputs, normal
+from inputs.generators import generator
+from tests.gpu_util import TOL, as64, dev, host, rel_err
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+
+def routing(T, E, k, key, skew=None):
+    """k distinct experts per token; skew='one' sends every token to expert 0 (plus k-1 others);
+    skew='empty' never uses the last two experts."""
+    g = generator(key)
+    rows = []
+    for _ in range(T):
+        if skew == "empty":
+            rows.append(g.permutation(E - 2)[:k])
+        elif skew == "one":
+            rows.append(np.concatenate([[0], 1 + g.permutation(E - 1)[:k - 1]]))
+        else:
+            rows.append(g.permutation(E)[:k])
+    return np.array(rows, np.int32).reshape(T, k)
+
+
+# ---- router -----------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,E,dtype", [(64, 64, 8, "f32"), (300, 136, 72, "bf16"), (1, 8, 1, "bf16"),
+                                         (513, 2048, 128, "bf16"), (37, 7168, 256, "bf16"), (70, 24, 130, "f32")])
+def test_router_logits_bit_exact(T, H, E, dtype):
+    x = normal((T, H), 1.0, (950, T, H), dtype)
+    w = normal((H, E), 0.02, (951, H, E), dtype)
+    got = host(moe.moe_router_logits(dev(x), dev(w)))
+    want = oracle.router_logits(x, w)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1000, 128, 8), (77, 256, 8), (50, 1024, 32), (10, 5, 5),
+                                   (33, 64, 1), (20, 3, 3), (129, 100, 7)])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_router_topk(T, E, k, renorm):
+    g = generator((952, T, E, k))
+    logits = (np.round(g.standard_normal((T, E)) * 4) / 4).astype(np.float32)   # frequent ties
+    idx, w = moe.moe_router_topk(dev(logits), k, renorm)
+    ridx, rw = oracle.router_topk(logits, k, renorm)
+    assert np.array_equal(host(idx), ridx)
+    assert rel_err(host(w), rw) <= TOL["f32"]
+
+
+# ---- permute ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,E,k,dtype,skew", [
+    (64, 64, 8, 2, "f32", None), (1000, 136, 16, 4, "bf16", None), (257, 2048, 128, 8, "bf16", None),
+    (1, 8, 1, 1, "bf16", None), (600, 40, 4, 4, "bf16", None), (700, 64, 32, 8, "bf16", "one"),
+    (513, 24, 12, 3, "bf16", "empty"), (300, 30, 8, 2, "bf16", None), (2049, 16, 1024, 32, "f32", None)])
+def test_permute_bit_exact(T, H, E, k, dtype, skew):
+    x = normal((T, H), 1.0, (953, T, H), dtype)
+    idx = routing(T, E, k, (954, T, E, k), skew)
+    x_perm, plan = moe.moe_permute(dev(x), dev(idx), E)
+    counts, offsets, ros, sor = oracle.permute_plan(idx, E)
+    assert np.array_equal(host(plan.counts), counts)
+    assert np.array_equal(host(plan.offsets), offsets)
+    assert np.array_equal(host(plan.row_of_slot), ros)
+    assert np.array_equal(host(plan.slot_of_row), sor)
+    want = oracle.permute_rows(x, sor, k)
+    assert np.array_equal(host(x_perm), want)
+
+
+# ---- grouped FFN ------------------------------------------------------------------------------
+@pytest.mark.parametrize("counts,H,I,dtype", [
+    ([0, 300, 1, 0, 257, 142], 136, 40, "bf16"),
+    ([256, 256, 256, 256], 256, 192, "bf16"),
+    ([1000], 64, 24, "bf16"),
+    ([3, 0, 0, 517, 31, 64, 0, 1], 512, 128, "bf16"),
+    ([16, 16, 16, 16, 16, 16, 16, 16], 64, 32, "f32"),
+    ([0, 5, 0, 40], 48, 16, "f32"),
+])
+def test_grouped_swiglu_ffn(counts, H, I, dtype):
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    pad = 5                                              # rows past offsets[E] must stay untouched
+    xp = normal((N + pad, H), 1.0, (955, N, H), dtype)
+    gu = normal((E * H, 2 * I), 0.02 * 4, (956, E, H, I), dtype)
+    dn = normal((E * I, H), 0.02 * 4, (957, E, H, I), dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    y = torch.full((N + pad, H), 7.0, dtype=tdt, device="cuda")
+    gu_saved = torch.zeros((N + pad, 2 * I), dtype=tdt, device="cuda")
+    y, h = moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), dev(offsets), y=y, gu_saved=gu_saved)
+    ry, ra, rgu = oracle.expert_rows(xp[:N], offsets, gu, dn, want_act=True, want_gu=True)
+    gy = host(y)
+    assert rel_err(gy[:N], ry) <= TOL[dtype]
+    assert rel_err(host(h)[:N], ra) <= TOL[dtype]
+    assert rel_err(host(gu_saved)[:N], rgu) <= TOL[dtype]
+    assert np.all(as64(gy[N:]) == 7.0)
+
+
+# ---- combine ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,k,dtype,res", [(64, 64, 2, "f32", False), (1000, 2048, 8, "bf16", True),
+                                             (77, 136, 3, "bf16", False), (5, 40, 1, "bf16", True),
+                                             (300, 7168, 8, "bf16", False), (31, 20, 4, "f32", True)])
+def test_unpermute_combine(T, H, k, dtype, res):
+    N = T * k
+    g = generator((958, T, H, k))
+    ros = g.permutation(N).astype(np.int32)
+    y = normal((N, H), 1.0, (959, N, H), dtype)
+    w = g.random((T, k), dtype=np.float32)
+    r = normal((T, H), 1.0, (960, T, H), dtype) if res else None
+    out = moe.moe_unpermute_combine(dev(y), dev(ros), dev(w), residual=dev(r) if res else None)
+    assert rel_err(host(out), oracle.combine(y, ros, w, residual=r)) <= TOL[dtype]
+
+
+# ---- whole layer, small shapes -------------------------------------------------------------------
+@pytest.mark.parametrize("T,H,I,E,k,dtype", [(64, 64, 32, 8, 2, "f32"), (300, 136, 40, 16, 4, "bf16"),
+                                             (1, 64, 32, 8, 8, "bf16"), (257, 256, 64, 64, 8, "bf16"),
+                                             (100, 48, 16, 1, 1, "bf16"), (50, 32, 16, 4, 4, "f32")])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_layer_small(T, H, I, E, k, dtype, renorm):
+    d = make_layer_inputs(T, H, I, E, k, dtype, (961, T, E), w_std=0.08, wg_std=0.3)
+    out, bufs = moe.moe_layer_forward(dev(d["x"]), dev(d["gate_up"]), dev(d["down"]), k, w_gate=dev(d["w_gate"]),
+                                      renorm=renorm)
+    ref, ridx, rw, rlog = oracle.moe_forward(d["x"], d["gate_up"], d["down"], k, w_gate=d["w_gate"], renorm=renorm)
+    assert np.array_equal(host(bufs.logits).view(np.uint32), rlog.view(np.uint32))
+    assert np.array_equal(host(bufs.topk_idx), ridx)
+    assert rel_err(host(out), ref) <= TOL[dtype]
+
+
+def test_layer_determinism():
+    d = make_layer_inputs(512, 256, 128, 32, 4, "bf16", (962,), w_std=0.08)
+    args = (dev(d["x"]), dev(d["gate_up"]), dev(d["down"]), 4)
+    o1, b1 = moe.moe_layer_forward(*args, w_gate=dev(d["w_gate"]))
+    o1 = host(o1).copy()
+    p1 = host(b1.plan.row_of_slot).copy()
+    o2, b2 = moe.moe_layer_forward(*args, w_gate=dev(d["w_gate"]))
+    assert np.array_equal(o1, host(o2)) and np.array_equal(p1, host(b2.plan.row_of_slot))
