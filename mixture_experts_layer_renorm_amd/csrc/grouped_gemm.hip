@@ -19,6 +19,8 @@
 // fragment reads (32 consecutive rows) and the transposed 8-byte writes stay conflict-light.
 // The MFMA is issued with the weight fragment as its first operand, so each lane ends up holding
 // four consecutive output columns of one row, which become one 8-byte store.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -26,50 +28,68 @@ namespace moe {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kBM = 256;
-constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kGemmThreads = 256;
-constexpr int kTileA = kBM * kBK * 2;
-constexpr int kTileB = kBN * kBK * 2;
-constexpr int kStage = kTileA + kTileB;
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data, offset addressing
+constexpr int kOutOfRange = 0x7ffffff0;    // an offset past every descriptor's end: loads return zero
+
+constexpr int kBM = 256;            // rows of one expert per workgroup tile
+constexpr int kBN = 256;            // weight columns per tile (GEMM-1: 128 gate + 128 up)
+constexpr int kBK = 32;             // K per pipeline step
+constexpr int kStages = 4;          // LDS ring depth: steps s+1..s+3 are in flight while s computes
+constexpr int kGemmThreads = 256;   // 4 waves: 2 along M (128 rows each) x 2 along N (128 columns each)
+constexpr int kTileA = kBM * kBK * 2;  // 16 KB: [256 rows][32 k], 64-byte rows
+constexpr int kTileB = kBK * kBN * 2;  // 16 KB: [32 k][256 n], 512-byte rows (natural weight layout)
+constexpr int kDmaPerWave = (kTileA + kTileB) / 1024 / 4;  // 1 KB per wave-wide DMA instruction
 constexpr int kGemmMaxE = 1024;
 
-__device__ __forceinline__ int lds_swz(int r) { return (r ^ (r >> 3)) & 7; }
-// byte offset of 16-byte chunk c (8 consecutive k) of row r in a [rows][64] bf16 LDS tile
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ lds_swz(r)) << 4); }
+// LDS swizzles, applied when choosing which global chunk each DMA lane fetches. They keep the
+// fragment reads free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
+//  - row tile (64-byte rows): 16-byte chunk c (8 k) of row r lives at chunk c ^ g(r) with
+//    g(r) = ((r >> 1) ^ (r >> 2)) & 3; the 8 (or 16) consecutive rows read together at one logical
+//    chunk then land on distinct banks;
+//  - weight tile (512-byte k-rows): 16-byte chunk c (8 n) of k-row r lives at chunk c ^ f(r) with
+//    f(r) = 4 (r & 3) + 2 ((r >> 1) & 1); the transpose read of four consecutive k-rows x 32 bytes
+//    (x 64 bytes for two lane groups) then lands on distinct banks. f is even and below 16, so a
+//    16-byte pair stays adjacent and the gate / up halves of a GEMM-1 row never mix.
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int swz_b(int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Shared tile schedule: linear workgroup index -> (expert, row range, column tile).
-// Returns false when this workgroup has no tile.
+// Linear workgroup index -> (expert, row range, column tile). Returns false when the workgroup
+// has no tile (the grid is sized for the worst case over any distribution of rows).
 struct TileInfo {
   int e, row0, row_end, nt;
 };
 
+template <int NT>
 __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offsets, int E, int bm, int ntiles_n,
                                               int* s_pref, int* s_wtot, int* s_e, TileInfo& ti) {
   const int tid = threadIdx.x;
   const int G = gridDim.x;  // a multiple of 8
   const int b = blockIdx.x;
-  // consecutive logical tiles land on the same XCD (blocks are dealt round-robin over 8 XCDs)
+  // consecutive logical tiles land on the same XCD (blocks are dealt round-robin over 8 XCDs),
+  // so the column tiles of one row tile share its rows through that XCD's L2
   const int L = (b & 7) * (G >> 3) + (b >> 3);
   const int mt_g = L / ntiles_n;
   ti.nt = L - mt_g * ntiles_n;
-  for (int e = tid; e < E; e += kGemmThreads) {
+  for (int e = tid; e < E; e += NT) {
     const int n = offsets[e + 1] - offsets[e];
     s_pref[e] = n > 0 ? (n + bm - 1) / bm : 0;
   }
   __syncthreads();
-  block_exclusive_scan<kGemmThreads>(s_pref, E, s_wtot);
+  block_exclusive_scan<NT>(s_pref, E, s_wtot);
   if (mt_g >= s_pref[E]) return false;
-  for (int e = tid; e < E; e += kGemmThreads)
+  for (int e = tid; e < E; e += NT)
     if (s_pref[e] <= mt_g && mt_g < s_pref[e + 1]) *s_e = e;
   __syncthreads();
-  ti.e = *s_e;
-  ti.row0 = offsets[ti.e] + (mt_g - s_pref[ti.e]) * bm;
-  ti.row_end = min(ti.row0 + bm, (int)offsets[ti.e + 1]);
+  ti.e = __builtin_amdgcn_readfirstlane(*s_e);
+  ti.row0 = __builtin_amdgcn_readfirstlane(offsets[ti.e] + (mt_g - s_pref[ti.e]) * bm);
+  ti.row_end = __builtin_amdgcn_readfirstlane(min(ti.row0 + bm, (int)offsets[ti.e + 1]));
   return true;
 }
 
@@ -77,138 +97,198 @@ template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const int32_t* __restrict__ offsets, int E, int K,
     int ncols, int ldw, int ntiles_n, uint16_t* __restrict__ out, int ldo, uint16_t* __restrict__ gu_saved) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  // one LDS object per ring slot, so that the compiler can tell a DMA into one slot from reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA], sA1[kTileA], sA2[kTileA], sA3[kTileA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
   __shared__ int s_pref[kGemmMaxE + 1];
   __shared__ int s_wtot[kGemmThreads / kWave];
   __shared__ int s_e;
 
   TileInfo ti;
-  if (!tile_of_block(offsets, E, kBM, ntiles_n, s_pref, s_wtot, &s_e, ti)) return;
+  if (!tile_of_block<kGemmThreads>(offsets, E, kBM, ntiles_n, s_pref, s_wtot, &s_e, ti)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave & 1, wn = wave >> 1;
   const int row0 = ti.row0, row_end = ti.row_end, nt = ti.nt;
-  const uint16_t* Wexp = W + (int64_t)ti.e * K * ldw;
 
-  // weight-tile loader: thread owns 8 columns x 4 consecutive k rows
-  const int ng = tid & 15, kg = tid >> 4;
-  int bcol;
-  bool bcol_ok;
-  if (MODE == 0) {
-    const int nl = ng * 8;
-    const int j = nt * 64 + (nl & 63);
-    bcol = (nl < 64 ? 0 : ncols) + j;
-    bcol_ok = j < ncols;
-  } else {
-    bcol = nt * kBN + ng * 8;
-    bcol_ok = bcol < ncols;
+  // Buffer descriptors: the row tile covers exactly rows [row0, row_end) and the weight block exactly
+  // expert e's K rows, so rows past either end read as zero.
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (int64_t)row0 * K), (short)0, (row_end - row0) * K * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)ti.e * K * ldw), (short)0, K * ldw * 2, kBufferWord3);
+
+  // ---- DMA lanes. Row tile: wave w, instruction i fills rows (4w + i) * 16 .. + 16, four lanes per
+  // row. Weight tile: instruction i fills k-rows (4w + i) * 2 .. + 2, 32 lanes per row.
+  int a_off[4], a_kc[4], b_off[4];
+  bool b_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz_a(r);
+    a_kc[i] = c * 8;
+    a_off[i] = (r * K + c * 8) * 2;
+    const int kr = (wave * 4 + i) * 2 + (lane >> 5);
+    const int cb = (lane & 31) ^ swz_b(kr);
+    int col;
+    if (MODE == 0) {
+      const int j = nt * 128 + (cb & 15) * 8;
+      b_ok[i] = j < ncols;
+      col = (cb < 16 ? 0 : ncols) + j;
+    } else {
+      col = nt * kBN + cb * 8;
+      b_ok[i] = col < ncols;
+    }
+    b_off[i] = (kr * ldw + col) * 2;
   }
-
-  uint4 ra[8], rb[4];
-  auto load_tiles = [&](int kt) {
+  auto dma = [&](int kt, uint8_t* sa, uint8_t* sb) {
     const int k0 = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + kGemmThreads * i;
-      const int r = idx >> 3, c = idx & 7;
-      const int grow = row0 + r;
-      const int kc = k0 + c * 8;
-      if (grow < row_end && kc < K)
-        ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)grow * K + kc);
-      else
-        ra[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 4; ++i) {
+      const int off = (k0 + a_kc[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + (wave * 4 + i) * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kr = k0 + kg * 4 + i;
-      if (bcol_ok && kr < K)
-        rb[i] = *reinterpret_cast<const uint4*>(Wexp + (int64_t)kr * ldw + bcol);
-      else
-        rb[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_tiles = [&](uint8_t* st) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + kGemmThreads * i;
-      *reinterpret_cast<uint4*>(st + lds_off(idx >> 3, idx & 7)) = ra[i];
-    }
-    uint8_t* sb = st + kTileA;
-    const uint32_t b0[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
-    const uint32_t b1[4] = {rb[1].x, rb[1].y, rb[1].z, rb[1].w};
-    const uint32_t b2[4] = {rb[2].x, rb[2].y, rb[2].z, rb[2].w};
-    const uint32_t b3[4] = {rb[3].x, rb[3].y, rb[3].z, rb[3].w};
-    const int koff = (kg & 1) * 8;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t lo01 = (b0[d] & 0xffffu) | (b1[d] << 16);
-      const uint32_t hi01 = (b0[d] >> 16) | (b1[d] & 0xffff0000u);
-      const uint32_t lo23 = (b2[d] & 0xffffu) | (b3[d] << 16);
-      const uint32_t hi23 = (b2[d] >> 16) | (b3[d] & 0xffff0000u);
-      const int n0 = ng * 8 + 2 * d;
-      *reinterpret_cast<uint2*>(sb + lds_off(n0, kg >> 1) + koff) = make_uint2(lo01, lo23);
-      *reinterpret_cast<uint2*>(sb + lds_off(n0 + 1, kg >> 1) + koff) = make_uint2(hi01, hi23);
+      const int off = b_ok[i] ? b_off[i] + k0 * ldw * 2 : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_void*)(sb + (wave * 4 + i) * 1024), 16, off, 0, 0, 0);
     }
   };
 
-  f32x16 acc[2][4];
+  // ---- fragments. Row block mb: lane reads row (lane & 31) of the block, k = kk*16 + (lane/32)*8
+  // .. +8. Weight block nb (32 columns from brow[nb]): two transpose reads give column
+  // brow + (lane & 31) at k = kk*16 + (lane/32)*8 + 0..3 and + 4..7.
+  int brow[4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int nb = 0; nb < 4; ++nb)
+    brow[nb] = MODE == 0 ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
+  const int q = lane >> 4, sl = lane & 15;
+  int a_rd[2][4], b_rd[2][4][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int r = wm * 128 + mb * 32 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      a_rd[kk][mb] = r * 64 + ((c ^ swz_a(r)) << 4);
+    }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
-
-  const int wrows = row_end - (row0 + wave * 64);
-  const int nmb = wrows <= 0 ? 0 : (wrows <= 32 ? 1 : 2);  // m-blocks of this wave holding real rows
-
-  const int KT = (K + kBK - 1) / kBK;
-  load_tiles(0);
-  store_tiles(smem);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint8_t* cur = smem + (kt & 1) * kStage;
-    if (kt + 1 < KT) load_tiles(kt + 1);
-    if (nmb > 0) {
-#pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int c = kk * 2 + (lane >> 5);
-        bf16x8 af[2], bfr[4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          af[mb] = *reinterpret_cast<const bf16x8*>(cur + lds_off(wave * 64 + mb * 32 + (lane & 31), c));
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          bfr[nb] = *reinterpret_cast<const bf16x8*>(cur + kTileA + lds_off(nb * 32 + (lane & 31), c));
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[0], acc[0][nb], 0, 0, 0);
-        if (nmb > 1) {
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[1], acc[1][nb], 0, 0, 0);
-        }
+      for (int ri = 0; ri < 2; ++ri) {
+        const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
+        const int col = brow[nb] + (q & 1) * 16 + 4 * (sl & 3);
+        b_rd[kk][nb][ri] = kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
       }
-    }
-    if (kt + 1 < KT) store_tiles(smem + ((kt + 1) & 1) * kStage);
-    __syncthreads();
   }
 
-  // epilogue: lane holds row m = .. + (lane & 31) and columns (q/4)*8 + (lane/32)*4 + q%4 of each block
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = row0 + wave * 64 + mb * 32 + (lane & 31);
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
+
+  struct Frags {
+    bf16x8 a[4], b[4];
+  };
+  // NMB = number of this wave's 32-row blocks that hold rows (0..4, wave-uniform). Waves of one
+  // tile may run different NMB variants: every variant issues the same DMAs and barriers.
+  auto read_frags = [&](auto nmb_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
+    constexpr int NMB = decltype(nmb_c)::value;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + b_rd[kk][nb][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + b_rd[kk][nb][1]));
+      const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      f.b[nb] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(sa + a_rd[kk][mb]);
+  };
+  auto mfmas = [&](auto nmb_c, const Frags& f) {
+    constexpr int NMB = decltype(nmb_c)::value;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
+  };
+  // One step: prefetch step kt+3 into the slot freed by step kt-1, compute step kt, then wait for
+  // this wave's DMA of step kt+1 (the two later steps stay in flight) and meet at the barrier.
+  // The scheduler is told to interleave: the first sub-step's fragment reads, then MFMAs with the
+  // DMA issues and the second sub-step's fragment reads threaded between them.
+  auto step = [&](auto nmb_c, int kt, const uint8_t* sa, const uint8_t* sb, uint8_t* pa, uint8_t* pb) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    if constexpr (NMB == 0) {
+      dma(kt + 3, pa, pb);
+    } else {
+      Frags f0, f1;
+      read_frags(nmb_c, sa, sb, 0, f0);
+      read_frags(nmb_c, sa, sb, 1, f1);
+      dma(kt + 3, pa, pb);
+      mfmas(nmb_c, f0);
+      mfmas(nmb_c, f1);
+      constexpr int R = 8 + NMB;  // fragment reads per sub-step
+      constexpr int M = 4 * NMB;  // MFMAs per sub-step
+      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M >= 16 ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, R > 8 ? R - 8 : 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+  };
+  auto main_loop = [&](auto nmb_c) {
+    // Steps past the last real one load zeros (out-of-range offsets) and add nothing, so the step
+    // count is padded to a multiple of the ring depth and the loop body has no memory branches.
+    const int KT = (K + kBK - 1) / kBK;
+    const int KT4 = (KT + kStages - 1) / kStages * kStages;
+    dma(0, sA0, sB0);
+    dma(1, sA1, sB1);
+    dma(2, sA2, sB2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+    for (int kt = 0; kt < KT4; kt += kStages) {
+      step(nmb_c, kt + 0, sA0, sB0, sA3, sB3);
+      step(nmb_c, kt + 1, sA1, sB1, sA0, sB0);
+      step(nmb_c, kt + 2, sA2, sB2, sA1, sB1);
+      step(nmb_c, kt + 3, sA3, sB3, sA2, sB2);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  const int wrows = row_end - (row0 + wm * 128);
+  const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(4, (wrows + 31) / 32));
+  switch (nmb) {
+    case 4: main_loop(std::integral_constant<int, 4>{}); break;
+    case 3: main_loop(std::integral_constant<int, 3>{}); break;
+    case 2: main_loop(std::integral_constant<int, 2>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    default: main_loop(std::integral_constant<int, 0>{}); break;
+  }
+
+  // ---- epilogue: lane holds row (lane & 31) of each 32-row block and, per 32-column block,
+  // columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = row0 + wm * 128 + mb * 32 + (lane & 31);
     if (m >= row_end) continue;
     if (MODE == 0) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = nt * 64 + nb * 32 + g * 8 + (lane >> 5) * 4;
+          const int col = nt * 128 + wn * 64 + nb * 32 + g * 8 + (lane >> 5) * 4;
           if (col >= ncols) continue;
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu_f(acc[mb][nb][g * 4 + q]) * acc[mb][nb + 2][g * 4 + q];
+          for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[mb][nb][g * 4 + qq]) * acc[mb][nb + 2][g * 4 + qq];
           *reinterpret_cast<uint2*>(out + (int64_t)m * ldo + col) =
               make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
           if (gu_saved) {
@@ -227,7 +307,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = nt * kBN + nb * 32 + g * 8 + (lane >> 5) * 4;
+          const int col = nt * kBN + wn * 128 + nb * 32 + g * 8 + (lane >> 5) * 4;
           if (col >= ncols) continue;
           *reinterpret_cast<uint2*>(out + (int64_t)m * ldo + col) =
               make_uint2(pack_bf16x2(acc[mb][nb][g * 4 + 0], acc[mb][nb][g * 4 + 1]),
@@ -297,7 +377,7 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
                                const int32_t* offsets, void* h, void* gu_saved, hipStream_t s) {
   if (dt == kBF16) {
     const int64_t mt_bound = ((int64_t)N + (int64_t)E * (kBM - 1)) / kBM;
-    const int nt1 = (I + 63) / 64;
+    const int nt1 = (I + 127) / 128;
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(round_up8(mt_bound * nt1)), dim3(kGemmThreads), 0, s,
                        (const uint16_t*)x_perm, (const uint16_t*)gate_up, offsets, E, H, I, 2 * I, nt1, (uint16_t*)h, I,
                        (uint16_t*)gu_saved);
