@@ -143,8 +143,8 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void router_logits_kernel(
     const int nh = min(HB, H - hc * HB);
     const float* xw = &xs[buf][wave * kTokPerWave][0];
     const float* wl = &ws[buf][0][lane * EQ];
-    int hh = 0;
-    for (; hh + 4 <= nh; hh += 4) {
+    // four h at a time: one broadcast float4 of x per token, EQ weights per lane per h
+    auto quad = [&](int hh) {
       float4 xv[kTokPerWave];
 #pragma unroll
       for (int i = 0; i < kTokPerWave; ++i) xv[i] = *reinterpret_cast<const float4*>(xw + i * HB + hh);
@@ -160,6 +160,15 @@ __global__ __launch_bounds__(kLogitWaves * kWave) void router_logits_kernel(
           for (int q = 0; q < EQ; ++q) acc[i][q] = __builtin_fmaf(xe, wv[q], acc[i][q]);
         }
       }
+    };
+    int hh = 0;
+    if (nh == HB) {
+      // full chunk: unrolled so that the next reads are issued under the current FMAs
+#pragma unroll
+      for (int h4 = 0; h4 < HB; h4 += 4) quad(h4);
+      hh = HB;
+    } else {
+      for (; hh + 4 <= nh; hh += 4) quad(hh);
     }
     for (; hh < nh; ++hh) {
 #pragma unroll
