@@ -40,10 +40,13 @@ constexpr int kBM = 256;            // rows of one expert per workgroup tile
 constexpr int kBN = 256;            // weight columns per tile (GEMM-1: 128 gate + 128 up)
 constexpr int kBK = 32;             // K per pipeline step
 constexpr int kStages = 4;          // LDS ring depth: steps s+1..s+3 are in flight while s computes
-constexpr int kGemmThreads = 256;   // 4 waves: 2 along M (128 rows each) x 2 along N (128 columns each)
+constexpr int kGemmThreads = 512;   // 8 waves (2 per SIMD): 4 along M (64 rows each) x 2 along N (128 columns each)
 constexpr int kTileA = kBM * kBK * 2;  // 16 KB: [256 rows][32 k], 64-byte rows
 constexpr int kTileB = kBK * kBN * 2;  // 16 KB: [32 k][256 n], 512-byte rows (natural weight layout)
-constexpr int kDmaPerWave = (kTileA + kTileB) / 1024 / 4;  // 1 KB per wave-wide DMA instruction
+constexpr int kWaves = kGemmThreads / 64;
+constexpr int kDmaPerWave = (kTileA + kTileB) / 1024 / kWaves;  // 1 KB per wave-wide DMA instruction
+constexpr int kDmaA = kTileA / 1024 / kWaves;  // row-tile DMA instructions per wave per step
+constexpr int kDmaB = kTileB / 1024 / kWaves;
 constexpr int kGemmMaxE = 1024;
 
 // LDS swizzles, applied when choosing which global chunk each DMA lane fetches. They keep the
@@ -94,7 +97,7 @@ __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offset
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const int32_t* __restrict__ offsets, int E, int K,
     int ncols, int ldw, int ntiles_n, uint16_t* __restrict__ out, int ldo, uint16_t* __restrict__ gu_saved) {
   // one LDS object per ring slot, so that the compiler can tell a DMA into one slot from reads of another
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int row0 = ti.row0, row_end = ti.row_end, nt = ti.nt;
 
   // Buffer descriptors: the row tile covers exactly rows [row0, row_end) and the weight block exactly
@@ -120,17 +123,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + (int64_t)ti.e * K * ldw), (short)0, K * ldw * 2, kBufferWord3);
 
-  // ---- DMA lanes. Row tile: wave w, instruction i fills rows (4w + i) * 16 .. + 16, four lanes per
-  // row. Weight tile: instruction i fills k-rows (4w + i) * 2 .. + 2, 32 lanes per row.
-  int a_off[4], a_kc[4], b_off[4];
-  bool b_ok[4];
+  // ---- DMA lanes. Row tile: wave w, instruction i fills rows (kDmaA w + i) * 16 .. + 16, four lanes
+  // per row. Weight tile: instruction i fills k-rows (kDmaB w + i) * 2 .. + 2, 32 lanes per row.
+  int a_off[kDmaA], a_kc[kDmaA], b_off[kDmaB];
+  bool b_ok[kDmaB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * 16 + (lane >> 2);
+  for (int i = 0; i < kDmaA; ++i) {
+    const int r = (wave * kDmaA + i) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz_a(r);
     a_kc[i] = c * 8;
     a_off[i] = (r * K + c * 8) * 2;
-    const int kr = (wave * 4 + i) * 2 + (lane >> 5);
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int kr = (wave * kDmaB + i) * 2 + (lane >> 5);
     const int cb = (lane & 31) ^ swz_b(kr);
     int col;
     if (MODE == 0) {
@@ -146,14 +152,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   auto dma = [&](int kt, uint8_t* sa, uint8_t* sb) {
     const int k0 = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kDmaA; ++i) {
       const int off = (k0 + a_kc[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + (wave * 4 + i) * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + (wave * kDmaA + i) * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kDmaB; ++i) {
       const int off = b_ok[i] ? b_off[i] + k0 * ldw * 2 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_void*)(sb + (wave * 4 + i) * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_void*)(sb + (wave * kDmaB + i) * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -165,12 +171,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   for (int nb = 0; nb < 4; ++nb)
     brow[nb] = MODE == 0 ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
   const int q = lane >> 4, sl = lane & 15;
-  int a_rd[2][4], b_rd[2][4][2];
+  int a_rd[2][2], b_rd[2][4][2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int r = wm * 128 + mb * 32 + (lane & 31);
+    for (int mb = 0; mb < 2; ++mb) {
+      const int r = wm * 64 + mb * 32 + (lane & 31);
       const int c = kk * 2 + (lane >> 5);
       a_rd[kk][mb] = r * 64 + ((c ^ swz_a(r)) << 4);
     }
@@ -184,18 +190,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       }
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
 
   struct Frags {
-    bf16x8 a[4], b[4];
+    bf16x8 a[2], b[4];
   };
-  // NMB = number of this wave's 32-row blocks that hold rows (0..4, wave-uniform). Waves of one
+  // NMB = number of this wave's 32-row blocks that hold rows (0..2, wave-uniform). Waves of one
   // tile may run different NMB variants: every variant issues the same DMAs and barriers.
   auto read_frags = [&](auto nmb_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
     constexpr int NMB = decltype(nmb_c)::value;
@@ -236,13 +242,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       constexpr int M = 4 * NMB;  // MFMAs per sub-step
       __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, M >= 16 ? 2 : 1, 0);
+      for (int i = 0; i < kDmaPerWave; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, R > 8 ? R - 8 : 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, R > 2 * kDmaPerWave ? R - 2 * kDmaPerWave : 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * M - kDmaPerWave, 0);
     }
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
   };
@@ -263,11 +269,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  const int wrows = row_end - (row0 + wm * 128);
-  const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(4, (wrows + 31) / 32));
+  const int wrows = row_end - (row0 + wm * 64);
+  const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(2, (wrows + 31) / 32));
   switch (nmb) {
-    case 4: main_loop(std::integral_constant<int, 4>{}); break;
-    case 3: main_loop(std::integral_constant<int, 3>{}); break;
     case 2: main_loop(std::integral_constant<int, 2>{}); break;
     case 1: main_loop(std::integral_constant<int, 1>{}); break;
     default: main_loop(std::integral_constant<int, 0>{}); break;
@@ -276,8 +280,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   // ---- epilogue: lane holds row (lane & 31) of each 32-row block and, per 32-column block,
   // columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int m = row0 + wm * 128 + mb * 32 + (lane & 31);
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = row0 + wm * 64 + mb * 32 + (lane & 31);
     if (m >= row_end) continue;
     if (MODE == 0) {
 #pragma unroll
