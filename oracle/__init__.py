@@ -262,3 +262,59 @@ def router_logits_bwd(x, w_gate, d_logits):
     _call("orc_router_logits_bwd", _p(x), _p(w_gate), _dt(x), _p(d_logits), I64(T), I64(H), I64(E),
           _p(dwg), _p(dx))
     return dwg, dx
+
+
+def _f32(a):
+    """bf16 bit patterns (uint16) -> float32, exactly; float32 and None pass through."""
+    if a is None or a.dtype == np.float32:
+        return a
+    if a.dtype == np.uint16:
+        return (np.ascontiguousarray(a).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    raise TypeError(f"oracle takes float32 or bf16 (uint16 bit patterns), got {a.dtype}")
+
+
+def moe_backward(x, gate_up, down, k, d_out, w_gate=None, logits=None, renorm=True, shared_gate_up=None,
+                 shared_down=None, experts=None):
+    """Gradients of <d_out, layer(x)> along the layer, composed from the per-step backward functions
+    above in the order the forward ran them (the combine is the dispatch's backward and vice versa:
+    "DeepSeek MoE: EP and FSDP" guide, Automodel/DeepEP section). The routing selection is fixed to
+    the forward's. Returns a dict of fp64 arrays: d_x, d_logits, d_w_gate (None without w_gate),
+    d_gate_up / d_down (only the experts listed in `experts`, default all, each [H, 2I] / [I, H]),
+    d_shared_gate_up / d_shared_down, plus the intermediates d_w [T,k] and d_x_perm [N,H]."""
+    # every data tensor in fp32 (bf16 -> fp32 is exact), so that the per-step calls, which take one
+    # data type per call, can mix data inputs with the fp32 intermediates below
+    x, gate_up, down, d_out = _f32(x), _f32(gate_up), _f32(down), _f32(d_out)
+    w_gate, shared_gate_up, shared_down = _f32(w_gate), _f32(shared_gate_up), _f32(shared_down)
+    T, H = x.shape
+    E = gate_up.shape[0] // H
+    I = gate_up.shape[1] // 2
+    if logits is None:
+        logits = router_logits(x, w_gate)
+    idx, w = router_topk(logits, k, renorm)
+    _, offsets, ros, sor = permute_plan(idx, E)
+    xp = permute_rows(x, sor, k)
+    y = expert_rows(xp, offsets, gate_up, down)
+    d_y_slots, d_w = combine_bwd(d_out, y.astype(np.float32), ros, w.astype(np.float32))
+    d_y = np.empty((T * k, H), np.float64)
+    d_y[ros] = d_y_slots.reshape(T * k, H)
+    d_y32 = d_y.astype(np.float32)
+    d_xp = expert_rows_bwd(xp, d_y32, offsets, gate_up, down)
+    d_x = permute_bwd(d_xp.astype(np.float32), ros, k)
+    res = {"d_w": d_w, "d_x_perm": d_xp, "d_w_gate": None, "d_shared_gate_up": None, "d_shared_down": None}
+    if shared_gate_up is not None:
+        # the shared expert is one segment holding every token, with weight 1
+        sh_off = np.array([0, T], np.int32)
+        d_x = d_x + expert_rows_bwd(x, d_out, sh_off, shared_gate_up, shared_down)
+        res["d_shared_gate_up"], res["d_shared_down"] = expert_weight_grads(x, d_out, sh_off, shared_gate_up,
+                                                                            shared_down, 0)
+    d_l = router_topk_bwd(logits, idx, d_w, renorm)
+    res["d_logits"] = d_l
+    if w_gate is not None:
+        res["d_w_gate"], d_x_router = router_logits_bwd(x, w_gate, d_l)
+        d_x = d_x + d_x_router
+    res["d_x"] = d_x
+    experts = range(E) if experts is None else experts
+    res["d_gate_up"], res["d_down"] = {}, {}
+    for e in experts:
+        res["d_gate_up"][e], res["d_down"][e] = expert_weight_grads(xp, d_y32, offsets, gate_up, down, e)
+    return res

@@ -207,6 +207,7 @@ int orc_combine(const void* y, int dt, int64_t H, int64_t k, const int32_t* row_
         for (int64_t j = 0; j < k; ++j) {
             const double w = (double)topk_w[t * k + j];
             const int64_t r = row_of_slot[t * k + j];
+            if (r < 0) continue; /* a dropped slot contributes nothing */
             for (int64_t c = 0; c < H; ++c) o[c] += w * eld(y, dt, r * H + c);
         }
     }
@@ -274,8 +275,9 @@ int orc_combine_bwd(const void* d_out, const void* y, int dt, int64_t H, int64_t
             double dot = 0.0;
             for (int64_t c = 0; c < H; ++c) {
                 const double go = eld(d_out, dt, t * H + c);
-                if (d_y_slots) d_y_slots[(n * k + j) * H + c] = w * go;
-                dot += go * eld(y, dt, r * H + c);
+                /* a dropped slot (no row) takes no part in the combine: zero gradients */
+                if (d_y_slots) d_y_slots[(n * k + j) * H + c] = r < 0 ? 0.0 : w * go;
+                if (r >= 0) dot += go * eld(y, dt, r * H + c);
             }
             if (d_w) d_w[n * k + j] = dot;
         }
@@ -432,6 +434,7 @@ int orc_permute_bwd(const void* d_x_perm, int dt, int64_t H, int64_t k, const in
         for (int64_t c = 0; c < H; ++c) o[c] = d_x_add ? eld(d_x_add, dt, t * H + c) : 0.0;
         for (int64_t j = 0; j < k; ++j) {
             const int64_t r = row_of_slot[t * k + j];
+            if (r < 0) continue; /* a dropped slot was never copied */
             for (int64_t c = 0; c < H; ++c) o[c] += eld(d_x_perm, dt, r * H + c);
         }
     }

@@ -59,7 +59,9 @@ int orc_expert_rows(const void* x_perm, int dt, int64_t H, int64_t I, int64_t E,
                     const int32_t* offsets, const void* gate_up, const void* down,
                     const int64_t* rows, int64_t nrows, double* y_out, double* a_out, double* gu_out);
 
-/* out[t] = sum_{j<k} w[t,j] * y[row_of_slot[t*k+j]] (+ residual[t]) for each requested token. */
+/* out[t] = sum_{j<k} w[t,j] * y[row_of_slot[t*k+j]] (+ residual[t]) for each requested token.
+ * A slot whose row map is negative has been dropped and contributes nothing (here and in the
+ * two backward functions below). */
 int orc_combine(const void* y, int dt, int64_t H, int64_t k, const int32_t* row_of_slot,
                 const float* topk_w, const void* residual, const int64_t* tokens, int64_t ntok,
                 double* out);

@@ -162,25 +162,12 @@ def test_whole_layer_backward_against_torch_autograd(renorm):
     x, wg, gu, dn = d["x"], d["w_gate"], d["gate_up"], d["down"]
     sgu, sdn, d_out = d["shared_gate_up"], d["shared_down"], d["d_out"]
     # ---- oracle composition
+    r = oracle.moe_backward(x, gu, dn, k, d_out, w_gate=wg, renorm=renorm, shared_gate_up=sgu, shared_down=sdn)
+    d_x, dwg = r["d_x"], r["d_w_gate"]
+    dgu = np.concatenate([r["d_gate_up"][e] for e in range(E)])
+    ddn = np.concatenate([r["d_down"][e] for e in range(E)])
     logits = oracle.router_logits(x, wg)
-    idx, w = oracle.router_topk(logits, k, renorm)
-    counts, offsets, ros, sor = oracle.permute_plan(idx, E)
-    xp = oracle.permute_rows(x, sor, k)
-    y = oracle.expert_rows(xp, offsets, gu, dn)
-    d_y_slots, d_w = oracle.combine_bwd(d_out, y.astype(np.float32), ros, w.astype(np.float32))
-    d_y = np.empty((T * k, H))
-    d_y[ros] = d_y_slots.reshape(T * k, H)
-    d_xp = oracle.expert_rows_bwd(xp, d_y.astype(np.float32), offsets, gu, dn)
-    # shared expert: one segment holding every token, weight 1
-    sh_off = np.array([0, T], np.int32)
-    d_x_sh = oracle.expert_rows_bwd(x, d_out, sh_off, sgu, sdn)
-    d_l = oracle.router_topk_bwd(logits, idx, d_w, renorm)
-    dwg, d_x_router = oracle.router_logits_bwd(x, wg, d_l)
-    d_x = oracle.permute_bwd(d_xp.astype(np.float32), ros, k) + d_x_sh + d_x_router
-    dgu = np.concatenate([oracle.expert_weight_grads(xp, d_y.astype(np.float32), offsets, gu, dn, e)[0]
-                          for e in range(E)])
-    ddn = np.concatenate([oracle.expert_weight_grads(xp, d_y.astype(np.float32), offsets, gu, dn, e)[1]
-                          for e in range(E)])
+    idx, _ = oracle.router_topk(logits, k, renorm)
     # ---- torch fp64 autograd, dense formulation
     X = torch.tensor(x.astype(np.float64), requires_grad=True)
     WG = torch.tensor(wg.astype(np.float64), requires_grad=True)
@@ -210,3 +197,45 @@ def test_whole_layer_backward_against_torch_autograd(renorm):
     np.testing.assert_allclose(dwg, WG.grad.numpy(), **tol)
     np.testing.assert_allclose(dgu, GU.grad.numpy(), **tol)
     np.testing.assert_allclose(ddn, DN.grad.numpy(), **tol)
+    np.testing.assert_allclose(r["d_shared_gate_up"], SGU.grad.numpy(), **tol)
+    np.testing.assert_allclose(r["d_shared_down"], SDN.grad.numpy(), **tol)
+
+
+def test_dropped_slots_contribute_nothing():
+    """A slot whose row map is -1 behaves as a slot of weight 0: the combine, its backward and the
+    permute backward give the same results as with that slot's weight (and gradient) set to zero."""
+    T, H, k, N = 9, 12, 3, 27
+    g = np.random.default_rng(6)
+    ros = g.permutation(N).astype(np.int32)
+    y = normal((N, H), 1.0, (926, 1), "f32")
+    w = g.random((T, k)).astype(np.float32)
+    d_out = normal((T, H), 1.0, (926, 2), "f32")
+    drop = np.zeros(T * k, bool)
+    drop[::4] = True
+    ros_d = np.where(drop, -1, ros).astype(np.int32)
+    w0 = np.where(drop.reshape(T, k), 0.0, w).astype(np.float32)
+    np.testing.assert_array_equal(oracle.combine(y, ros_d, w), oracle.combine(y, ros, w0))
+    dy_d, dw_d = oracle.combine_bwd(d_out, y, ros_d, w)
+    dy_0, dw_0 = oracle.combine_bwd(d_out, y, ros, w0)
+    np.testing.assert_array_equal(dy_d, dy_0)
+    assert np.all(dw_d.reshape(-1)[drop] == 0.0)
+    np.testing.assert_array_equal(dw_d.reshape(-1)[~drop], dw_0.reshape(-1)[~drop])
+    dxp = normal((N, H), 1.0, (926, 3), "f32")
+    dxp_0 = dxp.copy()
+    dxp_0[ros[drop]] = 0.0
+    np.testing.assert_array_equal(oracle.permute_bwd(dxp, ros_d, k), oracle.permute_bwd(dxp_0, ros, k))
+
+
+def test_moe_backward_bf16_inputs_equal_their_fp32_values():
+    """bf16 inputs give the same gradients as their (exact) fp32 values."""
+    T, H, I, E, k = 10, 16, 8, 4, 2
+    d = make_layer_inputs(T, H, I, E, k, "bf16", (927,), w_std=0.3, wg_std=0.3, shared=1, backward=True)
+    f = {n: as64(a).astype(np.float32) for n, a in d.items()}
+    args = ("x", "gate_up", "down")
+    kw = lambda s: dict(w_gate=s["w_gate"], shared_gate_up=s["shared_gate_up"], shared_down=s["shared_down"])
+    rb = oracle.moe_backward(*(d[n] for n in args), k, d["d_out"], **kw(d))
+    rf = oracle.moe_backward(*(f[n] for n in args), k, f["d_out"], **kw(f))
+    for key in ("d_x", "d_w_gate", "d_logits", "d_shared_gate_up", "d_shared_down"):
+        np.testing.assert_array_equal(rb[key], rf[key])
+    for e in range(E):
+        np.testing.assert_array_equal(rb["d_gate_up"][e], rf["d_gate_up"][e])
