@@ -1,8 +1,10 @@
 /*
  * moe_rocm.h — C ABI of the MI355X (gfx950) MoE expert layer with renormalised top-k routing.
  *
- * The layer (one GPU, forward):
- *   moe_router_logits -> moe_router_topk -> moe_permute -> moe_grouped_swiglu_ffn -> moe_unpermute_combine
+ * The layer (one GPU):
+ *   forward:  moe_router_logits -> moe_router_topk -> moe_permute -> moe_grouped_swiglu_ffn -> moe_unpermute_combine
+ *   backward: moe_unpermute_combine_bwd -> moe_grouped_swiglu_ffn_bwd -> moe_permute_bwd, and
+ *             moe_router_topk_bwd -> moe_router_logits_bwd
  *
  * Sources for what each call computes (web pages on the fused MoE layer):
  *   [MM]  MindSpeed-MM issue 625, "InternVL3.5 pure FSDP2" practice doc: section 8.2/8.3 (router is
@@ -29,8 +31,9 @@
  *   - Errors: a moe_status is returned; arguments are checked on the host before any launch and a
  *     failed check enqueues nothing. moe_last_error() gives the calling thread's last message.
  *     A launch failure reports MOE_ERR_HIP. Nothing aborts and nothing falls back silently.
- *     Device-side values (indices, offsets) are not checked on the host; the kernels stay in bounds
- *     for any values (see each call).
+ *     Device-side values are not checked on the host: expert indices outside [0, E) are dropped by the
+ *     permute, and negative row maps are skipped; expert_offsets must be non-decreasing with
+ *     offsets[E] <= the buffer's rows, and row maps must index existing rows.
  */
 #ifndef MOE_ROCM_H
 #define MOE_ROCM_H
@@ -124,6 +127,55 @@ moe_status moe_grouped_gemm_down(const void* h, const void* down, moe_dtype dt, 
  *   y [N, H] dt with N > every row_of_slot entry; topk_w [T, k] fp32; residual, out [T, H] dt.   */
 moe_status moe_unpermute_combine(const void* y, moe_dtype dt, int T, int H, int k, const int32_t* row_of_slot,
                                  const float* topk_w, const void* residual, void* out, hipStream_t stream);
+
+/* ==== backward =====================================================================================
+ * Gradients of a loss L given dL/dout, for the forward above. [DS Automodel/DeepEP]: the combine is
+ * the dispatch's backward and vice versa. All reductions in fp32; weight gradients are written, not
+ * accumulated. */
+
+/* ---- (6) combine backward ------------------------------------------------------------------------
+ *   d_y[row_of_slot[t*k+j]] = topk_w[t,j] * d_out[t]        (dt; rows without a slot are untouched)
+ *   d_w[t,j] = <d_out[t], y[row_of_slot[t*k+j]]>            (fp32)
+ *   d_out [T,H] dt; y [N,H] dt; row_of_slot [T*k]; topk_w [T,k] fp32; d_y [N,H] dt; d_w [T,k] fp32.  */
+moe_status moe_unpermute_combine_bwd(const void* d_out, const void* y, moe_dtype dt, int T, int H, int k,
+                                     const int32_t* row_of_slot, const float* topk_w, void* d_y, float* d_w,
+                                     hipStream_t stream);
+
+/* ---- (7) grouped SwiGLU FFN backward (bf16) --------------------------------------------------------
+ * For each expert e and its rows r (g, u = the forward pre-activations saved in gu_saved, s = sigmoid(g)):
+ *   dh[r] = d_y[r] @ down_e^T;  dg = dh * u * s * (1 + g (1 - s));  du = dh * g * s;   d_gu[r] = dg | du
+ *   d_x_perm[r] = d_gu[r] @ gate_up_e^T
+ *   d_down_e    = h_e^T @ d_y_e        [I, H]   (zeros for an expert without rows)
+ *   d_gate_up_e = x_perm_e^T @ d_gu_e  [H, 2I]  (zeros for an expert without rows)
+ *   d_y, x_perm [N,H]; gu_saved, d_gu [N,2I] (d_gu: caller scratch, also an output); h [N,I];
+ *   gate_up, d_gate_up [E*H, 2I]; down, d_down [E*I, H]; d_x_perm [N,H]. All bf16, 16-byte aligned.
+ * A shared expert is the same call with E = 1 and expert_offsets = {0, T}.
+ * MOE_ERR_UNSUPPORTED for fp32 data.                                                                 */
+moe_status moe_grouped_swiglu_ffn_bwd(const void* d_y, const void* x_perm, const void* gu_saved, const void* h,
+                                      const void* gate_up, const void* down, moe_dtype dt, int N, int H, int I, int E,
+                                      const int32_t* expert_offsets, void* d_x_perm, void* d_gate_up, void* d_down,
+                                      void* d_gu, hipStream_t stream);
+
+/* ---- (8) permute backward (gather-sum of a token's k rows) ----------------------------------------
+ *   d_x[t] = d_x_add[t] + sum_{j<k} d_x_perm[row_of_slot[t*k+j]]   (fp32, rounded once; d_x_add may
+ *   be NULL; slots with row_of_slot < 0 are skipped).  d_x_perm [N,H], d_x_add, d_x [T,H] dt.         */
+moe_status moe_permute_bwd(const void* d_x_perm, moe_dtype dt, int T, int H, int k, const int32_t* row_of_slot,
+                           const void* d_x_add, void* d_x, hipStream_t stream);
+
+/* ---- (9) top-k / renormalisation backward ----------------------------------------------------------
+ * Selection has no gradient. With w the forward weights and s = sum_j w_j d_w_j:
+ *   renorm = 1:  d_logits[t, S_j] = w_j (d_w_j - s), 0 for experts outside the selection;
+ *   renorm = 0:  d_logits[t, e] = p_e (1[e selected] d_w_e - s), p = softmax(logits[t]) recomputed
+ *                (logits may be NULL when renorm = 1).   d_logits [T,E] fp32, every entry written.     */
+moe_status moe_router_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w, const float* d_w,
+                               int T, int E, int k, int renorm, float* d_logits, hipStream_t stream);
+
+/* ---- (10) router logits backward -------------------------------------------------------------------
+ *   d_w_gate = x^T @ d_logits   [H,E] fp32   (skipped when NULL)
+ *   d_x      = d_x_in + d_logits @ w_gate^T   [T,H] dt   (skipped when NULL; d_x_in may be NULL)
+ * fp32 accumulation on the vector ALU.                                                                */
+moe_status moe_router_logits_bwd(const void* x, const void* w_gate, const float* d_logits, moe_dtype dt, int T,
+                                 int H, int E, float* d_w_gate, const void* d_x_in, void* d_x, hipStream_t stream);
 
 #ifdef __cplusplus
 }

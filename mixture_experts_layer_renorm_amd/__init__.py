@@ -51,6 +51,11 @@ def load_library() -> ctypes.CDLL:
             "moe_grouped_gemm_swiglu": (I, [P, P, I, I, I, I, I, P, P, P, P]),
             "moe_grouped_gemm_down": (I, [P, P, I, I, I, I, I, P, P, P]),
             "moe_unpermute_combine": (I, [P, I, I, I, I, P, P, P, P, P]),
+            "moe_unpermute_combine_bwd": (I, [P, P, I, I, I, I, P, P, P, P, P]),
+            "moe_grouped_swiglu_ffn_bwd": (I, [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P]),
+            "moe_permute_bwd": (I, [P, I, I, I, I, P, P, P, P]),
+            "moe_router_topk_bwd": (I, [P, P, P, P, I, I, I, I, P, P]),
+            "moe_router_logits_bwd": (I, [P, P, P, I, I, I, I, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -222,11 +227,95 @@ def moe_unpermute_combine(y, row_of_slot, topk_w, residual=None, out=None, strea
     return out
 
 
+# ---- backward ----------------------------------------------------------------------------------
+def moe_unpermute_combine_bwd(d_out, y, row_of_slot, topk_w, d_y=None, d_w=None, stream=None):
+    T, k = topk_w.shape
+    H = y.shape[1]
+    _need(d_out, "d_out", y.dtype, (T, H)), _need(y, "y"), _need(row_of_slot, "row_of_slot", torch.int32)
+    _need(topk_w, "topk_w", torch.float32)
+    if d_y is None:
+        d_y = torch.empty_like(y)
+    if d_w is None:
+        d_w = torch.empty((T, k), dtype=torch.float32, device=y.device)
+    _need(d_y, "d_y", y.dtype, tuple(y.shape)), _need(d_w, "d_w", torch.float32, (T, k))
+    _check(load_library().moe_unpermute_combine_bwd(_ptr(d_out), _ptr(y), _dt(y), T, H, k, _ptr(row_of_slot),
+                                                    _ptr(topk_w), _ptr(d_y), _ptr(d_w), _stream(stream)),
+           "moe_unpermute_combine_bwd")
+    return d_y, d_w
+
+
+def moe_grouped_swiglu_ffn_bwd(d_y, x_perm, gu_saved, h, gate_up, down, expert_offsets, d_x_perm=None, d_gate_up=None,
+                               d_down=None, d_gu=None, stream=None):
+    N, H = x_perm.shape
+    E = expert_offsets.shape[0] - 1
+    I = h.shape[1]
+    for t, nme, shp in [(d_y, "d_y", (N, H)), (x_perm, "x_perm", (N, H)), (gu_saved, "gu_saved", (N, 2 * I)),
+                        (h, "h", (N, I)), (gate_up, "gate_up", (E * H, 2 * I)), (down, "down", (E * I, H))]:
+        _need(t, nme, x_perm.dtype, shp)
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    dev = x_perm.device
+    if d_x_perm is None:
+        d_x_perm = torch.empty((N, H), dtype=x_perm.dtype, device=dev)
+    if d_gate_up is None:
+        d_gate_up = torch.empty_like(gate_up)
+    if d_down is None:
+        d_down = torch.empty_like(down)
+    if d_gu is None:
+        d_gu = torch.empty((N, 2 * I), dtype=x_perm.dtype, device=dev)
+    _check(load_library().moe_grouped_swiglu_ffn_bwd(_ptr(d_y), _ptr(x_perm), _ptr(gu_saved), _ptr(h), _ptr(gate_up),
+                                                     _ptr(down), _dt(x_perm), N, H, I, E, _ptr(expert_offsets),
+                                                     _ptr(d_x_perm), _ptr(d_gate_up), _ptr(d_down), _ptr(d_gu),
+                                                     _stream(stream)), "moe_grouped_swiglu_ffn_bwd")
+    return d_x_perm, d_gate_up, d_down, d_gu
+
+
+def moe_permute_bwd(d_x_perm, row_of_slot, T, k, d_x_add=None, d_x=None, stream=None):
+    H = d_x_perm.shape[1]
+    _need(d_x_perm, "d_x_perm"), _need(row_of_slot, "row_of_slot", torch.int32)
+    if d_x_add is not None:
+        _need(d_x_add, "d_x_add", d_x_perm.dtype, (T, H))
+    if d_x is None:
+        d_x = torch.empty((T, H), dtype=d_x_perm.dtype, device=d_x_perm.device)
+    _check(load_library().moe_permute_bwd(_ptr(d_x_perm), _dt(d_x_perm), T, H, k, _ptr(row_of_slot), _ptr(d_x_add),
+                                          _ptr(d_x), _stream(stream)), "moe_permute_bwd")
+    return d_x
+
+
+def moe_router_topk_bwd(logits, topk_idx, topk_w, d_w, renorm=True, d_logits=None, stream=None):
+    T, k = topk_idx.shape
+    E = logits.shape[1] if logits is not None else None
+    if d_logits is None:
+        d_logits = torch.empty((T, E), dtype=torch.float32, device=topk_idx.device)
+    E = d_logits.shape[1]
+    _check(load_library().moe_router_topk_bwd(_ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(d_w), T, E, k,
+                                              int(bool(renorm)), _ptr(d_logits), _stream(stream)),
+           "moe_router_topk_bwd")
+    return d_logits
+
+
+def moe_router_logits_bwd(x, w_gate, d_logits, d_w_gate=None, d_x_in=None, d_x=None, want_dw=True, want_dx=True,
+                          stream=None):
+    T, H = x.shape
+    E = w_gate.shape[1]
+    _need(d_logits, "d_logits", torch.float32, (T, E))
+    if want_dw and d_w_gate is None:
+        d_w_gate = torch.empty((H, E), dtype=torch.float32, device=x.device)
+    if want_dx and d_x is None:
+        d_x = torch.empty((T, H), dtype=x.dtype, device=x.device)
+    _check(load_library().moe_router_logits_bwd(_ptr(x), _ptr(w_gate), _ptr(d_logits), _dt(x), T, H, E,
+                                                _ptr(d_w_gate if want_dw else None), _ptr(d_x_in),
+                                                _ptr(d_x if want_dx else None), _stream(stream)),
+           "moe_router_logits_bwd")
+    return d_w_gate, d_x
+
+
 # ---- the layer: the five calls in order on one stream ---------------------------------------------
 class LayerBuffers:
-    """Device buffers of one layer call, allocated once and reused (no allocation in the timed path)."""
+    """Device buffers of one layer call, allocated once and reused (no allocation in the timed path).
+    gu_saved keeps the expert pre-activations for the backward; I_shared > 0 adds the shared expert's
+    buffers (its segment offsets {0, T} are copied to the device here, once)."""
 
-    def __init__(self, T, H, I, E, k, dtype, device, logits=True, gu_saved=False):
+    def __init__(self, T, H, I, E, k, dtype, device, logits=True, gu_saved=False, I_shared=0):
         N = T * k
         self.logits = torch.empty((T, E), dtype=torch.float32, device=device) if logits else None
         self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=device)
@@ -241,20 +330,95 @@ class LayerBuffers:
         self.gu_saved = torch.empty((N, 2 * I), dtype=dtype, device=device) if gu_saved else None
         self.y = torch.empty((N, H), dtype=dtype, device=device)
         self.out = torch.empty((T, H), dtype=dtype, device=device)
+        self.shared = None
+        if I_shared:
+            self.shared = {
+                "offsets": torch.tensor([0, T], dtype=torch.int32).to(device),
+                "h": torch.empty((T, I_shared), dtype=dtype, device=device),
+                "gu_saved": torch.empty((T, 2 * I_shared), dtype=dtype, device=device) if gu_saved else None,
+                "y": torch.empty((T, H), dtype=dtype, device=device),
+            }
 
 
 def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True, residual=None, bufs=None,
-                      stream=None):
-    """Router (logits unless given) -> top-k -> permute -> grouped SwiGLU FFN -> combine."""
+                      shared_gate_up=None, shared_down=None, save_for_backward=False, stream=None):
+    """Router (logits unless given) -> top-k -> permute -> grouped SwiGLU FFN -> combine.
+    With shared_gate_up / shared_down, the shared expert runs on every token as a one-segment grouped
+    FFN and its output is the combine's residual (a separate residual is then not accepted)."""
     T, H = x.shape
     E = gate_up.shape[0] // H
     I = gate_up.shape[1] // 2
+    I_sh = 0 if shared_gate_up is None else shared_gate_up.shape[1] // 2
+    if I_sh and residual is not None:
+        raise ValueError("moe_layer_forward: the shared expert's output is the residual; pass one or the other")
     if bufs is None:
-        bufs = LayerBuffers(T, H, I, E, k, x.dtype, x.device, logits=logits is None)
+        bufs = LayerBuffers(T, H, I, E, k, x.dtype, x.device, logits=logits is None, gu_saved=save_for_backward,
+                            I_shared=I_sh)
     if logits is None:
         logits = moe_router_logits(x, w_gate, bufs.logits, stream)
     moe_router_topk(logits, k, renorm, bufs.topk_idx, bufs.topk_w, stream)
     moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace, stream)
     moe_grouped_swiglu_ffn(bufs.x_perm, gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, bufs.gu_saved, stream)
+    if I_sh:
+        sh = bufs.shared
+        moe_grouped_swiglu_ffn(x, shared_gate_up, shared_down, sh["offsets"], sh["h"], sh["y"], sh["gu_saved"], stream)
+        residual = sh["y"]
     moe_unpermute_combine(bufs.y, bufs.plan.row_of_slot, bufs.topk_w, residual, bufs.out, stream)
     return bufs.out, bufs
+
+
+class LayerGrads:
+    """Gradient buffers of one layer backward (allocated once, reused)."""
+
+    def __init__(self, T, H, I, E, k, dtype, device, I_shared=0, router=True):
+        N = T * k
+        self.d_y = torch.empty((N, H), dtype=dtype, device=device)
+        self.d_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.d_gu = torch.empty((N, 2 * I), dtype=dtype, device=device)
+        self.d_x_perm = torch.empty((N, H), dtype=dtype, device=device)
+        self.d_gate_up = torch.empty((E * H, 2 * I), dtype=dtype, device=device)
+        self.d_down = torch.empty((E * I, H), dtype=dtype, device=device)
+        self.d_logits = torch.empty((T, E), dtype=torch.float32, device=device)
+        self.d_w_gate = torch.empty((H, E), dtype=torch.float32, device=device) if router else None
+        self.d_x_side = torch.empty((T, H), dtype=dtype, device=device)   # shared-expert / router dX
+        self.d_x_side2 = torch.empty((T, H), dtype=dtype, device=device) if I_shared and router else None
+        self.d_x = torch.empty((T, H), dtype=dtype, device=device)
+        self.d_shared_gate_up = self.d_shared_down = self.d_shared_gu = None
+        if I_shared:
+            self.d_shared_gate_up = torch.empty((H, 2 * I_shared), dtype=dtype, device=device)
+            self.d_shared_down = torch.empty((I_shared, H), dtype=dtype, device=device)
+            self.d_shared_gu = torch.empty((T, 2 * I_shared), dtype=dtype, device=device)
+
+
+def moe_layer_backward(d_out, x, gate_up, down, bufs, w_gate=None, logits=None, renorm=True, shared_gate_up=None,
+                       shared_down=None, grads=None, stream=None):
+    """Backward of moe_layer_forward(..., save_for_backward=True) given d_out = dL/d(out):
+    combine-bwd -> grouped FFN bwd (+ shared expert) -> top-k bwd -> router-logits bwd -> permute-bwd,
+    which sums each token's k expert-row gradients with the shared-expert and router contributions."""
+    T, H = x.shape
+    E = gate_up.shape[0] // H
+    I = gate_up.shape[1] // 2
+    k = bufs.topk_idx.shape[1]
+    I_sh = 0 if shared_gate_up is None else shared_gate_up.shape[1] // 2
+    if bufs.gu_saved is None:
+        raise ValueError("moe_layer_backward: run the forward with save_for_backward=True")
+    if grads is None:
+        grads = LayerGrads(T, H, I, E, k, x.dtype, x.device, I_shared=I_sh, router=w_gate is not None)
+    g = grads
+    moe_unpermute_combine_bwd(d_out, bufs.y, bufs.plan.row_of_slot, bufs.topk_w, g.d_y, g.d_w, stream)
+    moe_grouped_swiglu_ffn_bwd(g.d_y, bufs.x_perm, bufs.gu_saved, bufs.h, gate_up, down, bufs.plan.offsets,
+                               g.d_x_perm, g.d_gate_up, g.d_down, g.d_gu, stream)
+    side = None   # dX contributions besides the expert rows
+    if I_sh:
+        sh = bufs.shared
+        moe_grouped_swiglu_ffn_bwd(d_out, x, sh["gu_saved"], sh["h"], shared_gate_up, shared_down, sh["offsets"],
+                                   g.d_x_side, g.d_shared_gate_up, g.d_shared_down, g.d_shared_gu, stream)
+        side = g.d_x_side
+    logits = bufs.logits if logits is None else logits
+    moe_router_topk_bwd(logits, bufs.topk_idx, bufs.topk_w, g.d_w, renorm, g.d_logits, stream)
+    if w_gate is not None:
+        dst = g.d_x_side2 if side is not None else g.d_x_side
+        moe_router_logits_bwd(x, w_gate, g.d_logits, g.d_w_gate, d_x_in=side, d_x=dst, stream=stream)
+        side = dst
+    moe_permute_bwd(g.d_x_perm, bufs.plan.row_of_slot, T, k, d_x_add=side, d_x=g.d_x, stream=stream)
+    return g

@@ -108,6 +108,9 @@ moe_status check_ffn(const char* fn, moe_dtype dt, int N, int H, int I, int E) {
   if (dt == MOE_BF16)
     REQUIRE(H % 8 == 0 && I % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: bf16 needs H and I multiples of 8 (H=%d I=%d)", fn, H,
             I);
+  // the bf16 kernels address one expert's weight block with 32-bit byte offsets
+  REQUIRE((int64_t)H * 2 * I * 4 < 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "%s: H*I=%lld too large", fn,
+          (long long)H * I);
   return MOE_OK;
 }
 }  // namespace
@@ -165,6 +168,84 @@ moe_status moe_unpermute_combine(const void* y, moe_dtype dt, int T, int H, int 
   REQUIRE(y && row_of_slot && topk_w && out, MOE_ERR_INVALID_ARG, "moe_unpermute_combine: null pointer");
   return hip_status(moe::launch_combine(y, (int)dt, T, H, k, row_of_slot, topk_w, residual, out, stream),
                     "moe_unpermute_combine");
+}
+
+// ---- backward ---------------------------------------------------------------------------------
+moe_status moe_unpermute_combine_bwd(const void* d_out, const void* y, moe_dtype dt, int T, int H, int k,
+                                     const int32_t* row_of_slot, const float* topk_w, void* d_y, float* d_w,
+                                     hipStream_t stream) {
+  const char* fn = "moe_unpermute_combine_bwd";
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_ARG, "%s: T=%d H=%d must be >= 0", fn, T, H);
+  REQUIRE(k >= 1 && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, %d]", fn, k, kMaxK);
+  if (T == 0) return ok();
+  REQUIRE(d_out && y && row_of_slot && topk_w && d_y && d_w, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  return hip_status(moe::launch_combine_bwd(d_out, y, (int)dt, T, H, k, row_of_slot, topk_w, d_y, d_w, stream), fn);
+}
+
+moe_status moe_grouped_swiglu_ffn_bwd(const void* d_y, const void* x_perm, const void* gu_saved, const void* h,
+                                      const void* gate_up, const void* down, moe_dtype dt, int N, int H, int I, int E,
+                                      const int32_t* expert_offsets, void* d_x_perm, void* d_gate_up, void* d_down,
+                                      void* d_gu, hipStream_t stream) {
+  const char* fn = "moe_grouped_swiglu_ffn_bwd";
+  moe_status st = check_ffn(fn, dt, N, H, I, E);
+  if (st != MOE_OK) return st;
+  REQUIRE(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: the backward is implemented for bf16", fn);
+  // the weight-gradient products address all rows of one expert with 32-bit byte offsets
+  REQUIRE((int64_t)N * (H > 2 * I ? H : 2 * I) * 2 < 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
+          "%s: N*max(H, 2I) too large for one call (N=%d H=%d I=%d)", fn, N, H, I);
+  REQUIRE(d_gate_up && d_down && expert_offsets, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(!misaligned16(d_y) && !misaligned16(x_perm) && !misaligned16(gu_saved) && !misaligned16(h) &&
+              !misaligned16(gate_up) && !misaligned16(down) && !misaligned16(d_x_perm) && !misaligned16(d_gate_up) &&
+              !misaligned16(d_down) && !misaligned16(d_gu),
+          MOE_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  if (N > 0) REQUIRE(d_y && x_perm && gu_saved && h && gate_up && down && d_x_perm && d_gu, MOE_ERR_INVALID_ARG,
+                     "%s: null pointer", fn);
+  hipError_t e = hipSuccess;
+  if (N > 0) {
+    e = moe::launch_gemm_down_bwd(d_y, down, gu_saved, N, H, I, E, expert_offsets, d_gu, stream);
+    if (e == hipSuccess) e = moe::launch_gemm_gate_up_bwd(d_gu, gate_up, N, H, I, E, expert_offsets, d_x_perm, stream);
+  }
+  // weight gradients cover every expert (zeros for experts without rows, and for N == 0)
+  if (e == hipSuccess) e = moe::launch_gemm_wgrad(h, d_y, I, H, E, expert_offsets, d_down, stream);
+  if (e == hipSuccess) e = moe::launch_gemm_wgrad(x_perm, d_gu, H, 2 * I, E, expert_offsets, d_gate_up, stream);
+  return hip_status(e, fn);
+}
+
+moe_status moe_permute_bwd(const void* d_x_perm, moe_dtype dt, int T, int H, int k, const int32_t* row_of_slot,
+                           const void* d_x_add, void* d_x, hipStream_t stream) {
+  const char* fn = "moe_permute_bwd";
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_ARG, "%s: T=%d H=%d must be >= 0", fn, T, H);
+  REQUIRE(k >= 1 && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, %d]", fn, k, kMaxK);
+  if (T == 0 || H == 0) return ok();
+  REQUIRE(d_x_perm && row_of_slot && d_x, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  return hip_status(moe::launch_permute_bwd(d_x_perm, (int)dt, T, H, k, row_of_slot, d_x_add, d_x, stream), fn);
+}
+
+moe_status moe_router_topk_bwd(const float* logits, const int32_t* topk_idx, const float* topk_w, const float* d_w,
+                               int T, int E, int k, int renorm, float* d_logits, hipStream_t stream) {
+  const char* fn = "moe_router_topk_bwd";
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "%s: T=%d must be >= 0", fn, T);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  REQUIRE(k >= 1 && k <= E && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, min(E=%d, %d)]", fn, k, E, kMaxK);
+  REQUIRE(renorm == 0 || renorm == 1, MOE_ERR_INVALID_ARG, "%s: renorm=%d must be 0 or 1", fn, renorm);
+  if (T == 0) return ok();
+  REQUIRE(topk_idx && topk_w && d_w && d_logits, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(renorm || logits, MOE_ERR_INVALID_ARG, "%s: the raw-softmax gradient needs the logits", fn);
+  return hip_status(moe::launch_router_topk_bwd(logits, topk_idx, topk_w, d_w, T, E, k, renorm, d_logits, stream), fn);
+}
+
+moe_status moe_router_logits_bwd(const void* x, const void* w_gate, const float* d_logits, moe_dtype dt, int T, int H,
+                                 int E, float* d_w_gate, const void* d_x_in, void* d_x, hipStream_t stream) {
+  const char* fn = "moe_router_logits_bwd";
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  REQUIRE(T >= 0 && H >= 1, MOE_ERR_INVALID_ARG, "%s: T=%d H=%d out of range", fn, T, H);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  REQUIRE(x && w_gate && d_logits, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(d_w_gate || d_x, MOE_ERR_INVALID_ARG, "%s: nothing to compute (d_w_gate and d_x are both NULL)", fn);
+  return hip_status(
+      moe::launch_router_logits_bwd(x, w_gate, d_logits, (int)dt, T, H, E, d_w_gate, d_x_in, d_x, stream), fn);
 }
 
 }  // extern "C"

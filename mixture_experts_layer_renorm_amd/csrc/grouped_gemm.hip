@@ -1,4 +1,4 @@
-// Grouped SwiGLU expert FFN over the fused expert weights.
+// Grouped GEMMs of the expert FFN (forward and backward) over the fused expert weights.
 //
 // The fused layout is the one of the MindSpeed-MM InternVL3.5 practice doc (issue 625, section 2,
 // model integration): gate_up [E*H, 2*I] and down [E*I, H], row-major; its section 8.3 runs the
@@ -6,19 +6,23 @@
 // optimisation doc (section 2.1) groups the experts into one call to avoid per-expert launches.
 // Gate columns are [0, I) and up columns [I, 2I) of an expert's block; h = silu(gate) * up.
 //
-//   GEMM-1 (MODE 0): for each expert e, rows r of segment e:  h[r, :] = silu(x_perm[r] @ Wg_e) * (x_perm[r] @ Wu_e)
-//   GEMM-2 (MODE 1): y[r, :] = h[r] @ down_e
+// One kernel serves every grouped product of the layer, for each expert e with rows
+// [offsets[e], offsets[e+1]) of the expert-grouped buffers:
+//   forward   h  = silu(X_e Wg_e) * (X_e Wu_e)            (SwiGLU epilogue, optional saved g|u)
+//             y  = h_e D_e
+//   backward  dGU = SwiGLU'(dY_e D_e^T, g, u)              (SwiGLU-backward epilogue)
+//             dX  = dGU_e GU_e^T
+//             dD_e  = h_e^T dY_e,   dGU_e = X_e^T dGU_e   (weight gradients; K = rows of expert e,
+//                                                          experts without rows get zeros)
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation. A workgroup (4 waves) owns a
-// 256-row x 128-column tile of one expert; each wave owns 64 rows x all 128 columns. Tiles are
-// derived on the device from expert_offsets (empty experts own no tile), so no host sync is needed.
-// K is staged through a double-buffered LDS ring in steps of 64. The weights are row-major [K, N]
-// (N contiguous) while the matrix cores want K contiguous per lane, so each thread loads a 4 x 8
-// block of the weight tile and transposes it in registers before writing it to LDS. LDS rows are
-// 128 bytes; 16-byte chunks are XOR-swizzled by (row ^ row >> 3) & 7 so that both the 16-byte
-// fragment reads (32 consecutive rows) and the transposed 8-byte writes stay conflict-light.
-// The MFMA is issued with the weight fragment as its first operand, so each lane ends up holding
-// four consecutive output columns of one row, which become one 8-byte store.
+// gfx950 design: v_mfma_f32_32x32x16_bf16, fp32 accumulation. A workgroup of 8 waves (2 per SIMD)
+// computes a 256 x 256 tile; each wave 64 x 128. Both operand tiles go global -> LDS by 16-byte
+// buffer DMA into a 4-stage ring of 32-deep K steps. An operand whose K dimension is contiguous in
+// memory is staged as a "row tile" ([256 rows][32 k], 64-byte rows) and read with ds_read_b128; an
+// operand whose M or N dimension is contiguous is staged in its natural layout as a "k-row tile"
+// ([32 k][256 cols], 512-byte rows) and read with the LDS transpose read ds_read_b64_tr_b16, so no
+// operand is ever repacked. The MFMA takes the B fragment first, so a lane ends up holding four
+// consecutive output columns of one row, which become one 8-byte store.
 #include <type_traits>
 
 #include "common.hpp"
@@ -36,17 +40,17 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data, offset addressing
 constexpr int kOutOfRange = 0x7ffffff0;    // an offset past every descriptor's end: loads return zero
 
-constexpr int kBM = 256;            // rows of one expert per workgroup tile
-constexpr int kBN = 256;            // weight columns per tile (GEMM-1: 128 gate + 128 up)
+constexpr int kBM = 256;            // output rows per workgroup tile
+constexpr int kBN = 256;            // output columns per tile (forward GEMM-1: 128 gate + 128 up)
 constexpr int kBK = 32;             // K per pipeline step
 constexpr int kStages = 4;          // LDS ring depth: steps s+1..s+3 are in flight while s computes
 constexpr int kGemmThreads = 512;   // 8 waves (2 per SIMD): 4 along M (64 rows each) x 2 along N (128 columns each)
-constexpr int kTileA = kBM * kBK * 2;  // 16 KB: [256 rows][32 k], 64-byte rows
-constexpr int kTileB = kBK * kBN * 2;  // 16 KB: [32 k][256 n], 512-byte rows (natural weight layout)
+constexpr int kTileA = kBM * kBK * 2;  // 16 KB per operand tile, either layout
+constexpr int kTileB = kBK * kBN * 2;
 constexpr int kWaves = kGemmThreads / 64;
 constexpr int kDmaPerWave = (kTileA + kTileB) / 1024 / kWaves;  // 1 KB per wave-wide DMA instruction
-constexpr int kDmaA = kTileA / 1024 / kWaves;  // row-tile DMA instructions per wave per step
-constexpr int kDmaB = kTileB / 1024 / kWaves;
+constexpr int kDmaA = kTileA / 1024 / kWaves;  // DMA instructions per wave per step, operand A
+constexpr int kDmaB = kTileB / 1024 / kWaves;  // and operand B
 constexpr int kGemmMaxE = 1024;
 
 // LDS swizzles, applied when choosing which global chunk each DMA lane fetches. They keep the
@@ -54,17 +58,17 @@ constexpr int kGemmMaxE = 1024;
 //  - row tile (64-byte rows): 16-byte chunk c (8 k) of row r lives at chunk c ^ g(r) with
 //    g(r) = ((r >> 1) ^ (r >> 2)) & 3; the 8 (or 16) consecutive rows read together at one logical
 //    chunk then land on distinct banks;
-//  - weight tile (512-byte k-rows): 16-byte chunk c (8 n) of k-row r lives at chunk c ^ f(r) with
+//  - k-row tile (512-byte k-rows): 16-byte chunk c (8 columns) of k-row r lives at chunk c ^ f(r) with
 //    f(r) = 4 (r & 3) + 2 ((r >> 1) & 1); the transpose read of four consecutive k-rows x 32 bytes
 //    (x 64 bytes for two lane groups) then lands on distinct banks. f is even and below 16, so a
-//    16-byte pair stays adjacent and the gate / up halves of a GEMM-1 row never mix.
+//    16-byte pair stays adjacent and the gate / up halves of a forward GEMM-1 row never mix.
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ __forceinline__ int swz_b(int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// Linear workgroup index -> (expert, row range, column tile). Returns false when the workgroup
-// has no tile (the grid is sized for the worst case over any distribution of rows).
+// Row-grouped schedule: linear workgroup index -> (expert, row range, column tile). Returns false
+// when the workgroup has no tile (the grid is sized for the worst case over any row distribution).
 struct TileInfo {
   int e, row0, row_end, nt;
 };
@@ -96,10 +100,31 @@ __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offset
   return true;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, const int32_t* __restrict__ offsets, int E, int K,
-    int ncols, int ldw, int ntiles_n, uint16_t* __restrict__ out, int ldo, uint16_t* __restrict__ gu_saved) {
+
+enum { kEpiSwiglu = 0, kEpiStore = 1, kEpiSwigluBwd = 2 };
+enum { kSchedRows = 0, kSchedWgrad = 1 };
+
+// Arguments of one grouped product C = A B (per expert). Sizes in elements.
+struct GemmArgs {
+  const uint16_t* A;   // rows-grouped operand (SchedRows) or activations whose rows are K (SchedWgrad)
+  const uint16_t* B;   // weights (SchedRows) or the second activation (SchedWgrad)
+  uint16_t* C;
+  const uint16_t* gu;  // saved g|u [rows, 2*N] read by the SwiGLU-backward epilogue
+  uint16_t* gu_out;    // optional g|u written by the SwiGLU epilogue [rows, 2*N]
+  const int32_t* offsets;
+  int E;
+  int M, N, K;         // SchedRows: N output columns, K; SchedWgrad: M, N per expert (K from offsets)
+  int lda, ldb, ldc;
+  int64_t b_expert;    // SchedRows: elements between two experts' weight blocks
+  int64_t c_expert;    // SchedWgrad: elements between two experts' output blocks
+  int b_rows;          // SchedRows: rows of one expert's weight block (K for a k-row B, N for a row B)
+  int ntiles_m, ntiles_n;
+};
+
+// A_ROWS: A is a row tile (K contiguous) - else a k-row tile (M contiguous).
+// B_ROWS: B is a row tile (K contiguous) - else a k-row tile (N contiguous).
+template <bool A_ROWS, bool B_ROWS, int EPI, int SCHED>
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const GemmArgs g) {
   // one LDS object per ring slot, so that the compiler can tell a DMA into one slot from reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA], sA1[kTileA], sA2[kTileA], sA3[kTileA];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
@@ -107,87 +132,165 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
   __shared__ int s_wtot[kGemmThreads / kWave];
   __shared__ int s_e;
 
-  TileInfo ti;
-  if (!tile_of_block<kGemmThreads>(offsets, E, kBM, ntiles_n, s_pref, s_wtot, &s_e, ti)) return;
-
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave & 3, wn = wave >> 2;
-  const int row0 = ti.row0, row_end = ti.row_end, nt = ti.nt;
 
-  // Buffer descriptors: the row tile covers exactly rows [row0, row_end) and the weight block exactly
-  // expert e's K rows, so rows past either end read as zero.
-  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + (int64_t)row0 * K), (short)0, (row_end - row0) * K * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)ti.e * K * ldw), (short)0, K * ldw * 2, kBufferWord3);
+  // ---- tile, rows and K of this workgroup
+  int e, m0, n0, mvalid, K, nt;
+  const uint16_t* abase;
+  const uint16_t* bbase;
+  int a_records, b_records;
+  if constexpr (SCHED == kSchedRows) {
+    TileInfo ti;
+    if (!tile_of_block<kGemmThreads>(g.offsets, g.E, kBM, g.ntiles_n, s_pref, s_wtot, &s_e, ti)) return;
+    e = ti.e;
+    m0 = ti.row0;
+    mvalid = ti.row_end - ti.row0;
+    nt = ti.nt;
+    n0 = nt * kBN;
+    K = g.K;
+    abase = g.A + (int64_t)m0 * g.lda;       // rows [row0, row_end) of the grouped operand
+    a_records = mvalid * g.lda * 2;
+    bbase = g.B + (int64_t)e * g.b_expert;   // expert e's weight block
+    b_records = g.b_rows * g.ldb * 2;
+  } else {
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int L = (b & 7) * (G >> 3) + (b >> 3);
+    const int per_e = g.ntiles_m * g.ntiles_n;
+    e = L / per_e;
+    if (e >= g.E) return;
+    const int rem = L - e * per_e;
+    const int mt = rem / g.ntiles_n;
+    nt = rem - mt * g.ntiles_n;
+    m0 = mt * kBM;
+    n0 = nt * kBN;
+    mvalid = min(kBM, g.M - m0);
+    const int r0 = g.offsets[e];
+    K = __builtin_amdgcn_readfirstlane(max(0, (int)g.offsets[e + 1] - r0));  // rows of expert e
+    abase = g.A + (int64_t)r0 * g.lda;       // expert e's rows; k-row tiles over them
+    bbase = g.B + (int64_t)r0 * g.ldb;
+    a_records = K * g.lda * 2;
+    b_records = K * g.ldb * 2;
+  }
+  const __amdgpu_buffer_rsrc_t rsA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, a_records, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, b_records, kBufferWord3);
 
-  // ---- DMA lanes. Row tile: wave w, instruction i fills rows (kDmaA w + i) * 16 .. + 16, four lanes
-  // per row. Weight tile: instruction i fills k-rows (kDmaB w + i) * 2 .. + 2, 32 lanes per row.
-  int a_off[kDmaA], a_kc[kDmaA], b_off[kDmaB];
-  bool b_ok[kDmaB];
+  // ---- DMA lanes (offsets in bytes from the descriptor base, for k0 = 0)
+  // Row tile: instruction i fills rows (kDma w + i) * 16 .. +16, four lanes (16-byte chunks) per row.
+  // k-row tile: instruction i fills k-rows (kDma w + i) * 2 .. +2, 32 lanes per row.
+  int a_off[kDmaA], b_off[kDmaB];
+  bool a_ok[kDmaA], b_ok[kDmaB];
+  int a_kc[kDmaA], b_kc[kDmaB];  // row tiles: k offset of the lane's chunk (for the K tail)
 #pragma unroll
   for (int i = 0; i < kDmaA; ++i) {
-    const int r = (wave * kDmaA + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz_a(r);
-    a_kc[i] = c * 8;
-    a_off[i] = (r * K + c * 8) * 2;
+    if constexpr (A_ROWS) {
+      const int r = (wave * kDmaA + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_a(r);
+      a_kc[i] = c * 8;
+      a_ok[i] = true;
+      a_off[i] = (r * g.lda + c * 8) * 2;
+    } else {
+      const int kr = (wave * kDmaA + i) * 2 + (lane >> 5);
+      const int cb = (lane & 31) ^ swz_b(kr);
+      const int col = m0 + cb * 8;
+      a_kc[i] = 0;
+      a_ok[i] = col < g.M;
+      a_off[i] = (kr * g.lda + (a_ok[i] ? col : 0)) * 2;
+    }
   }
 #pragma unroll
   for (int i = 0; i < kDmaB; ++i) {
-    const int kr = (wave * kDmaB + i) * 2 + (lane >> 5);
-    const int cb = (lane & 31) ^ swz_b(kr);
-    int col;
-    if (MODE == 0) {
-      const int j = nt * 128 + (cb & 15) * 8;
-      b_ok[i] = j < ncols;
-      col = (cb < 16 ? 0 : ncols) + j;
+    if constexpr (B_ROWS) {
+      const int r = (wave * kDmaB + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_a(r);
+      const int n = n0 + r;
+      b_kc[i] = c * 8;
+      b_ok[i] = n < g.N;
+      b_off[i] = ((b_ok[i] ? n : 0) * g.ldb + c * 8) * 2;
     } else {
-      col = nt * kBN + cb * 8;
-      b_ok[i] = col < ncols;
+      const int kr = (wave * kDmaB + i) * 2 + (lane >> 5);
+      const int cb = (lane & 31) ^ swz_b(kr);
+      int col;
+      if constexpr (EPI == kEpiSwiglu) {  // 128 gate columns then the matching 128 up columns
+        const int j = nt * 128 + (cb & 15) * 8;
+        b_ok[i] = j < g.N;
+        col = (cb < 16 ? 0 : g.N) + (b_ok[i] ? j : 0);
+      } else {
+        col = n0 + cb * 8;
+        b_ok[i] = col < g.N;
+        if (!b_ok[i]) col = 0;
+      }
+      b_kc[i] = 0;
+      b_off[i] = (kr * g.ldb + col) * 2;
     }
-    b_off[i] = (kr * ldw + col) * 2;
   }
   auto dma = [&](int kt, uint8_t* sa, uint8_t* sb) {
     const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i) {
-      const int off = (k0 + a_kc[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange;
+      int off;
+      if constexpr (A_ROWS)
+        off = (k0 + a_kc[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange;
+      else
+        off = a_ok[i] ? a_off[i] + k0 * g.lda * 2 : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + (wave * kDmaA + i) * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
-      const int off = b_ok[i] ? b_off[i] + k0 * ldw * 2 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsW, (lds_void*)(sb + (wave * kDmaB + i) * 1024), 16, off, 0, 0, 0);
+      int off;
+      if constexpr (B_ROWS)
+        off = (b_ok[i] && k0 + b_kc[i] < K) ? b_off[i] + k0 * 2 : kOutOfRange;
+      else
+        off = b_ok[i] ? b_off[i] + k0 * g.ldb * 2 : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(sb + (wave * kDmaB + i) * 1024), 16, off, 0, 0, 0);
     }
   };
 
-  // ---- fragments. Row block mb: lane reads row (lane & 31) of the block, k = kk*16 + (lane/32)*8
-  // .. +8. Weight block nb (32 columns from brow[nb]): two transpose reads give column
-  // brow + (lane & 31) at k = kk*16 + (lane/32)*8 + 0..3 and + 4..7.
-  int brow[4];
+  // ---- fragment addresses. A block mb: rows (or k-row-tile columns) wm*64 + mb*32 + (lane & 31).
+  // B block nb: 32 tile columns from bcol[nb]. Row tile: one ds_read_b128 at k = kk*16 + (lane/32)*8.
+  // k-row tile: two transpose reads at k = kk*16 + (lane/32)*8 + {0..3, 4..7}.
+  int bcol[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
-    brow[nb] = MODE == 0 ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
+    bcol[nb] = EPI == kEpiSwiglu ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
   const int q = lane >> 4, sl = lane & 15;
-  int a_rd[2][2], b_rd[2][4][2];
+  auto row_rd = [&](int r, int kk) {
+    const int c = kk * 2 + (lane >> 5);
+    return r * 64 + ((c ^ swz_a(r)) << 4);
+  };
+  auto krow_rd = [&](int col32, int kk, int ri) {
+    const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
+    const int col = col32 + (q & 1) * 16 + 4 * (sl & 3);
+    return kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+  };
+  int a_rd[2][2][2], b_rd[2][4][2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int r = wm * 64 + mb * 32 + (lane & 31);
-      const int c = kk * 2 + (lane >> 5);
-      a_rd[kk][mb] = r * 64 + ((c ^ swz_a(r)) << 4);
+      if constexpr (A_ROWS) {
+        a_rd[kk][mb][0] = row_rd(wm * 64 + mb * 32 + (lane & 31), kk);
+        a_rd[kk][mb][1] = 0;
+      } else {
+        a_rd[kk][mb][0] = krow_rd(wm * 64 + mb * 32, kk, 0);
+        a_rd[kk][mb][1] = krow_rd(wm * 64 + mb * 32, kk, 1);
+      }
     }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int ri = 0; ri < 2; ++ri) {
-        const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
-        const int col = brow[nb] + (q & 1) * 16 + 4 * (sl & 3);
-        b_rd[kk][nb][ri] = kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+    for (int nb = 0; nb < 4; ++nb) {
+      if constexpr (B_ROWS) {
+        b_rd[kk][nb][0] = row_rd(bcol[nb] + (lane & 31), kk);
+        b_rd[kk][nb][1] = 0;
+      } else {
+        b_rd[kk][nb][0] = krow_rd(bcol[nb], kk, 0);
+        b_rd[kk][nb][1] = krow_rd(bcol[nb], kk, 1);
       }
+    }
   }
 
   f32x16 acc[2][4];
@@ -201,19 +304,20 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
   struct Frags {
     bf16x8 a[2], b[4];
   };
+  auto frag = [&](const uint8_t* base, const int* rd, bool rows) -> bf16x8 {
+    if (rows) return *reinterpret_cast<const bf16x8*>(base + rd[0]);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   // NMB = number of this wave's 32-row blocks that hold rows (0..2, wave-uniform). Waves of one
   // tile may run different NMB variants: every variant issues the same DMAs and barriers.
   auto read_frags = [&](auto nmb_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
     constexpr int NMB = decltype(nmb_c)::value;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + b_rd[kk][nb][0]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sb + b_rd[kk][nb][1]));
-      const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      f.b[nb] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag(sb, b_rd[kk][nb], B_ROWS);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(sa + a_rd[kk][mb]);
+    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = frag(sa, a_rd[kk][mb], A_ROWS);
   };
   auto mfmas = [&](auto nmb_c, const Frags& f) {
     constexpr int NMB = decltype(nmb_c)::value;
@@ -238,8 +342,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
       dma(kt + 3, pa, pb);
       mfmas(nmb_c, f0);
       mfmas(nmb_c, f1);
-      constexpr int R = 8 + NMB;  // fragment reads per sub-step
-      constexpr int M = 4 * NMB;  // MFMAs per sub-step
+      constexpr int R = (B_ROWS ? 4 : 8) + (A_ROWS ? 1 : 2) * NMB;  // LDS reads per sub-step
+      constexpr int M = 4 * NMB;                                  // MFMAs per sub-step
       __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
       for (int i = 0; i < kDmaPerWave; ++i) {
@@ -269,7 +373,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  const int wrows = row_end - (row0 + wm * 64);
+  const int wrows = mvalid - wm * 64;
   const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(2, (wrows + 31) / 32));
   switch (nmb) {
     case 2: main_loop(std::integral_constant<int, 2>{}); break;
@@ -277,32 +381,34 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     default: main_loop(std::integral_constant<int, 0>{}); break;
   }
 
-  // ---- epilogue: lane holds row (lane & 31) of each 32-row block and, per 32-column block,
-  // columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
+  // ---- epilogue: lane holds output row (lane & 31) of each 32-row block and, per 32-column
+  // block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
+  uint16_t* cbase = SCHED == kSchedRows ? g.C : g.C + (int64_t)e * g.c_expert;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const int m = row0 + wm * 64 + mb * 32 + (lane & 31);
-    if (m >= row_end) continue;
-    if (MODE == 0) {
+    const int mloc = wm * 64 + mb * 32 + (lane & 31);
+    if (mloc >= mvalid) continue;
+    const int64_t m = m0 + mloc;
+    if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = nt * 128 + wn * 64 + nb * 32 + g * 8 + (lane >> 5) * 4;
-          if (col >= ncols) continue;
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = nt * 128 + wn * 64 + nb * 32 + gq * 8 + (lane >> 5) * 4;
+          if (col >= g.N) continue;
           float hv[4];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[mb][nb][g * 4 + qq]) * acc[mb][nb + 2][g * 4 + qq];
-          *reinterpret_cast<uint2*>(out + (int64_t)m * ldo + col) =
+          for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[mb][nb][gq * 4 + qq]) * acc[mb][nb + 2][gq * 4 + qq];
+          *reinterpret_cast<uint2*>(cbase + m * g.ldc + col) =
               make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-          if (gu_saved) {
-            uint16_t* gs = gu_saved + (int64_t)m * 2 * ncols;
+          if (g.gu_out) {
+            uint16_t* gs = g.gu_out + m * 2 * g.N;
             *reinterpret_cast<uint2*>(gs + col) =
-                make_uint2(pack_bf16x2(acc[mb][nb][g * 4 + 0], acc[mb][nb][g * 4 + 1]),
-                           pack_bf16x2(acc[mb][nb][g * 4 + 2], acc[mb][nb][g * 4 + 3]));
-            *reinterpret_cast<uint2*>(gs + ncols + col) =
-                make_uint2(pack_bf16x2(acc[mb][nb + 2][g * 4 + 0], acc[mb][nb + 2][g * 4 + 1]),
-                           pack_bf16x2(acc[mb][nb + 2][g * 4 + 2], acc[mb][nb + 2][g * 4 + 3]));
+                make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                           pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
+            *reinterpret_cast<uint2*>(gs + g.N + col) =
+                make_uint2(pack_bf16x2(acc[mb][nb + 2][gq * 4 + 0], acc[mb][nb + 2][gq * 4 + 1]),
+                           pack_bf16x2(acc[mb][nb + 2][gq * 4 + 2], acc[mb][nb + 2][gq * 4 + 3]));
           }
         }
       }
@@ -310,12 +416,36 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = nt * kBN + wn * 128 + nb * 32 + g * 8 + (lane >> 5) * 4;
-          if (col >= ncols) continue;
-          *reinterpret_cast<uint2*>(out + (int64_t)m * ldo + col) =
-              make_uint2(pack_bf16x2(acc[mb][nb][g * 4 + 0], acc[mb][nb][g * 4 + 1]),
-                         pack_bf16x2(acc[mb][nb][g * 4 + 2], acc[mb][nb][g * 4 + 3]));
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = n0 + wn * 128 + nb * 32 + gq * 8 + (lane >> 5) * 4;
+          if (col >= g.N) continue;
+          float v[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mb][nb][gq * 4 + qq];
+          if constexpr (EPI == kEpiSwigluBwd) {
+            // v = dL/dh; with s = sigmoid(g): dL/dg = v * u * s * (1 + g (1 - s)), dL/du = v * g * s
+            const uint16_t* gr = g.gu + m * 2 * g.N;
+            const uint2 gp = *reinterpret_cast<const uint2*>(gr + col);
+            const uint2 up = *reinterpret_cast<const uint2*>(gr + g.N + col);
+            const float gv[4] = {bf16_to_f32(gp.x & 0xffffu), bf16_to_f32(gp.x >> 16), bf16_to_f32(gp.y & 0xffffu),
+                                 bf16_to_f32(gp.y >> 16)};
+            const float uv[4] = {bf16_to_f32(up.x & 0xffffu), bf16_to_f32(up.x >> 16), bf16_to_f32(up.y & 0xffffu),
+                                 bf16_to_f32(up.y >> 16)};
+            float dg[4], du[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const float sg = 1.0f / (1.0f + __expf(-gv[qq]));
+              dg[qq] = v[qq] * uv[qq] * sg * (1.0f + gv[qq] * (1.0f - sg));
+              du[qq] = v[qq] * gv[qq] * sg;
+            }
+            uint16_t* dr = cbase + m * g.ldc;
+            *reinterpret_cast<uint2*>(dr + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(dr + g.N + col) =
+                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          } else {
+            *reinterpret_cast<uint2*>(cbase + m * g.ldc + col) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
         }
       }
     }
@@ -377,14 +507,34 @@ __global__ __launch_bounds__(256) void grouped_ffn2_f32_kernel(const float* __re
 // ---------------------------------------------------------------------------------------------
 static inline int round_up8(int64_t v) { return (int)((v + 7) / 8 * 8); }
 
+template <bool A_ROWS, bool B_ROWS, int EPI, int SCHED>
+static void launch_generic(GemmArgs g, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<A_ROWS, B_ROWS, EPI, SCHED>), dim3(round_up8(grid)), dim3(kGemmThreads),
+                     0, s, g);
+}
+
+// worst-case row tiles over any distribution of N rows among E experts
+static inline int64_t row_tiles_bound(int N, int E) { return ((int64_t)N + (int64_t)E * (kBM - 1)) / kBM; }
+
 hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, int N, int H, int I, int E,
                                const int32_t* offsets, void* h, void* gu_saved, hipStream_t s) {
   if (dt == kBF16) {
-    const int64_t mt_bound = ((int64_t)N + (int64_t)E * (kBM - 1)) / kBM;
-    const int nt1 = (I + 127) / 128;
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(round_up8(mt_bound * nt1)), dim3(kGemmThreads), 0, s,
-                       (const uint16_t*)x_perm, (const uint16_t*)gate_up, offsets, E, H, I, 2 * I, nt1, (uint16_t*)h, I,
-                       (uint16_t*)gu_saved);
+    GemmArgs g{};
+    g.A = (const uint16_t*)x_perm;
+    g.B = (const uint16_t*)gate_up;
+    g.C = (uint16_t*)h;
+    g.gu_out = (uint16_t*)gu_saved;
+    g.offsets = offsets;
+    g.E = E;
+    g.N = I;
+    g.K = H;
+    g.lda = H;
+    g.ldb = 2 * I;
+    g.ldc = I;
+    g.b_expert = (int64_t)H * 2 * I;
+    g.b_rows = H;
+    g.ntiles_n = (I + 127) / 128;
+    launch_generic<true, false, kEpiSwiglu, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
     const int64_t n1 = (int64_t)N * I;
     hipLaunchKernelGGL(grouped_ffn1_f32_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s,
@@ -396,16 +546,94 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
 hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int H, int I, int E, const int32_t* offsets,
                             void* y, hipStream_t s) {
   if (dt == kBF16) {
-    const int64_t mt_bound = ((int64_t)N + (int64_t)E * (kBM - 1)) / kBM;
-    const int nt2 = (H + kBN - 1) / kBN;
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(round_up8(mt_bound * nt2)), dim3(kGemmThreads), 0, s,
-                       (const uint16_t*)h, (const uint16_t*)down, offsets, E, I, H, H, nt2, (uint16_t*)y, H,
-                       (uint16_t*)nullptr);
+    GemmArgs g{};
+    g.A = (const uint16_t*)h;
+    g.B = (const uint16_t*)down;
+    g.C = (uint16_t*)y;
+    g.offsets = offsets;
+    g.E = E;
+    g.N = H;
+    g.K = I;
+    g.lda = I;
+    g.ldb = H;
+    g.ldc = H;
+    g.b_expert = (int64_t)I * H;
+    g.b_rows = I;
+    g.ntiles_n = (H + kBN - 1) / kBN;
+    launch_generic<true, false, kEpiStore, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
     const int64_t n2 = (int64_t)N * H;
     hipLaunchKernelGGL(grouped_ffn2_f32_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, (const float*)h,
                        (const float*)down, offsets, E, N, I, H, (float*)y);
   }
+  return hipGetLastError();
+}
+
+// ---- backward (bf16) --------------------------------------------------------------------------
+// dGU[r] = SwiGLU'(dY[r] down_e^T, g, u): rows grouped; A = dY (K = H contiguous), B = down_e rows
+// (n = i, K = H contiguous); epilogue writes dG into columns [0, I) and dU into [I, 2I).
+hipError_t launch_gemm_down_bwd(const void* d_y, const void* down, const void* gu_saved, int N, int H, int I, int E,
+                                const int32_t* offsets, void* d_gu, hipStream_t s) {
+  GemmArgs g{};
+  g.A = (const uint16_t*)d_y;
+  g.B = (const uint16_t*)down;
+  g.C = (uint16_t*)d_gu;
+  g.gu = (const uint16_t*)gu_saved;
+  g.offsets = offsets;
+  g.E = E;
+  g.N = I;
+  g.K = H;
+  g.lda = H;
+  g.ldb = H;
+  g.ldc = 2 * I;
+  g.b_expert = (int64_t)I * H;
+  g.b_rows = I;
+  g.ntiles_n = (I + kBN - 1) / kBN;
+  launch_generic<true, true, kEpiSwigluBwd, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+  return hipGetLastError();
+}
+
+// dX[r] = dGU[r] gate_up_e^T: rows grouped; A = dGU (K = 2I contiguous), B = gate_up_e rows (n = h).
+hipError_t launch_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, int N, int H, int I, int E,
+                                   const int32_t* offsets, void* d_x, hipStream_t s) {
+  GemmArgs g{};
+  g.A = (const uint16_t*)d_gu;
+  g.B = (const uint16_t*)gate_up;
+  g.C = (uint16_t*)d_x;
+  g.offsets = offsets;
+  g.E = E;
+  g.N = H;
+  g.K = 2 * I;
+  g.lda = 2 * I;
+  g.ldb = 2 * I;
+  g.ldc = H;
+  g.b_expert = (int64_t)H * 2 * I;
+  g.b_rows = H;
+  g.ntiles_n = (H + kBN - 1) / kBN;
+  launch_generic<true, true, kEpiStore, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+  return hipGetLastError();
+}
+
+// dW_e = P_e^T Q_e over the rows of expert e: P [rows, M] and Q [rows, Nq] both row-major, so both
+// are k-row tiles; the result block of expert e is [M, Nq] at dW + e * M * Nq. Every expert gets a
+// block (zeros when it has no rows).
+hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E, const int32_t* offsets, void* d_w,
+                             hipStream_t s) {
+  GemmArgs g{};
+  g.A = (const uint16_t*)P;
+  g.B = (const uint16_t*)Q;
+  g.C = (uint16_t*)d_w;
+  g.offsets = offsets;
+  g.E = E;
+  g.M = M;
+  g.N = Nq;
+  g.lda = M;
+  g.ldb = Nq;
+  g.ldc = Nq;
+  g.c_expert = (int64_t)M * Nq;
+  g.ntiles_m = (M + kBM - 1) / kBM;
+  g.ntiles_n = (Nq + kBN - 1) / kBN;
+  launch_generic<false, false, kEpiStore, kSchedWgrad>(g, (int64_t)E * g.ntiles_m * g.ntiles_n, s);
   return hipGetLastError();
 }
 

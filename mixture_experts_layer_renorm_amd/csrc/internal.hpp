@@ -31,6 +31,22 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
                                const int32_t* offsets, void* h, void* gu_saved, hipStream_t s);
 hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int H, int I, int E, const int32_t* offsets,
                             void* y, hipStream_t s);
+hipError_t launch_gemm_down_bwd(const void* d_y, const void* down, const void* gu_saved, int N, int H, int I, int E,
+                                const int32_t* offsets, void* d_gu, hipStream_t s);
+hipError_t launch_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, int N, int H, int I, int E,
+                                   const int32_t* offsets, void* d_x, hipStream_t s);
+hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E, const int32_t* offsets, void* d_w,
+                             hipStream_t s);
+
+// backward.hip
+hipError_t launch_combine_bwd(const void* d_out, const void* y, int dt, int T, int H, int k, const int32_t* row_of_slot,
+                              const float* topk_w, void* d_y, float* d_w, hipStream_t s);
+hipError_t launch_permute_bwd(const void* d_x_perm, int dt, int T, int H, int k, const int32_t* row_of_slot,
+                              const void* d_x_add, void* d_x, hipStream_t s);
+hipError_t launch_router_topk_bwd(const float* logits, const int32_t* idx, const float* w, const float* d_w, int T,
+                                  int E, int k, int renorm, float* d_logits, hipStream_t s);
+hipError_t launch_router_logits_bwd(const void* x, const void* w_gate, const float* d_logits, int dt, int T, int H,
+                                    int E, float* d_w_gate, const void* d_x_in, void* d_x, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const void* y, int dt, int T, int H, int k, const int32_t* row_of_slot, const float* topk_w,
