@@ -11,4 +11,4 @@ from .generators import (  # noqa: F401
     randint,
     permutation,
 )
-from .workloads import WORKLOADS, Workload, make_layer_inputs, make_ep_share_inputs  # noqa: F401
+from .workloads import WORKLOADS, Workload, make_ep_share_inputs, make_layer_inputs, workload_inputs  # noqa: F401

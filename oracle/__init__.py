@@ -56,6 +56,12 @@ def _dt(a) -> int:
     raise TypeError(f"oracle takes float32 or bf16 (uint16 bit patterns), got {a.dtype}")
 
 
+def _same_dt(*arrays):
+    if len({a.dtype for a in arrays}) != 1:
+        raise TypeError("oracle: these operands must share one data type: "
+                        + ", ".join(str(a.dtype) for a in arrays))
+
+
 def _c(a, dtype=None):
     return np.ascontiguousarray(a if dtype is None else a.astype(dtype, copy=False))
 
@@ -193,7 +199,7 @@ def combine_bwd(d_out, y, row_of_slot, topk_w, tokens=None):
     n = tokens.shape[0]
     d_y = np.empty((n, k, H), np.float64)
     d_w = np.empty((n, k), np.float64)
-    _call("orc_combine_bwd", _p(d_out), _p(y), _dt(y), I64(H), I64(k), _p(row_of_slot), _p(topk_w), _p(tokens),
+    _call("orc_combine_bwd", _p(d_out), _dt(d_out), _p(y), _dt(y), I64(H), I64(k), _p(row_of_slot), _p(topk_w), _p(tokens),
           I64(n), _p(d_y), _p(d_w))
     return d_y, d_w
 
@@ -208,7 +214,8 @@ def expert_rows_bwd(x_perm, d_y, offsets, gate_up, down, rows=None, want_gu=Fals
     n = rows.shape[0]
     d_x = np.empty((n, H), np.float64)
     d_gu = np.empty((n, 2 * I), np.float64) if want_gu else None
-    _call("orc_expert_rows_bwd", _p(x_perm), _p(d_y), _dt(x_perm), I64(H), I64(I), I64(E), _p(offsets),
+    _same_dt(x_perm, gate_up, down)
+    _call("orc_expert_rows_bwd", _p(x_perm), _p(d_y), _dt(x_perm), _dt(d_y), I64(H), I64(I), I64(E), _p(offsets),
           _p(gate_up), _p(down), _p(rows), I64(n), _p(d_x), _p(d_gu))
     return (d_x, d_gu) if want_gu else d_x
 
@@ -221,9 +228,28 @@ def expert_weight_grads(x_perm, d_y, offsets, gate_up, down, e):
     I = gate_up.shape[1] // 2
     dgu = np.empty((H, 2 * I), np.float64)
     ddn = np.empty((I, H), np.float64)
-    _call("orc_expert_weight_grads", _p(x_perm), _p(d_y), _dt(x_perm), I64(H), I64(I), I64(E), _p(offsets),
+    _same_dt(x_perm, gate_up, down)
+    _call("orc_expert_weight_grads", _p(x_perm), _p(d_y), _dt(x_perm), _dt(d_y), I64(H), I64(I), I64(E), _p(offsets),
           _p(gate_up), _p(down), I64(e), _p(dgu), _p(ddn))
     return dgu, ddn
+
+
+def expert_weight_grads_units(x_perm, d_y, offsets, gate_up, down, e, units):
+    """Entries of expert e's weight gradients for the intermediate units listed: returns
+    (d_gate_up[:, units], d_gate_up[:, I + units], d_down[units, :]) as fp64 [H,n], [H,n], [n,H]."""
+    x_perm, d_y, gate_up, down = _c(x_perm), _c(d_y), _c(gate_up), _c(down)
+    offsets = _c(offsets, np.int32)
+    units = _c(units, np.int64)
+    H = x_perm.shape[1]
+    E = offsets.shape[0] - 1
+    I = gate_up.shape[1] // 2
+    n = units.shape[0]
+    cols = np.empty((n, 2, H), np.float64)
+    rows = np.empty((n, H), np.float64)
+    _same_dt(x_perm, gate_up, down)
+    _call("orc_expert_weight_grads_units", _p(x_perm), _p(d_y), _dt(x_perm), _dt(d_y), I64(H), I64(I), I64(E), _p(offsets),
+          _p(gate_up), _p(down), I64(e), _p(units), I64(n), _p(cols), _p(rows))
+    return cols[:, 0].T.copy(), cols[:, 1].T.copy(), rows
 
 
 def permute_bwd(d_x_perm, row_of_slot, k, d_x_add=None, tokens=None):
@@ -264,15 +290,6 @@ def router_logits_bwd(x, w_gate, d_logits):
     return dwg, dx
 
 
-def _f32(a):
-    """bf16 bit patterns (uint16) -> float32, exactly; float32 and None pass through."""
-    if a is None or a.dtype == np.float32:
-        return a
-    if a.dtype == np.uint16:
-        return (np.ascontiguousarray(a).astype(np.uint32) << np.uint32(16)).view(np.float32)
-    raise TypeError(f"oracle takes float32 or bf16 (uint16 bit patterns), got {a.dtype}")
-
-
 def moe_backward(x, gate_up, down, k, d_out, w_gate=None, logits=None, renorm=True, shared_gate_up=None,
                  shared_down=None, experts=None):
     """Gradients of <d_out, layer(x)> along the layer, composed from the per-step backward functions
@@ -281,10 +298,7 @@ def moe_backward(x, gate_up, down, k, d_out, w_gate=None, logits=None, renorm=Tr
     the forward's. Returns a dict of fp64 arrays: d_x, d_logits, d_w_gate (None without w_gate),
     d_gate_up / d_down (only the experts listed in `experts`, default all, each [H, 2I] / [I, H]),
     d_shared_gate_up / d_shared_down, plus the intermediates d_w [T,k] and d_x_perm [N,H]."""
-    # every data tensor in fp32 (bf16 -> fp32 is exact), so that the per-step calls, which take one
-    # data type per call, can mix data inputs with the fp32 intermediates below
-    x, gate_up, down, d_out = _f32(x), _f32(gate_up), _f32(down), _f32(d_out)
-    w_gate, shared_gate_up, shared_down = _f32(w_gate), _f32(shared_gate_up), _f32(shared_down)
+    x = _c(x)
     T, H = x.shape
     E = gate_up.shape[0] // H
     I = gate_up.shape[1] // 2
@@ -318,3 +332,60 @@ def moe_backward(x, gate_up, down, k, d_out, w_gate=None, logits=None, renorm=Tr
     for e in experts:
         res["d_gate_up"][e], res["d_down"][e] = expert_weight_grads(xp, d_y32, offsets, gate_up, down, e)
     return res
+
+
+def moe_backward_tokens(x, gate_up, down, k, d_out, tokens, w_gate=None, logits=None, renorm=True,
+                        shared_gate_up=None, shared_down=None):
+    """moe_backward restricted to some tokens: the routing runs for every token (it is cheap), the
+    expert rows only for the listed tokens' slots. Returns fp64 d_x [n,H], d_logits [n,E], d_w [n,k]
+    for tokens in the order given; with the same inputs these equal moe_backward's rows."""
+    x = _c(x)
+    tokens = np.asarray(tokens, np.int64)
+    T, H = x.shape
+    E = gate_up.shape[0] // H
+    if logits is None:
+        logits = router_logits(x, w_gate)
+    idx, w = router_topk(logits, k, renorm)
+    _, offsets, ros, sor = permute_plan(idx, E)
+    xp = permute_rows(x, sor, k)
+    slots = (tokens[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    R = ros[slots].astype(np.int64)                      # the grouped rows of these tokens' slots
+    y_R = expert_rows(xp, offsets, gate_up, down, rows=R).astype(np.float32)
+    ros_c = np.full(T * k, -1, np.int32)                 # row map into the compact buffers
+    ros_c[slots] = np.arange(slots.shape[0], dtype=np.int32)
+    d_y_slots, d_w = combine_bwd(d_out, y_R, ros_c, w.astype(np.float32), tokens=tokens)
+    d_y = np.zeros((T * k, H), np.float32)
+    d_y[R] = d_y_slots.reshape(-1, H)
+    d_xp_R = expert_rows_bwd(xp, d_y, offsets, gate_up, down, rows=R).astype(np.float32)
+    d_x = permute_bwd(d_xp_R, ros_c, k, tokens=tokens)
+    if shared_gate_up is not None:
+        d_x = d_x + expert_rows_bwd(x, d_out, np.array([0, T], np.int32), shared_gate_up, shared_down, rows=tokens)
+    d_l = router_topk_bwd(logits[tokens], idx[tokens], d_w, renorm)
+    if w_gate is not None:
+        _, d_x_router = router_logits_bwd(x[tokens], w_gate, d_l)
+        d_x = d_x + d_x_router
+    return {"d_x": d_x, "d_logits": d_l, "d_w": d_w}
+
+
+def moe_weight_grads_units(x, gate_up, down, topk_idx, topk_w, d_out, e, units):
+    """Entries of the layer's d_gate_up / d_down for routed expert e and the listed intermediate
+    units, given the routing (topk_idx, topk_w) of the forward. Returns the same triple as
+    expert_weight_grads_units; equal to the matching entries of moe_backward's d_gate_up[e] /
+    d_down[e]."""
+    x = _c(x)
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E = gate_up.shape[0] // H
+    I = gate_up.shape[1] // 2
+    _, offsets, _, sor = permute_plan(topk_idx, E)
+    r0, r1 = int(offsets[e]), int(offsets[e + 1])
+    slots = sor[r0:r1].astype(np.int64)
+    xp_e = permute_rows(x, slots, k)                      # expert e's rows, in grouped order
+    # a row's d_y is its slot weight times its token's d_out (the combine's backward); it does not
+    # depend on y, so the combine backward runs with a placeholder y and its d_w is not used
+    d_y_slots, _ = combine_bwd(d_out, np.zeros((1, H), np.float32), np.zeros(T * k, np.int32),
+                               _c(topk_w, np.float32), tokens=slots // k)
+    d_y_e = d_y_slots[np.arange(slots.shape[0]), slots % k].astype(np.float32)
+    seg = np.array([0, r1 - r0], np.int32)
+    return expert_weight_grads_units(xp_e, d_y_e, seg, gate_up[e * H:(e + 1) * H], down[e * I:(e + 1) * I], 0,
+                                     units)

@@ -261,10 +261,11 @@ int orc_moe_forward_tokens(const void* x, int dt, int64_t H, int64_t I, int64_t 
 
 /* ------------------------------------------------------------------------------------------ */
 /* Backward.                                                                                   */
-int orc_combine_bwd(const void* d_out, const void* y, int dt, int64_t H, int64_t k,
+int orc_combine_bwd(const void* d_out, int dt, const void* y, int dt_y, int64_t H, int64_t k,
                     const int32_t* row_of_slot, const float* topk_w, const int64_t* tokens,
                     int64_t ntok, double* d_y_slots, double* d_w) {
-    if (!d_out || !y || !row_of_slot || !topk_w || !tokens || bad_dt(dt) || H < 1 || k < 1 || ntok < 0)
+    if (!d_out || !y || !row_of_slot || !topk_w || !tokens || bad_dt(dt) || bad_dt(dt_y) || H < 1 || k < 1 ||
+        ntok < 0)
         return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < ntok; ++n) {
@@ -277,7 +278,7 @@ int orc_combine_bwd(const void* d_out, const void* y, int dt, int64_t H, int64_t
                 const double go = eld(d_out, dt, t * H + c);
                 /* a dropped slot (no row) takes no part in the combine: zero gradients */
                 if (d_y_slots) d_y_slots[(n * k + j) * H + c] = r < 0 ? 0.0 : w * go;
-                if (r >= 0) dot += go * eld(y, dt, r * H + c);
+                if (r >= 0) dot += go * eld(y, dt_y, r * H + c);
             }
             if (d_w) d_w[n * k + j] = dot;
         }
@@ -319,10 +320,10 @@ static void ffn_row_bwd(const double* xr, const double* dyr, int dt, const void*
     }
 }
 
-int orc_expert_rows_bwd(const void* x_perm, const void* d_y, int dt, int64_t H, int64_t I,
+int orc_expert_rows_bwd(const void* x_perm, const void* d_y, int dt, int dt_dy, int64_t H, int64_t I,
                         int64_t E, const int32_t* offsets, const void* gate_up, const void* down,
                         const int64_t* rows, int64_t nrows, double* d_x_out, double* d_gu_out) {
-    if (!x_perm || !d_y || !offsets || !gate_up || !down || !rows || !d_x_out || bad_dt(dt) || H < 1 ||
+    if (!x_perm || !d_y || !offsets || !gate_up || !down || !rows || !d_x_out || bad_dt(dt) || bad_dt(dt_dy) || H < 1 ||
         I < 1 || E < 1 || nrows < 0)
         return -1;
     for (int64_t n = 0; n < nrows; ++n)
@@ -342,7 +343,7 @@ int orc_expert_rows_bwd(const void* x_perm, const void* d_y, int dt, int64_t H, 
             const int64_t e = expert_of_row(offsets, E, r);
             for (int64_t h = 0; h < H; ++h) {
                 xr[h] = eld(x_perm, dt, r * H + h);
-                dyr[h] = eld(d_y, dt, r * H + h);
+                dyr[h] = eld(d_y, dt_dy, r * H + h);
             }
             ffn_row_bwd(xr, dyr, dt, gate_up, e * H * 2 * I, down, e * I * H, H, I, g, u, da, dg, du,
                         d_x_out + n * H);
@@ -362,10 +363,10 @@ int orc_expert_rows_bwd(const void* x_perm, const void* d_y, int dt, int64_t H, 
     return 0;
 }
 
-int orc_expert_weight_grads(const void* x_perm, const void* d_y, int dt, int64_t H, int64_t I,
+int orc_expert_weight_grads(const void* x_perm, const void* d_y, int dt, int dt_dy, int64_t H, int64_t I,
                             int64_t E, const int32_t* offsets, const void* gate_up,
                             const void* down, int64_t e, double* d_gate_up_e, double* d_down_e) {
-    if (!x_perm || !d_y || !offsets || !gate_up || !down || !d_gate_up_e || !d_down_e || bad_dt(dt) ||
+    if (!x_perm || !d_y || !offsets || !gate_up || !down || !d_gate_up_e || !d_down_e || bad_dt(dt) || bad_dt(dt_dy) ||
         H < 1 || I < 1 || e < 0 || e >= E)
         return -1;
     const int64_t r0 = offsets[e], r1 = offsets[e + 1];
@@ -386,7 +387,7 @@ int orc_expert_weight_grads(const void* x_perm, const void* d_y, int dt, int64_t
             const int64_t r = r0 + q;
             for (int64_t h = 0; h < H; ++h) {
                 xr[h] = eld(x_perm, dt, r * H + h);
-                dyr[h] = eld(d_y, dt, r * H + h);
+                dyr[h] = eld(d_y, dt_dy, r * H + h);
             }
             ffn_row_bwd(xr, dyr, dt, gate_up, e * H * 2 * I, down, e * I * H, H, I, g, u, da,
                         DG + q * 2 * I, DG + q * 2 * I + I, dx);
@@ -416,11 +417,55 @@ int orc_expert_weight_grads(const void* x_perm, const void* d_y, int dt, int64_t
         for (int64_t c = 0; c < H; ++c) o[c] = 0.0;
         for (int64_t q = 0; q < n; ++q) {
             const double ai = A[q * I + i];
-            for (int64_t c = 0; c < H; ++c) o[c] += ai * eld(d_y, dt, (r0 + q) * H + c);
+            for (int64_t c = 0; c < H; ++c) o[c] += ai * eld(d_y, dt_dy, (r0 + q) * H + c);
         }
     }
     free(A);
     free(DG);
+    return 0;
+}
+
+/* The same weight gradients restricted to a few intermediate units i (columns i and I+i of
+ * d_gate_up_e, row i of d_down_e): each unit's entries depend only on that unit's pre-activations,
+ * so they can be computed one unit at a time over all rows of the expert. Rows ascending. */
+int orc_expert_weight_grads_units(const void* x_perm, const void* d_y, int dt, int dt_dy, int64_t H, int64_t I,
+                                  int64_t E, const int32_t* offsets, const void* gate_up,
+                                  const void* down, int64_t e, const int64_t* units, int64_t nunits,
+                                  double* d_gate_up_cols, double* d_down_rows) {
+    if (!x_perm || !d_y || !offsets || !gate_up || !down || !units || !d_gate_up_cols || !d_down_rows ||
+        bad_dt(dt) || bad_dt(dt_dy) || H < 1 || I < 1 || e < 0 || e >= E || nunits < 0)
+        return -1;
+    for (int64_t q = 0; q < nunits; ++q)
+        if (units[q] < 0 || units[q] >= I) return -2;
+    const int64_t r0 = offsets[e], r1 = offsets[e + 1];
+    const int64_t gu_off = e * H * 2 * I, dn_off = e * I * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nunits; ++q) {
+        const int64_t i = units[q];
+        double* dgc = d_gate_up_cols + q * 2 * H; /* [H] gate column, then [H] up column */
+        double* duc = dgc + H;
+        double* ddr = d_down_rows + q * H;
+        for (int64_t h = 0; h < H; ++h) dgc[h] = duc[h] = ddr[h] = 0.0;
+        for (int64_t r = r0; r < r1; ++r) {
+            double g = 0.0, u = 0.0, da = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                const double xh = eld(x_perm, dt, r * H + h);
+                g += xh * eld(gate_up, dt, gu_off + h * 2 * I + i);
+                u += xh * eld(gate_up, dt, gu_off + h * 2 * I + I + i);
+            }
+            for (int64_t c = 0; c < H; ++c) da += eld(d_y, dt_dy, r * H + c) * eld(down, dt, dn_off + i * H + c);
+            const double sg = sigmoid(g);
+            const double dg = da * u * sg * (1.0 + g * (1.0 - sg));
+            const double du = da * g * sg;
+            const double a = silu(g) * u;
+            for (int64_t h = 0; h < H; ++h) {
+                const double xh = eld(x_perm, dt, r * H + h);
+                dgc[h] += xh * dg;
+                duc[h] += xh * du;
+                ddr[h] += a * eld(d_y, dt_dy, r * H + h);
+            }
+        }
+    }
     return 0;
 }
 

@@ -73,25 +73,35 @@ int orc_moe_forward_tokens(const void* x, int dt, int64_t H, int64_t I, int64_t 
                            const void* down, const void* shared_gate_up, const void* shared_down,
                            int64_t Is, const int64_t* tokens, int64_t ntok, double* out);
 
-/* ---- backward (loss L with dL/dout = d_out) ---- */
+/* ---- backward (loss L with dL/dout = d_out) ----
+ * The incoming gradients (d_y, and y in the combine backward) carry their own data type, so that
+ * fp32 intermediates can meet bf16 parameters. */
 
 /* d_y[t*k+j] = w[t,j] * d_out[t];  d_w[t,j] = <d_out[t], y[row_of_slot[t*k+j]]> */
-int orc_combine_bwd(const void* d_out, const void* y, int dt, int64_t H, int64_t k,
+int orc_combine_bwd(const void* d_out, int dt, const void* y, int dt_y, int64_t H, int64_t k,
                     const int32_t* row_of_slot, const float* topk_w, const int64_t* tokens,
                     int64_t ntok, double* d_y_slots, double* d_w);
 
 /* Per grouped row r: da = d_y[r] @ down_e^T; dg = da*u*s*(1+g*(1-s)), du = da*g*s (s = sigmoid g);
  * d_x[r] = dg @ gate_up_e[:, :I]^T + du @ gate_up_e[:, I:]^T.  Outputs fp64: d_x_out [nrows,H],
  * d_gu_out [nrows, 2I] (dg then du) when non-null. */
-int orc_expert_rows_bwd(const void* x_perm, const void* d_y, int dt, int64_t H, int64_t I,
+int orc_expert_rows_bwd(const void* x_perm, const void* d_y, int dt, int dt_dy, int64_t H, int64_t I,
                         int64_t E, const int32_t* offsets, const void* gate_up, const void* down,
                         const int64_t* rows, int64_t nrows, double* d_x_out, double* d_gu_out);
 
 /* Weight gradients of expert e: d_gate_up_e [H, 2I] = sum_r x_perm[r]^T (dg|du)[r],
  * d_down_e [I, H] = sum_r a[r]^T d_y[r], over rows r of expert e (zeros when it has none). */
-int orc_expert_weight_grads(const void* x_perm, const void* d_y, int dt, int64_t H, int64_t I,
+int orc_expert_weight_grads(const void* x_perm, const void* d_y, int dt, int dt_dy, int64_t H, int64_t I,
                             int64_t E, const int32_t* offsets, const void* gate_up,
                             const void* down, int64_t e, double* d_gate_up_e, double* d_down_e);
+
+/* The entries of expert e's weight gradients that belong to intermediate units[q] (0 <= q < nunits):
+ * d_gate_up_cols [nunits, 2, H] = columns units[q] and I+units[q] of d_gate_up_e,
+ * d_down_rows [nunits, H] = row units[q] of d_down_e. */
+int orc_expert_weight_grads_units(const void* x_perm, const void* d_y, int dt, int dt_dy, int64_t H, int64_t I,
+                                  int64_t E, const int32_t* offsets, const void* gate_up,
+                                  const void* down, int64_t e, const int64_t* units, int64_t nunits,
+                                  double* d_gate_up_cols, double* d_down_rows);
 
 /* d_x[t] = sum_j d_x_perm[row_of_slot[t*k+j]] (+ d_x_add[t]) */
 int orc_permute_bwd(const void* d_x_perm, int dt, int64_t H, int64_t k, const int32_t* row_of_slot,

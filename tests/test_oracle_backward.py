@@ -239,3 +239,47 @@ def test_moe_backward_bf16_inputs_equal_their_fp32_values():
         np.testing.assert_array_equal(rb[key], rf[key])
     for e in range(E):
         np.testing.assert_array_equal(rb["d_gate_up"][e], rf["d_gate_up"][e])
+
+
+def test_weight_grad_units_match_full_weight_grads():
+    T, H, I, E, k = 40, 24, 12, 3, 2
+    d = make_layer_inputs(T, H, I, E, k, "bf16", (928,), w_std=0.3, backward=True)
+    counts = np.array([30, 0, 50], np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xp = normal((80, H), 1.0, (928, 1), "bf16")
+    dy = normal((80, H), 1.0, (928, 2), "bf16")
+    units = np.array([0, 5, 11, 3])
+    for e in range(E):
+        dgu, ddn = oracle.expert_weight_grads(xp, dy, offsets, d["gate_up"], d["down"], e)
+        g, u, r = oracle.expert_weight_grads_units(xp, dy, offsets, d["gate_up"], d["down"], e, units)
+        np.testing.assert_allclose(g, dgu[:, units], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(u, dgu[:, I + units], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(r, ddn[units], rtol=1e-12, atol=1e-14)
+        if counts[e] == 0:
+            assert not g.any() and not u.any() and not r.any()
+
+
+@pytest.mark.parametrize("renorm,shared", [(True, 1), (False, 0)])
+def test_backward_tokens_match_full_backward(renorm, shared):
+    T, H, I, E, k = 30, 16, 8, 6, 3
+    d = make_layer_inputs(T, H, I, E, k, "bf16", (929,), w_std=0.3, wg_std=0.3, shared=shared, backward=True)
+    kw = dict(w_gate=d["w_gate"], renorm=renorm, shared_gate_up=d.get("shared_gate_up"),
+              shared_down=d.get("shared_down"))
+    full = oracle.moe_backward(d["x"], d["gate_up"], d["down"], k, d["d_out"], **kw)
+    toks = np.array([7, 0, 29, 13])
+    part = oracle.moe_backward_tokens(d["x"], d["gate_up"], d["down"], k, d["d_out"], toks, **kw)
+    for key in ("d_x", "d_logits", "d_w"):
+        np.testing.assert_allclose(part[key], full[key][toks], rtol=1e-12, atol=1e-13)
+
+
+def test_layer_weight_grad_units_match_full_backward():
+    T, H, I, E, k = 40, 16, 8, 6, 2
+    d = make_layer_inputs(T, H, I, E, k, "bf16", (930,), w_std=0.3, wg_std=0.3, backward=True)
+    full = oracle.moe_backward(d["x"], d["gate_up"], d["down"], k, d["d_out"], w_gate=d["w_gate"])
+    idx, w = oracle.router_topk(oracle.router_logits(d["x"], d["w_gate"]), k)
+    units = np.array([6, 1, 7])
+    for e in range(E):
+        g, u, r = oracle.moe_weight_grads_units(d["x"], d["gate_up"], d["down"], idx, w, d["d_out"], e, units)
+        np.testing.assert_allclose(g, full["d_gate_up"][e][:, units], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(u, full["d_gate_up"][e][:, I + units], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(r, full["d_down"][e][units], rtol=1e-12, atol=1e-14)
