@@ -77,20 +77,23 @@ template <int NT>
 __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offsets, int E, int bm, int ntiles_n,
                                               int* s_pref, int* s_wtot, int* s_e, TileInfo& ti) {
   const int tid = threadIdx.x;
-  const int G = gridDim.x;  // a multiple of 8
   const int b = blockIdx.x;
-  // consecutive logical tiles land on the same XCD (blocks are dealt round-robin over 8 XCDs),
-  // so the column tiles of one row tile share its rows through that XCD's L2
-  const int L = (b & 7) * (G >> 3) + (b >> 3);
-  const int mt_g = L / ntiles_n;
-  ti.nt = L - mt_g * ntiles_n;
   for (int e = tid; e < E; e += NT) {
     const int n = offsets[e + 1] - offsets[e];
     s_pref[e] = n > 0 ? (n + bm - 1) / bm : 0;
   }
   __syncthreads();
   block_exclusive_scan<NT>(s_pref, E, s_wtot);
-  if (mt_g >= s_pref[E]) return false;
+  // The grid is sized for the worst row distribution; only the first `total` tiles exist. Blocks
+  // are dealt round-robin over the 8 XCDs, so block b runs on XCD b % 8: give XCD x the
+  // contiguous tile range [x Q, (x+1) Q) with Q = ceil(total / 8), which keeps the column tiles
+  // of one row tile (and the row tiles of one expert) in one XCD's L2 and uses every XCD.
+  const int total = s_pref[E] * ntiles_n;
+  const int Q = (total + 7) >> 3;
+  const int L = (b & 7) * Q + (b >> 3);
+  if ((b >> 3) >= Q || L >= total) return false;
+  const int mt_g = L / ntiles_n;
+  ti.nt = L - mt_g * ntiles_n;
   for (int e = tid; e < E; e += NT)
     if (s_pref[e] <= mt_g && mt_g < s_pref[e + 1]) *s_e = e;
   __syncthreads();
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = (wave >> 1) & 3, wn = wave & 1;  // a tile with few rows still spreads over two SIMDs
 
   // ---- tile, rows and K of this workgroup
   int e, m0, n0, mvalid, K, nt;
