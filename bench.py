@@ -1,14 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE expert layer on one MI355X.
 
-One step = one forward pass of the whole layer over one batch of synthetic tokens already resident
-in HBM: router logits -> top-k/renormalise -> permute -> grouped GEMM + SwiGLU -> grouped GEMM ->
-unpermute/combine, each a call into libmoe_rocm.so on the current stream.
+One step = one pass of the whole layer over one batch of synthetic tokens already resident in HBM,
+each stage a call into libmoe_rocm.so on the current stream:
+  forward:  router logits -> top-k/renormalise -> permute -> grouped GEMM + SwiGLU -> grouped GEMM
+            -> unpermute/combine (+ the shared expert, run as a one-segment grouped FFN, when the
+            workload has one);
+  backward (workloads with a backward pass): combine-bwd -> grouped FFN bwd (+ shared expert) ->
+            top-k bwd -> router-logits bwd -> permute-bwd.
 
 Prints ONE JSON line. `value` is tokens/s of the layer. The timed region is bracketed by
-torch.cuda.synchronize(); HIP events between the calls give each step's per-kernel durations,
-from which the roofline of the dominant kernel (the gate_up grouped GEMM) is computed.
-The CPU baseline is the oracle (C, fp64, OpenMP) timed on a bounded sample of the same tokens.
+torch.cuda.synchronize(); HIP events recorded on the launch stream between the calls give each
+stage's duration, from which the roofline of the dominant kernel (the gate_up grouped GEMM) is
+computed. The CPU baseline is the oracle (C, fp64, OpenMP) timed on a bounded sample of the same
+tokens. --copy-calibration runs one 512 MiB device-to-device copy first, the known-size kernel
+that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters into HBM bytes.
 """
 from __future__ import annotations
 
@@ -79,7 +85,7 @@ def cpu_baseline(wl, d, budget_s: float):
     el = time.perf_counter() - t0
     return {"value": round(done / el, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {done} of {wl.T} tokens of {wl.name} (router logits + top-k + per-token "
-                      f"SwiGLU experts + combine, fp64), {el:.1f} s"}
+                      f"SwiGLU experts + combine, fp64{', forward only' if wl.backward else ''}), {el:.1f} s"}
 
 
 def main():
@@ -87,8 +93,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32"])
+    ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 512 MiB device copy before the warm-up (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
@@ -114,51 +122,95 @@ def main():
     down = dev(d["down"], torch)
     w_gate = dev(d["w_gate"], torch) if "w_gate" in d else None
     given_logits = dev(d["logits"], torch) if "logits" in d else None
+    sh_gu = dev(d["shared_gate_up"], torch) if "shared_gate_up" in d else None
+    sh_dn = dev(d["shared_down"], torch) if "shared_down" in d else None
+    d_out = dev(d["d_out"], torch) if "d_out" in d else None
     tdt = x.dtype
-    bufs = moe.LayerBuffers(T, H, I, E, k, tdt, x.device, logits=given_logits is None)
+    I_sh = 0 if sh_gu is None else sh_gu.shape[1] // 2
+    bufs = moe.LayerBuffers(T, H, I, E, k, tdt, x.device, logits=given_logits is None, gu_saved=wl.backward,
+                            I_shared=I_sh)
+    grads = moe.LayerGrads(T, H, I, E, k, tdt, x.device, I_shared=I_sh, router=w_gate is not None) if wl.backward else None
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=x.device).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    names = ["router_logits", "router_topk", "permute", "gemm_gate_up", "gemm_down", "combine"]
+    # the stages of one step, in order; HIP events go between them
+    sh = bufs.shared
+    stages = []
+    if given_logits is None:
+        stages.append(("router_logits", lambda: moe.moe_router_logits(x, w_gate, bufs.logits)))
+    logits = bufs.logits if given_logits is None else given_logits
+    stages += [
+        ("router_topk", lambda: moe.moe_router_topk(logits, k, True, bufs.topk_idx, bufs.topk_w)),
+        ("permute", lambda: moe.moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace)),
+        ("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu(bufs.x_perm, gate_up, bufs.plan.offsets, bufs.h,
+                                                             bufs.gu_saved)),
+        ("gemm_down", lambda: moe.moe_grouped_gemm_down(bufs.h, down, bufs.plan.offsets, bufs.y)),
+    ]
+    if sh is not None:
+        stages.append(("shared_ffn", lambda: moe.moe_grouped_swiglu_ffn(x, sh_gu, sh_dn, sh["offsets"], sh["h"], sh["y"],
+                                                                         sh["gu_saved"])))
+    stages.append(("combine", lambda: moe.moe_unpermute_combine(bufs.y, bufs.plan.row_of_slot, bufs.topk_w,
+                                                                None if sh is None else sh["y"], bufs.out)))
+    if grads is not None:
+        g = grads
+        stages += [
+            ("combine_bwd", lambda: moe.moe_unpermute_combine_bwd(d_out, bufs.y, bufs.plan.row_of_slot, bufs.topk_w,
+                                                                  g.d_y, g.d_w)),
+            ("ffn_bwd", lambda: moe.moe_grouped_swiglu_ffn_bwd(g.d_y, bufs.x_perm, bufs.gu_saved, bufs.h, gate_up, down,
+                                                               bufs.plan.offsets, g.d_x_perm, g.d_gate_up, g.d_down,
+                                                               g.d_gu)),
+        ]
+        if sh is not None:
+            stages.append(("shared_ffn_bwd", lambda: moe.moe_grouped_swiglu_ffn_bwd(
+                d_out, x, sh["gu_saved"], sh["h"], sh_gu, sh_dn, sh["offsets"], g.d_x_side, g.d_shared_gate_up,
+                g.d_shared_down, g.d_shared_gu)))
+        stages.append(("router_topk_bwd", lambda: moe.moe_router_topk_bwd(logits, bufs.topk_idx, bufs.topk_w, g.d_w, True,
+                                                                          g.d_logits)))
+        side = g.d_x_side if sh is not None else None
+        if w_gate is not None:
+            dst = g.d_x_side2 if sh is not None else g.d_x_side
+            stages.append(("router_logits_bwd", lambda: moe.moe_router_logits_bwd(x, w_gate, g.d_logits, g.d_w_gate,
+                                                                                  d_x_in=side, d_x=dst)))
+            side = dst
+        stages.append(("permute_bwd", lambda: moe.moe_permute_bwd(g.d_x_perm, bufs.plan.row_of_slot, T, k,
+                                                                  d_x_add=side, d_x=g.d_x)))
+    names = [n for n, _ in stages]
+    ns = len(stages)
 
     def step(evs=None):
-        def mark(i):
+        for i, (_, fn) in enumerate(stages):
             if evs is not None:
                 evs[i].record(stream)
-        mark(0)
-        logits = given_logits
-        if logits is None:
-            logits = moe.moe_router_logits(x, w_gate, bufs.logits)
-        mark(1)
-        moe.moe_router_topk(logits, k, True, bufs.topk_idx, bufs.topk_w)
-        mark(2)
-        moe.moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace)
-        mark(3)
-        moe.moe_grouped_gemm_swiglu(bufs.x_perm, gate_up, bufs.plan.offsets, bufs.h)
-        mark(4)
-        moe.moe_grouped_gemm_down(bufs.h, down, bufs.plan.offsets, bufs.y)
-        mark(5)
-        moe.moe_unpermute_combine(bufs.y, bufs.plan.row_of_slot, bufs.topk_w, None, bufs.out)
-        mark(6)
+            fn()
+        if evs is not None:
+            evs[ns].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg = np.zeros(6)
+    seg = np.zeros(ns)
     total_ev = 0.0
     for evs in events:
-        for i in range(6):
+        for i in range(ns):
             seg[i] += evs[i].elapsed_time(evs[i + 1])
-        total_ev += evs[0].elapsed_time(evs[6])
+        total_ev += evs[0].elapsed_time(evs[ns])
     seg /= args.steps
     ms_per_step = max(wall * 1e3 / args.steps, total_ev / args.steps)
     tokens_per_s = T / (ms_per_step / 1e3)
+    t_of = {n: seg[i] * 1e-3 for i, n in enumerate(names)}
 
     counts = bufs.plan.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
@@ -170,7 +222,7 @@ def main():
     dn_bytes = n_active * I * H * b + N * I * b + N * H * b
     perm_bytes = T * H * b + N * H * b + T * k * 4 * 3 + E * 4 * 2
     comb_bytes = N * H * b + T * H * b + T * k * 8
-    t_gu, t_dn = seg[3] * 1e-3, seg[4] * 1e-3
+    t_gu, t_dn = t_of["gemm_gate_up"], t_of["gemm_down"]
     peak_tf = PEAK_BF16_TFLOPS if tdt == torch.bfloat16 else PEAK_F32_TFLOPS
     ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
     if gu_flops / gu_bytes < ridge:
@@ -179,14 +231,12 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gu_flops / t_gu / 1e12, 1), "peak": peak_tf, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = load_traffic(wl.name)
-    roof["kernel"] = "grouped_gemm_bf16_kernel<0> (gate_up + SwiGLU)"
+    roof["kernel"] = "grouped_gemm_bf16_kernel<true, false, 0, 0> (gate_up + SwiGLU)"
     roof["algorithmic_bytes"] = gu_bytes
     roof["algorithmic_flops"] = gu_flops
-    roof["avg_launch_us"] = round(seg[3] * 1e3, 2)
+    roof["avg_launch_us"] = round(t_gu * 1e6, 2)
 
     breakdown = {n: round(seg[i] * 1e3, 2) for i, n in enumerate(names)}
-    if given_logits is not None:
-        breakdown["router_logits"] = 0.0
     perf = {
         "kernel_us": breakdown,
         "grouped_gemm_mfma_util_pct": round(100 * (gu_flops + dn_flops) / (t_gu + t_dn) / (peak_tf * 1e12), 2),
@@ -194,8 +244,8 @@ def main():
         "gemm_down_tflops": round(dn_flops / t_dn / 1e12, 1),
         "gemm_gate_up_hbm_gbs": round(gu_bytes / t_gu / 1e9, 1),
         "gemm_down_hbm_gbs": round(dn_bytes / t_dn / 1e9, 1),
-        "permute_hbm_gbs": round(perm_bytes / (seg[2] * 1e-3) / 1e9, 1),
-        "combine_hbm_gbs": round(comb_bytes / (seg[5] * 1e-3) / 1e9, 1),
+        "permute_hbm_gbs": round(perm_bytes / t_of["permute"] / 1e9, 1),
+        "combine_hbm_gbs": round(comb_bytes / t_of["combine"] / 1e9, 1),
         "active_experts": n_active,
     }
     line = {
@@ -204,7 +254,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if tdt == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "k": k, "renorm": True,
-                   "router": "logits given" if given_logits is not None else "x @ W_g"},
+                   "router": "logits given" if given_logits is not None else "x @ W_g",
+                   "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward"},
         "roofline": roof, "perf": perf,
     }
     if args.cpu_seconds > 0:
