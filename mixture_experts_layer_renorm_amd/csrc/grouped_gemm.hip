@@ -52,6 +52,13 @@ constexpr int kDmaPerWave = (kTileA + kTileB) / 1024 / kWaves;  // 1 KB per wave
 constexpr int kDmaA = kTileA / 1024 / kWaves;  // DMA instructions per wave per step, operand A
 constexpr int kDmaB = kTileB / 1024 / kWaves;  // and operand B
 constexpr int kGemmMaxE = 1024;
+// Row-grouped products: a tile holds up to kBMX = 288 rows, the regular 256 plus an extra band of
+// up to 32 rows, so an expert with 257..288 rows (common at E = 128, k = 8, T = 4096, where counts
+// sit around 256 +- 16) is one tile instead of a full tile plus a nearly empty one that streams the
+// same weight panel again. The extra band is spread over the eight waves as one 32-row block each,
+// against a 32-column slice (16 gate + 16 up output columns in the SwiGLU case).
+constexpr int kBMX = kBM + 32;
+constexpr int kTileAX = kBMX * kBK * 2;   // 18 KB: 18 DMA instructions, 2 per wave + 1 for waves 0, 1
 
 // LDS swizzles, applied when choosing which global chunk each DMA lane fetches. They keep the
 // fragment reads free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
@@ -72,6 +79,8 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 struct TileInfo {
   int e, row0, row_end, nt;
 };
+
+// An expert with c rows gets ceil(c / bm) tiles of near-equal height.
 
 template <int NT>
 __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offsets, int E, int bm, int ntiles_n,
@@ -98,8 +107,11 @@ __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offset
     if (s_pref[e] <= mt_g && mt_g < s_pref[e + 1]) *s_e = e;
   __syncthreads();
   ti.e = __builtin_amdgcn_readfirstlane(*s_e);
-  ti.row0 = __builtin_amdgcn_readfirstlane(offsets[ti.e] + (mt_g - s_pref[ti.e]) * bm);
-  ti.row_end = __builtin_amdgcn_readfirstlane(min(ti.row0 + bm, (int)offsets[ti.e + 1]));
+  const int p0 = __builtin_amdgcn_readfirstlane(s_pref[ti.e]), p1 = __builtin_amdgcn_readfirstlane(s_pref[ti.e + 1]);
+  const int j = mt_g - p0, nte = p1 - p0;
+  const int o0 = offsets[ti.e], c = offsets[ti.e + 1] - o0;
+  ti.row0 = __builtin_amdgcn_readfirstlane(o0 + (int)((int64_t)j * c / nte));
+  ti.row_end = __builtin_amdgcn_readfirstlane(o0 + (int)((int64_t)(j + 1) * c / nte));
   return true;
 }
 
@@ -124,13 +136,83 @@ struct GemmArgs {
   int ntiles_m, ntiles_n;
 };
 
+// dL/dh -> (dL/dg, dL/du) for four consecutive columns of row m, with s = sigmoid(g):
+// dL/dg = v * u * s * (1 + g (1 - s)), dL/du = v * g * s; writes dG | dU into C (row stride ldc).
+__device__ __forceinline__ void store_swiglu_bwd(const GemmArgs& g, uint16_t* cbase, int64_t m, int col,
+                                                 const float* v) {
+  const uint16_t* gr = g.gu + m * 2 * g.N;
+  const uint2 gp = *reinterpret_cast<const uint2*>(gr + col);
+  const uint2 up = *reinterpret_cast<const uint2*>(gr + g.N + col);
+  const float gv[4] = {bf16_to_f32(gp.x & 0xffffu), bf16_to_f32(gp.x >> 16), bf16_to_f32(gp.y & 0xffffu),
+                       bf16_to_f32(gp.y >> 16)};
+  const float uv[4] = {bf16_to_f32(up.x & 0xffffu), bf16_to_f32(up.x >> 16), bf16_to_f32(up.y & 0xffffu),
+                       bf16_to_f32(up.y >> 16)};
+  float dg[4], du[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const float sg = 1.0f / (1.0f + __expf(-gv[qq]));
+    dg[qq] = v[qq] * uv[qq] * sg * (1.0f + gv[qq] * (1.0f - sg));
+    du[qq] = v[qq] * gv[qq] * sg;
+  }
+  uint16_t* dr = cbase + m * g.ldc;
+  *reinterpret_cast<uint2*>(dr + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+  *reinterpret_cast<uint2*>(dr + g.N + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+}
+
+// Epilogue of the extra band (row-grouped products): lane holds tile row 256 + (lane & 31) and, for
+// accumulator element q, slice column (q / 4) * 8 + (lane / 32) * 4 + q % 4: gate columns 0..15
+// and up columns 16..31 of the SwiGLU slice g0, else columns wn*128 + wm*32 + 0..31.
+template <int EPI>
+__device__ __forceinline__ void store_extra(const GemmArgs& g, const f32x16& acc, int m0, int mvalid, int n0, int nt,
+                                            int g0, int wm, int wn, int lane) {
+  const int mloc = kBM + (lane & 31);
+  if (mloc >= mvalid) return;
+  const int64_t m = m0 + mloc;
+  if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+    for (int gq = 0; gq < 2; ++gq) {
+      const int col = nt * 128 + g0 + gq * 8 + (lane >> 5) * 4;
+      if (col >= g.N) continue;
+      float hv[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[gq * 4 + qq]) * acc[(gq + 2) * 4 + qq];
+      *reinterpret_cast<uint2*>(g.C + m * g.ldc + col) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      if (g.gu_out) {
+        uint16_t* gs = g.gu_out + m * 2 * g.N;
+        *reinterpret_cast<uint2*>(gs + col) =
+            make_uint2(pack_bf16x2(acc[gq * 4 + 0], acc[gq * 4 + 1]), pack_bf16x2(acc[gq * 4 + 2], acc[gq * 4 + 3]));
+        *reinterpret_cast<uint2*>(gs + g.N + col) = make_uint2(pack_bf16x2(acc[gq * 4 + 8], acc[gq * 4 + 9]),
+                                                               pack_bf16x2(acc[gq * 4 + 10], acc[gq * 4 + 11]));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int col = n0 + wn * 128 + wm * 32 + gq * 8 + (lane >> 5) * 4;
+      if (col >= g.N) continue;
+      float v[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) v[qq] = acc[gq * 4 + qq];
+      if constexpr (EPI == kEpiSwigluBwd) {
+        store_swiglu_bwd(g, g.C, m, col, v);
+      } else {
+        *reinterpret_cast<uint2*>(g.C + m * g.ldc + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  }
+}
+
 // A_ROWS: A is a row tile (K contiguous) - else a k-row tile (M contiguous).
 // B_ROWS: B is a row tile (K contiguous) - else a k-row tile (N contiguous).
 template <bool A_ROWS, bool B_ROWS, int EPI, int SCHED>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const GemmArgs g) {
+  constexpr bool ROWS = SCHED == kSchedRows;
+  constexpr int TA = ROWS ? kTileAX : kTileA;
+  constexpr int DPW = ROWS ? kDmaPerWave + 1 : kDmaPerWave;  // DMA instructions per wave per step
   // one LDS object per ring slot, so that the compiler can tell a DMA into one slot from reads of another
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA], sA1[kTileA], sA2[kTileA], sA3[kTileA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TA], sA1[TA], sA2[TA], sA3[TA];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sSpare[ROWS ? 1024 : 16];
   __shared__ int s_pref[kGemmMaxE + 1];
   __shared__ int s_wtot[kGemmThreads / kWave];
   __shared__ int s_e;
@@ -147,7 +229,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   int a_records, b_records;
   if constexpr (SCHED == kSchedRows) {
     TileInfo ti;
-    if (!tile_of_block<kGemmThreads>(g.offsets, g.E, kBM, g.ntiles_n, s_pref, s_wtot, &s_e, ti)) return;
+    if (!tile_of_block<kGemmThreads>(g.offsets, g.E, kBMX, g.ntiles_n, s_pref, s_wtot, &s_e, ti)) return;
     e = ti.e;
     m0 = ti.row0;
     mvalid = ti.row_end - ti.row0;
@@ -232,8 +314,19 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       b_off[i] = (kr * g.ldb + col) * 2;
     }
   }
+  // extra-band rows 256 + 16 w .. + 15 for waves 0, 1 (the other waves aim a spare kilobyte)
+  const bool x_real = wave < (kTileAX - kTileA) / 1024;
+  const int x_r = kBM + wave * 16 + (lane >> 2);
+  const int x_c = (lane & 3) ^ swz_a(x_r);
+  const int x_kc = x_c * 8;
+  const int x_off = (x_r * g.lda + x_c * 8) * 2;
   auto dma = [&](int kt, uint8_t* sa, uint8_t* sb) {
     const int k0 = kt * kBK;
+    if constexpr (ROWS) {
+      const int off = (x_real && k0 + x_kc < K) ? x_off + k0 * 2 : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(x_real ? sa + (kBM / 16 + wave) * 1024 : sSpare), 16,
+                                               off, 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i) {
       int off;
@@ -296,6 +389,30 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     }
   }
 
+  // Extra band (row-grouped products): A block = tile rows 256..287; B block = this wave's
+  // 32-column slice: columns wn*128 + wm*32 of its half, or for SwiGLU the 16 gate columns
+  // g0 .. g0+15 (lanes with column index < 16) and the matching 16 up columns, g0 = (wn*4+wm)*16.
+  const int g0 = (wn * 4 + wm) * 16;
+  int xa_rd[2], xb_rd[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    xa_rd[kk] = row_rd(kBM + (lane & 31), kk);
+    if constexpr (B_ROWS) {
+      xb_rd[kk][0] = row_rd(wn * 128 + wm * 32 + (lane & 31), kk);
+      xb_rd[kk][1] = 0;
+    } else if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+      for (int ri = 0; ri < 2; ++ri) {
+        const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
+        const int col = (q & 1) * 128 + g0 + 4 * (sl & 3);
+        xb_rd[kk][ri] = kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+      }
+    } else {
+      xb_rd[kk][0] = krow_rd(wn * 128 + wm * 32, kk, 0);
+      xb_rd[kk][1] = krow_rd(wn * 128 + wm * 32, kk, 1);
+    }
+  }
+
   f32x16 acc[2][4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -305,7 +422,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
 
   struct Frags {
-    bf16x8 a[2], b[4];
+    bf16x8 a[2], b[4], xa, xb;
   };
   auto frag = [&](const uint8_t* base, const int* rd, bool rows) -> bf16x8 {
     if (rows) return *reinterpret_cast<const bf16x8*>(base + rd[0]);
@@ -315,73 +432,89 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   };
   // NMB = number of this wave's 32-row blocks that hold rows (0..2, wave-uniform). Waves of one
   // tile may run different NMB variants: every variant issues the same DMAs and barriers.
-  auto read_frags = [&](auto nmb_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
+  auto read_frags = [&](auto nmb_c, auto x_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
     constexpr int NMB = decltype(nmb_c)::value;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag(sb, b_rd[kk][nb], B_ROWS);
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) f.a[mb] = frag(sa, a_rd[kk][mb], A_ROWS);
+    if constexpr (decltype(x_c)::value) {
+      f.xa = frag(sa, &xa_rd[kk], true);
+      f.xb = frag(sb, xb_rd[kk], B_ROWS);
+    }
   };
-  auto mfmas = [&](auto nmb_c, const Frags& f) {
+  auto mfmas = [&](auto nmb_c, auto x_c, const Frags& f, f32x16& acc_x) {
     constexpr int NMB = decltype(nmb_c)::value;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
+    if constexpr (decltype(x_c)::value) acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb, f.xa, acc_x, 0, 0, 0);
   };
   // One step: prefetch step kt+3 into the slot freed by step kt-1, compute step kt, then wait for
   // this wave's DMA of step kt+1 (the two later steps stay in flight) and meet at the barrier.
   // The scheduler is told to interleave: the first sub-step's fragment reads, then MFMAs with the
   // DMA issues and the second sub-step's fragment reads threaded between them.
-  auto step = [&](auto nmb_c, int kt, const uint8_t* sa, const uint8_t* sb, uint8_t* pa, uint8_t* pb) {
+  auto step = [&](auto nmb_c, auto x_c, f32x16& acc_x, int kt, const uint8_t* sa, const uint8_t* sb, uint8_t* pa,
+                  uint8_t* pb) {
     constexpr int NMB = decltype(nmb_c)::value;
+    constexpr int X = decltype(x_c)::value ? 1 : 0;
     if constexpr (NMB == 0) {
       dma(kt + 3, pa, pb);
     } else {
       Frags f0, f1;
-      read_frags(nmb_c, sa, sb, 0, f0);
-      read_frags(nmb_c, sa, sb, 1, f1);
+      read_frags(nmb_c, x_c, sa, sb, 0, f0);
+      read_frags(nmb_c, x_c, sa, sb, 1, f1);
       dma(kt + 3, pa, pb);
-      mfmas(nmb_c, f0);
-      mfmas(nmb_c, f1);
-      constexpr int R = (B_ROWS ? 4 : 8) + (A_ROWS ? 1 : 2) * NMB;  // LDS reads per sub-step
-      constexpr int M = 4 * NMB;                                  // MFMAs per sub-step
+      mfmas(nmb_c, x_c, f0, acc_x);
+      mfmas(nmb_c, x_c, f1, acc_x);
+      constexpr int R = (B_ROWS ? 4 : 8) + (A_ROWS ? 1 : 2) * NMB + X * (1 + (B_ROWS ? 1 : 2));  // LDS reads per sub-step
+      constexpr int M = 4 * NMB + X;                                                          // MFMAs per sub-step
       __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-      for (int i = 0; i < kDmaPerWave; ++i) {
+      for (int i = 0; i < DPW; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, R > 2 * kDmaPerWave ? R - 2 * kDmaPerWave : 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * M - kDmaPerWave, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, R > 2 * DPW ? R - 2 * DPW : 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * M - DPW, 0);
     }
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * DPW) : "memory");
   };
-  auto main_loop = [&](auto nmb_c) {
+  auto main_loop = [&](auto nmb_c, auto x_c) {
     // Steps past the last real one load zeros (out-of-range offsets) and add nothing, so the step
     // count is padded to a multiple of the ring depth and the loop body has no memory branches.
     const int KT = (K + kBK - 1) / kBK;
     const int KT4 = (KT + kStages - 1) / kStages * kStages;
+    f32x16 acc_x;
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) acc_x[qq] = 0.0f;
     dma(0, sA0, sB0);
     dma(1, sA1, sB1);
     dma(2, sA2, sB2);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * DPW) : "memory");
     for (int kt = 0; kt < KT4; kt += kStages) {
-      step(nmb_c, kt + 0, sA0, sB0, sA3, sB3);
-      step(nmb_c, kt + 1, sA1, sB1, sA0, sB0);
-      step(nmb_c, kt + 2, sA2, sB2, sA1, sB1);
-      step(nmb_c, kt + 3, sA3, sB3, sA2, sB2);
+      step(nmb_c, x_c, acc_x, kt + 0, sA0, sB0, sA3, sB3);
+      step(nmb_c, x_c, acc_x, kt + 1, sA1, sB1, sA0, sB0);
+      step(nmb_c, x_c, acc_x, kt + 2, sA2, sB2, sA1, sB1);
+      step(nmb_c, x_c, acc_x, kt + 3, sA3, sB3, sA2, sB2);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (decltype(x_c)::value) store_extra<EPI>(g, acc_x, m0, mvalid, n0, nt, g0, wm, wn, lane);
   };
   const int wrows = mvalid - wm * 64;
   const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(2, (wrows + 31) / 32));
-  switch (nmb) {
-    case 2: main_loop(std::integral_constant<int, 2>{}); break;
-    case 1: main_loop(std::integral_constant<int, 1>{}); break;
-    default: main_loop(std::integral_constant<int, 0>{}); break;
+  using F = std::false_type;
+  if (ROWS && mvalid > kBM) {  // the extra band holds rows: every regular band is full
+    if constexpr (ROWS) main_loop(std::integral_constant<int, 2>{}, std::true_type{});
+  } else {
+    switch (nmb) {
+      case 2: main_loop(std::integral_constant<int, 2>{}, F{}); break;
+      case 1: main_loop(std::integral_constant<int, 1>{}, F{}); break;
+      default: main_loop(std::integral_constant<int, 0>{}, F{}); break;
+    }
   }
 
   // ---- epilogue: lane holds output row (lane & 31) of each 32-row block and, per 32-column
@@ -426,25 +559,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mb][nb][gq * 4 + qq];
           if constexpr (EPI == kEpiSwigluBwd) {
-            // v = dL/dh; with s = sigmoid(g): dL/dg = v * u * s * (1 + g (1 - s)), dL/du = v * g * s
-            const uint16_t* gr = g.gu + m * 2 * g.N;
-            const uint2 gp = *reinterpret_cast<const uint2*>(gr + col);
-            const uint2 up = *reinterpret_cast<const uint2*>(gr + g.N + col);
-            const float gv[4] = {bf16_to_f32(gp.x & 0xffffu), bf16_to_f32(gp.x >> 16), bf16_to_f32(gp.y & 0xffffu),
-                                 bf16_to_f32(gp.y >> 16)};
-            const float uv[4] = {bf16_to_f32(up.x & 0xffffu), bf16_to_f32(up.x >> 16), bf16_to_f32(up.y & 0xffffu),
-                                 bf16_to_f32(up.y >> 16)};
-            float dg[4], du[4];
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const float sg = 1.0f / (1.0f + __expf(-gv[qq]));
-              dg[qq] = v[qq] * uv[qq] * sg * (1.0f + gv[qq] * (1.0f - sg));
-              du[qq] = v[qq] * gv[qq] * sg;
-            }
-            uint16_t* dr = cbase + m * g.ldc;
-            *reinterpret_cast<uint2*>(dr + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>(dr + g.N + col) =
-                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            store_swiglu_bwd(g, cbase, m, col, v);
           } else {
             *reinterpret_cast<uint2*>(cbase + m * g.ldc + col) =
                 make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -517,7 +632,7 @@ static void launch_generic(GemmArgs g, int64_t grid, hipStream_t s) {
 }
 
 // worst-case row tiles over any distribution of N rows among E experts
-static inline int64_t row_tiles_bound(int N, int E) { return ((int64_t)N + (int64_t)E * (kBM - 1)) / kBM; }
+static inline int64_t row_tiles_bound(int N, int E) { return ((int64_t)N + (int64_t)E * (kBMX - 1)) / kBMX; }
 
 hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, int N, int H, int I, int E,
                                const int32_t* offsets, void* h, void* gu_saved, hipStream_t s) {
