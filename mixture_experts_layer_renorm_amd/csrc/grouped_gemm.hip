@@ -23,6 +23,7 @@
 // ([32 k][256 cols], 512-byte rows) and read with the LDS transpose read ds_read_b64_tr_b16, so no
 // operand is ever repacked. The MFMA takes the B fragment first, so a lane ends up holding four
 // consecutive output columns of one row, which become one 8-byte store.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -570,6 +571,220 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Weight gradients, persistent. dW_e = P_e^T Q_e with K = the rows of expert e (about 128 for
+// the fine-grained shape), so a 256 x 256 output tile is only a few K steps followed by 128 KB of
+// stores: one workgroup per tile would spend most of its life starting up and draining. Here a
+// fixed grid of workgroups (one per CU) walks the tile list; during the last three K steps of a
+// tile the DMAs for the first three steps of the workgroup's next tile are issued, so that the
+// loads of tile i+1 overlap the epilogue stores of tile i. The epilogue uses buffer stores with
+// out-of-range offsets for masked elements, so every wave issues exactly kWgStores stores per
+// tile and the vmcnt accounting stays exact. Tiles of one XCD are contiguous in the list (an
+// expert's tiles share its P and Q rows in that XCD's L2).
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+constexpr int kWgStores = 2 * 4 * 4;  // per wave: 2 row blocks x 4 column blocks x 4 quads
+
+struct WgTile {
+  __amdgpu_buffer_rsrc_t rsA, rsB, rsC;
+  int K, KT4;
+  int a_off[kDmaA], b_off[kDmaB];
+  bool a_ok[kDmaA], b_ok[kDmaB];
+};
+
+__global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmArgs g, int total) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA], sA1[kTileA], sA2[kTileA], sA3[kTileA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = (wave >> 1) & 3, wn = wave & 1;
+  const int b = blockIdx.x;
+  const int Q = (total + 7) >> 3;
+  const int t_end = min(((b & 7) + 1) * Q, total);
+  const int stride = gridDim.x >> 3;
+  int t = (b & 7) * Q + (b >> 3);
+  if (t >= t_end) return;
+
+  // tile t -> expert, output origin, K rows, descriptors and DMA lane offsets (k-row tiles of P
+  // [rows, M] and Q [rows, N]: instruction i fills k-rows (wave*2 + i)*2 .. +2, 32 lanes per row)
+  auto setup = [&](int tt, WgTile& w) {
+    const bool real = tt < t_end;
+    const int per_e = g.ntiles_m * g.ntiles_n;
+    const int e = real ? tt / per_e : 0;
+    const int rem = tt - e * per_e;
+    const int mt = rem / g.ntiles_n;
+    const int m0 = mt * kBM, n0 = (rem - mt * g.ntiles_n) * kBN;
+    const int r0 = __builtin_amdgcn_readfirstlane(g.offsets[e]);
+    const int K = real ? __builtin_amdgcn_readfirstlane(max(0, (int)g.offsets[e + 1] - r0)) : 0;
+    w.K = K;
+    w.KT4 = max(kStages, (K + kBK * kStages - 1) / (kBK * kStages) * kStages);
+    w.rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(g.A + (int64_t)r0 * g.lda), (short)0, K * g.lda * 2, kBufferWord3);
+    w.rsB = __builtin_amdgcn_make_buffer_rsrc((void*)(g.B + (int64_t)r0 * g.ldb), (short)0, K * g.ldb * 2, kBufferWord3);
+    w.rsC = __builtin_amdgcn_make_buffer_rsrc((void*)(g.C + (int64_t)e * g.c_expert), (short)0,
+                                              real ? g.M * g.N * 2 : 0, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i) {
+      const int kr = (wave * kDmaA + i) * 2 + (lane >> 5);
+      const int col = m0 + (((lane & 31) ^ swz_b(kr)) * 8);
+      w.a_ok[i] = col < g.M;
+      w.a_off[i] = (kr * g.lda + (w.a_ok[i] ? col : 0)) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) {
+      const int kr = (wave * kDmaB + i) * 2 + (lane >> 5);
+      const int col = n0 + (((lane & 31) ^ swz_b(kr)) * 8);
+      w.b_ok[i] = col < g.N;
+      w.b_off[i] = (kr * g.ldb + (w.b_ok[i] ? col : 0)) * 2;
+    }
+  };
+  int cm0, cn0;  // output origin of the current tile
+  auto origin = [&](int tt) {
+    const int per_e = g.ntiles_m * g.ntiles_n;
+    const int rem = tt - (tt / per_e) * per_e;
+    const int mt = rem / g.ntiles_n;
+    cm0 = mt * kBM;
+    cn0 = (rem - mt * g.ntiles_n) * kBN;
+  };
+  auto dma = [&](const WgTile& w, int kt, uint8_t* sa, uint8_t* sb) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w.rsA, (lds_void*)(sa + (wave * kDmaA + i) * 1024), 16,
+                                               w.a_ok[i] ? w.a_off[i] + k0 * g.lda * 2 : kOutOfRange, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w.rsB, (lds_void*)(sb + (wave * kDmaB + i) * 1024), 16,
+                                               w.b_ok[i] ? w.b_off[i] + k0 * g.ldb * 2 : kOutOfRange, 0, 0, 0);
+  };
+
+  // fragment addresses (both operands k-row tiles, read with the transpose read)
+  const int q = lane >> 4, sl = lane & 15;
+  auto krow_rd = [&](int col32, int kk, int ri) {
+    const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
+    const int col = col32 + (q & 1) * 16 + 4 * (sl & 3);
+    return kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+  };
+  int a_rd[2][2][2], b_rd[2][4][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int ri = 0; ri < 2; ++ri) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) a_rd[kk][mb][ri] = krow_rd(wm * 64 + mb * 32, kk, ri);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) b_rd[kk][nb][ri] = krow_rd(wn * 128 + nb * 32, kk, ri);
+    }
+  auto frag = [&](const uint8_t* base, const int* rd) -> bf16x8 {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 acc[2][4];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
+  };
+
+  // One step: fragments of step kt, one prefetch (this tile's step kt+3, or the next tile's step
+  // kt+3-KT4 in the last three steps), MFMAs, then wait for step kt+1's DMA and meet at the
+  // barrier. `wide`: the previous tile's kWgStores epilogue stores sit between this step's needed
+  // DMA and the newest instructions (the first two steps of a tile after the first).
+  auto step = [&](int kt, bool wide, const WgTile& cur, const WgTile& nxt, const uint8_t* sa, const uint8_t* sb,
+                  uint8_t* pa, uint8_t* pb) {
+    // the tile's step count is padded to the ring depth; padded steps (past K) only keep the DMA
+    // and barrier cadence and skip the fragment reads and MFMAs
+    if (kt * kBK < cur.K) {
+      bf16x8 fa[2][2], fb[2][4];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) fb[kk][nb] = frag(sb, b_rd[kk][nb]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) fa[kk][mb] = frag(sa, a_rd[kk][mb]);
+      }
+      if (kt + 3 < cur.KT4)
+        dma(cur, kt + 3, pa, pb);
+      else
+        dma(nxt, kt + 3 - cur.KT4, pa, pb);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][nb], fa[kk][mb], acc[mb][nb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
+#pragma unroll
+      for (int i = 0; i < kDmaPerWave; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16 - kDmaPerWave, 0);
+    } else {
+      if (kt + 3 < cur.KT4)
+        dma(cur, kt + 3, pa, pb);
+      else
+        dma(nxt, kt + 3 - cur.KT4, pa, pb);
+    }
+    if (wide)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave + kWgStores) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+  };
+  // epilogue: lane holds output row (lane & 31) of each 32-row block and four consecutive columns
+  auto store = [&](const WgTile& w) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = cm0 + wm * 64 + mb * 32 + (lane & 31);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = cn0 + wn * 128 + nb * 32 + gq * 8 + (lane >> 5) * 4;
+          const int off = (m < g.M && col < g.N) ? (m * g.ldc + col) * 2 : kOutOfRange;
+          const u32x2 v = {pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                           pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b64(v, w.rsC, off, 0, 0);
+        }
+    }
+  };
+
+  WgTile cur, nxt;
+  setup(t, cur);
+  origin(t);
+  zero_acc();
+  dma(cur, 0, sA0, sB0);
+  dma(cur, 1, sA1, sB1);
+  dma(cur, 2, sA2, sB2);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+  bool first = true;
+  for (;;) {
+    setup(t + stride, nxt);  // a tile past the end gives zero-length descriptors (loads return zero)
+    for (int kb = 0; kb < cur.KT4; kb += kStages) {
+      const bool w0 = !first && kb == 0;
+      step(kb + 0, w0, cur, nxt, sA0, sB0, sA3, sB3);
+      step(kb + 1, w0, cur, nxt, sA1, sB1, sA0, sB0);
+      step(kb + 2, false, cur, nxt, sA2, sB2, sA1, sB1);
+      step(kb + 3, false, cur, nxt, sA3, sB3, sA2, sB2);
+    }
+    store(cur);
+    t += stride;
+    if (t >= t_end) break;
+    cur = nxt;
+    origin(t);
+    zero_acc();
+    first = false;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------------------
 // fp32 path: one thread per output element, fp32 fused multiply-add over k ascending.
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E, int r) {
@@ -751,7 +966,17 @@ hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E,
   g.c_expert = (int64_t)M * Nq;
   g.ntiles_m = (M + kBM - 1) / kBM;
   g.ntiles_n = (Nq + kBN - 1) / kBN;
-  launch_generic<false, false, kEpiStore, kSchedWgrad>(g, (int64_t)E * g.ntiles_m * g.ntiles_n, s);
+  const int64_t total = (int64_t)E * g.ntiles_m * g.ntiles_n;
+  // one workgroup per CU (each holds 128 KB of LDS and a full register file)
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const int64_t grid = std::min<int64_t>(round_up8(total), (int64_t)round_up8(cus));
+  hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g, (int)total);
   return hipGetLastError();
 }
 
