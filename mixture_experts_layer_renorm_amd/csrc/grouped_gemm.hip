@@ -575,26 +575,61 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
 // ---------------------------------------------------------------------------------------------
 // Weight gradients, persistent. dW_e = P_e^T Q_e with K = the rows of expert e (about 128 for
 // the fine-grained shape), so a 256 x 256 output tile is only a few K steps followed by 128 KB of
-// stores: one workgroup per tile would spend most of its life starting up and draining. Here a
-// fixed grid of workgroups (one per CU) walks the tile list; during the last three K steps of a
-// tile the DMAs for the first three steps of the workgroup's next tile are issued, so that the
-// loads of tile i+1 overlap the epilogue stores of tile i. The epilogue uses buffer stores with
-// out-of-range offsets for masked elements, so every wave issues exactly kWgStores stores per
-// tile and the vmcnt accounting stays exact. Tiles of one XCD are contiguous in the list (an
-// expert's tiles share its P and Q rows in that XCD's L2).
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-constexpr int kWgStores = 2 * 4 * 4;  // per wave: 2 row blocks x 4 column blocks x 4 quads
+// stores, and the kernel is bound by writing the gradients. A fixed grid of workgroups (one per
+// CU) walks the tile list; tiles of one XCD are contiguous in the list (an expert's tiles share
+// its P and Q rows in that XCD's L2).
+//
+// The waves split the memory work: waves 0-3 issue every global -> LDS DMA, waves 4-7 every
+// global store; all eight compute a 64 x 128 block of the tile. Loads and stores share one
+// in-order counter per wave, so if one wave did both, waiting for a K step's loads would also
+// wait for the previous tile's stores; split this way the stores of tile i drain while tile i+1
+// loads and computes. During the last three K steps of a tile the DMAs for the first three steps
+// of the next tile are issued. The epilogue is staged through ring slot 3 (sA3 = rows 0-31,
+// sB3 = rows 32-63 of a 64-row quarter): slot 3 held the last K step, which every wave has read
+// by that step's barrier, while slots 0-2 already receive the next tile's first steps. Per
+// quarter, the two waves of that 64-row band write their accumulators as bf16 (16-byte chunk c
+// of row r at chunk position c ^ (r & 31), so the 32 rows of one write fall on different banks);
+// after a barrier the store waves copy the quarter out as whole 512-byte rows, two rows (1 KB)
+// per buffer store, and a second barrier frees the staging area.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+constexpr int kWgLoaders = 4;                              // waves 0-3 load, waves 4-7 store
+constexpr int kWgDmaA = kTileA / 1024 / kWgLoaders;        // DMA instructions per loader per step
+constexpr int kWgDmaB = kTileB / 1024 / kWgLoaders;
+constexpr int kWgDma = kWgDmaA + kWgDmaB;
+constexpr int kWgRowsPerStore = 64 / (kWaves - kWgLoaders) / 2;  // 1 KB stores per store wave per quarter
+
+constexpr int kMaxExperts = 1024;  // the library's limit on E (checked on the host)
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// raw buffer descriptor over [p, p + bytes): 32-bit offsets, loads past the end return zero
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)p;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kBufferWord3;
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane (one wave-wide 1 KB DMA)
+__device__ __forceinline__ void dma_16(const i32x4& rsrc, int voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
 
 struct WgTile {
-  __amdgpu_buffer_rsrc_t rsA, rsB, rsC;
-  int K, KT4;
-  int a_off[kDmaA], b_off[kDmaB];
-  bool a_ok[kDmaA], b_ok[kDmaB];
+  const uint16_t* a;  // P rows of the expert, from its first row
+  const uint16_t* b;  // Q rows of the expert
+  int e, m0, n0, K, KT4;
 };
 
 __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmArgs g, int total) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA], sA1[kTileA], sA2[kTileA], sA3[kTileA];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
+  __shared__ int s_off[kMaxExperts + 1];  // expert offsets, read once (LDS reads do not touch vmcnt)
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -604,59 +639,27 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmA
   const int Q = (total + 7) >> 3;
   const int t_end = min(((b & 7) + 1) * Q, total);
   const int stride = gridDim.x >> 3;
-  int t = (b & 7) * Q + (b >> 3);
-  if (t >= t_end) return;
+  const int t0 = (b & 7) * Q + (b >> 3);
+  if (t0 >= t_end) return;
+  for (int i = tid; i <= g.E; i += kGemmThreads) s_off[i] = g.offsets[i];
+  __syncthreads();
 
-  // tile t -> expert, output origin, K rows, descriptors and DMA lane offsets (k-row tiles of P
-  // [rows, M] and Q [rows, N]: instruction i fills k-rows (wave*2 + i)*2 .. +2, 32 lanes per row)
+  // tile tt -> expert, output origin, K rows and operand rows. A tile past the end has K = 0.
   auto setup = [&](int tt, WgTile& w) {
     const bool real = tt < t_end;
     const int per_e = g.ntiles_m * g.ntiles_n;
     const int e = real ? tt / per_e : 0;
     const int rem = tt - e * per_e;
     const int mt = rem / g.ntiles_n;
-    const int m0 = mt * kBM, n0 = (rem - mt * g.ntiles_n) * kBN;
-    const int r0 = __builtin_amdgcn_readfirstlane(g.offsets[e]);
-    const int K = real ? __builtin_amdgcn_readfirstlane(max(0, (int)g.offsets[e + 1] - r0)) : 0;
+    w.e = e;
+    w.m0 = mt * kBM;
+    w.n0 = (rem - mt * g.ntiles_n) * kBN;
+    const int r0 = __builtin_amdgcn_readfirstlane(s_off[e]);
+    const int K = real ? __builtin_amdgcn_readfirstlane(max(0, s_off[e + 1] - r0)) : 0;
     w.K = K;
     w.KT4 = max(kStages, (K + kBK * kStages - 1) / (kBK * kStages) * kStages);
-    w.rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(g.A + (int64_t)r0 * g.lda), (short)0, K * g.lda * 2, kBufferWord3);
-    w.rsB = __builtin_amdgcn_make_buffer_rsrc((void*)(g.B + (int64_t)r0 * g.ldb), (short)0, K * g.ldb * 2, kBufferWord3);
-    w.rsC = __builtin_amdgcn_make_buffer_rsrc((void*)(g.C + (int64_t)e * g.c_expert), (short)0,
-                                              real ? g.M * g.N * 2 : 0, kBufferWord3);
-#pragma unroll
-    for (int i = 0; i < kDmaA; ++i) {
-      const int kr = (wave * kDmaA + i) * 2 + (lane >> 5);
-      const int col = m0 + (((lane & 31) ^ swz_b(kr)) * 8);
-      w.a_ok[i] = col < g.M;
-      w.a_off[i] = (kr * g.lda + (w.a_ok[i] ? col : 0)) * 2;
-    }
-#pragma unroll
-    for (int i = 0; i < kDmaB; ++i) {
-      const int kr = (wave * kDmaB + i) * 2 + (lane >> 5);
-      const int col = n0 + (((lane & 31) ^ swz_b(kr)) * 8);
-      w.b_ok[i] = col < g.N;
-      w.b_off[i] = (kr * g.ldb + (w.b_ok[i] ? col : 0)) * 2;
-    }
-  };
-  int cm0, cn0;  // output origin of the current tile
-  auto origin = [&](int tt) {
-    const int per_e = g.ntiles_m * g.ntiles_n;
-    const int rem = tt - (tt / per_e) * per_e;
-    const int mt = rem / g.ntiles_n;
-    cm0 = mt * kBM;
-    cn0 = (rem - mt * g.ntiles_n) * kBN;
-  };
-  auto dma = [&](const WgTile& w, int kt, uint8_t* sa, uint8_t* sb) {
-    const int k0 = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < kDmaA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w.rsA, (lds_void*)(sa + (wave * kDmaA + i) * 1024), 16,
-                                               w.a_ok[i] ? w.a_off[i] + k0 * g.lda * 2 : kOutOfRange, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kDmaB; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w.rsB, (lds_void*)(sb + (wave * kDmaB + i) * 1024), 16,
-                                               w.b_ok[i] ? w.b_off[i] + k0 * g.ldb * 2 : kOutOfRange, 0, 0, 0);
+    w.a = g.A + (int64_t)r0 * g.lda;
+    w.b = g.B + (int64_t)r0 * g.ldb;
   };
 
   // fragment addresses (both operands k-row tiles, read with the transpose read)
@@ -692,97 +695,176 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmA
         for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
   };
 
-  // One step: fragments of step kt, one prefetch (this tile's step kt+3, or the next tile's step
-  // kt+3-KT4 in the last three steps), MFMAs, then wait for step kt+1's DMA and meet at the
-  // barrier. `wide`: the previous tile's kWgStores epilogue stores sit between this step's needed
-  // DMA and the newest instructions (the first two steps of a tile after the first).
-  auto step = [&](int kt, bool wide, const WgTile& cur, const WgTile& nxt, const uint8_t* sa, const uint8_t* sb,
-                  uint8_t* pa, uint8_t* pb) {
-    // the tile's step count is padded to the ring depth; padded steps (past K) only keep the DMA
-    // and barrier cadence and skip the fragment reads and MFMAs
-    if (kt * kBK < cur.K) {
-      bf16x8 fa[2][2], fb[2][4];
+  // The whole walk, once per role, so that each role's loop is scheduled on its own. Both roles
+  // meet the same barriers in the same order: one per K step, two per epilogue quarter.
+  auto walk = [&](auto loader_tag) {
+    constexpr bool LOADER = decltype(loader_tag)::value;
+    const int lw = wave & (kWgLoaders - 1);
+    // loader lane offsets within a k-row tile: instruction i fills k-rows (lw*n + i)*2 .. +2, 32
+    // lanes per 512-byte row; rows of P are g.lda elements apart, rows of Q g.ldb
+    int a_lane[kWgDmaA], b_lane[kWgDmaB];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) fb[kk][nb] = frag(sb, b_rd[kk][nb]);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) fa[kk][mb] = frag(sa, a_rd[kk][mb]);
-      }
-      if (kt + 3 < cur.KT4)
-        dma(cur, kt + 3, pa, pb);
-      else
-        dma(nxt, kt + 3 - cur.KT4, pa, pb);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][nb], fa[kk][mb], acc[mb][nb], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
-#pragma unroll
-      for (int i = 0; i < kDmaPerWave; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16 - kDmaPerWave, 0);
-    } else {
-      if (kt + 3 < cur.KT4)
-        dma(cur, kt + 3, pa, pb);
-      else
-        dma(nxt, kt + 3 - cur.KT4, pa, pb);
+    for (int i = 0; i < kWgDmaA; ++i) {
+      const int kr = (lw * kWgDmaA + i) * 2 + (lane >> 5);
+      a_lane[i] = kr * g.lda * 2 + (((lane & 31) ^ swz_b(kr)) * 16);
     }
-    if (wide)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave + kWgStores) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
-  };
-  // epilogue: lane holds output row (lane & 31) of each 32-row block and four consecutive columns
-  auto store = [&](const WgTile& w) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int m = cm0 + wm * 64 + mb * 32 + (lane & 31);
+    for (int i = 0; i < kWgDmaB; ++i) {
+      const int kr = (lw * kWgDmaB + i) * 2 + (lane >> 5);
+      b_lane[i] = kr * g.ldb * 2 + (((lane & 31) ^ swz_b(kr)) * 16);
+    }
+    // Step kt of tile w: the descriptors start at the step's first k-row and end at the expert's
+    // last row, so k-rows past K (the step count is padded to the ring depth) read as zero; they
+    // are rebuilt per step in scalar registers, which keeps the per-step offsets out of vector
+    // registers. Columns past M or N are not masked: they read other elements of the same
+    // operands and only reach outputs that are never stored.
+    //
+    // The DMAs are written as inline assembly: the compiler then does not track them, and only
+    // the explicit waits below order them against the fragment reads. (Tracked, its own
+    // conservative waits before the fragment reads cut the prefetch depth from three steps to
+    // two.)
+    auto dma = [&](const WgTile& w, int kt, uint8_t* sa, uint8_t* sb) {
+      if constexpr (LOADER) {
+        const int k0 = kt * kBK, rows = max(0, w.K - k0);
+        const i32x4 rsA = buffer_rsrc(w.a + (int64_t)k0 * g.lda, rows * g.lda * 2);
+        const i32x4 rsB = buffer_rsrc(w.b + (int64_t)k0 * g.ldb, rows * g.ldb * 2);
+        const uint32_t da = lds_addr(sa) + lw * kWgDmaA * 1024, db = lds_addr(sb) + lw * kWgDmaB * 1024;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+        for (int i = 0; i < kWgDmaA; ++i) dma_16(rsA, a_lane[i] + w.m0 * 2, da + i * 1024);
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int col = cn0 + wn * 128 + nb * 32 + gq * 8 + (lane >> 5) * 4;
-          const int off = (m < g.M && col < g.N) ? (m * g.ldc + col) * 2 : kOutOfRange;
-          const u32x2 v = {pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
-                           pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3])};
-          __builtin_amdgcn_raw_buffer_store_b64(v, w.rsC, off, 0, 0);
+        for (int i = 0; i < kWgDmaB; ++i) dma_16(rsB, b_lane[i] + w.n0 * 2, db + i * 1024);
+      }
+    };
+    // end of a step: loaders wait until only the two newer steps' DMAs are outstanding
+    auto meet = [&]() {
+      if constexpr (LOADER)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kWgDma) : "memory");
+      else
+        asm volatile("s_barrier" ::: "memory");
+    };
+    // One step: fragments of step kt, one prefetch (this tile's step kt+3, or the next tile's
+    // step kt+3-KT4 in the last three steps), MFMAs, then meet. Padded steps (past K) keep only
+    // the prefetch and the barrier.
+    auto step = [&](int kt, const WgTile& cur, const WgTile& nxt, const uint8_t* sa, const uint8_t* sb, uint8_t* pa,
+                    uint8_t* pb) {
+      if (kt * kBK < cur.K) {
+        bf16x8 fa[2][2], fb[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) fb[kk][nb] = frag(sb, b_rd[kk][nb]);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) fa[kk][mb] = frag(sa, a_rd[kk][mb]);
         }
-    }
-  };
+        if (kt + 3 < cur.KT4)
+          dma(cur, kt + 3, pa, pb);
+        else
+          dma(nxt, kt + 3 - cur.KT4, pa, pb);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][nb], fa[kk][mb], acc[mb][nb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);
+        if constexpr (LOADER) {
+#pragma unroll
+          for (int i = 0; i < kWgDma; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 16 - kWgDma, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        }
+      } else {
+        if (kt + 3 < cur.KT4)
+          dma(cur, kt + 3, pa, pb);
+        else
+          dma(nxt, kt + 3 - cur.KT4, pa, pb);
+      }
+      meet();
+    };
+    // Epilogue (see above). The lane offsets are built from a value the compiler cannot see
+    // through, so that they are computed here instead of being hoisted out of the tile loop.
+    auto store = [&](const WgTile& w) {
+      int z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      const int lr = (lane & 31) + z;
+      const int wr_lo = lr * 512 + (lane >> 5) * 8;  // row lr, half-chunk lane / 32
+      const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(g.C + (int64_t)w.e * g.c_expert), (short)0, g.M * g.N * 2, kBufferWord3);
+      if constexpr (!LOADER) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the previous tile's stores
+      // round to bf16 first: the quarter loop then keeps 64 packed registers live, not 128
+      uint2 pk[2][4][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            pk[mb][nb][gq] = make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                                        pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
+#pragma unroll 1
+      for (int qb = 0; qb < 4; ++qb) {
+        if (wm == qb) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            uint8_t* rowp = (mb == 0 ? sA3 : sB3) + wr_lo;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int chunk = (wn * 16 + nb * 4 + gq) ^ lr;
+                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = pk[mb][nb][gq];
+              }
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if constexpr (!LOADER) {
+#pragma unroll
+          for (int j = 0; j < kWgRowsPerStore; ++j) {
+            const int r = ((wave - kWgLoaders) * kWgRowsPerStore + j) * 2 + (lane >> 5) + z;
+            const int c = lane & 31;
+            const u32x4 v = *reinterpret_cast<const u32x4*>((r < 32 ? sA3 : sB3) + (r & 31) * 512 + ((c ^ (r & 31)) << 4));
+            const int m = w.m0 + qb * 64 + r, col = w.n0 + c * 8;
+            const int off = (m < g.M && col < g.N) ? (m * g.ldc + col) * 2 : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 0);
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    };
 
-  WgTile cur, nxt;
-  setup(t, cur);
-  origin(t);
-  zero_acc();
-  dma(cur, 0, sA0, sB0);
-  dma(cur, 1, sA1, sB1);
-  dma(cur, 2, sA2, sB2);
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
-  bool first = true;
-  for (;;) {
-    setup(t + stride, nxt);  // a tile past the end gives zero-length descriptors (loads return zero)
-    for (int kb = 0; kb < cur.KT4; kb += kStages) {
-      const bool w0 = !first && kb == 0;
-      step(kb + 0, w0, cur, nxt, sA0, sB0, sA3, sB3);
-      step(kb + 1, w0, cur, nxt, sA1, sB1, sA0, sB0);
-      step(kb + 2, false, cur, nxt, sA2, sB2, sA1, sB1);
-      step(kb + 3, false, cur, nxt, sA3, sB3, sA2, sB2);
-    }
-    store(cur);
-    t += stride;
-    if (t >= t_end) break;
-    cur = nxt;
-    origin(t);
+    int t = t0;
+    WgTile cur, nxt;
+    setup(t, cur);
     zero_acc();
-    first = false;
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    dma(cur, 0, sA0, sB0);
+    dma(cur, 1, sA1, sB1);
+    dma(cur, 2, sA2, sB2);
+    meet();
+    for (;;) {
+      setup(t + stride, nxt);
+      for (int kb = 0; kb < cur.KT4; kb += kStages) {
+        step(kb + 0, cur, nxt, sA0, sB0, sA3, sB3);
+        step(kb + 1, cur, nxt, sA1, sB1, sA0, sB0);
+        step(kb + 2, cur, nxt, sA2, sB2, sA1, sB1);
+        step(kb + 3, cur, nxt, sA3, sB3, sA2, sB2);
+      }
+      store(cur);
+      t += stride;
+      if (t >= t_end) break;
+      cur = nxt;
+      zero_acc();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  if (wave < kWgLoaders)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------------------------
