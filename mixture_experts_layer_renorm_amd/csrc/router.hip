@@ -13,26 +13,16 @@ namespace moe {
 // ---------------------------------------------------------------------------------------------
 // logits[t, e] = fp32 chain over h = 0..H-1 of fma(x[t,h], w_gate[h,e], acc).
 //
-// A workgroup (4 waves) owns 16 tokens x 64*EQ experts; each lane owns 4 tokens x EQ adjacent
-// experts, i.e. 4*EQ independent chains. The hidden dimension is walked in chunks of HB: the
-// chunk's x tile [16 x HB] and W_g tile [HB x 64*EQ] are loaded cooperatively (16-byte loads when
-// the rows allow), widened to fp32 once, and staged in LDS (double buffered, the next chunk's
-// global loads in flight during this chunk's FMAs). Within a lane, every chain still consumes
-// h = 0, 1, ..., H-1 in order.
+// Lanes are tokens: a workgroup of 4 waves owns 64 tokens (one per lane) and 4 * EQ experts
+// (EQ per wave), so a lane runs EQ independent chains, all consuming h = 0, 1, ..., H-1 in order.
+// The hidden dimension is walked in chunks of HB. Each chunk's x tile [64 x HB] and W_g tile
+// [HB x 4*EQ] are loaded into registers DEPTH chunks ahead (the loads of x come from HBM, so
+// their latency has to be covered by more than one chunk of arithmetic), widened to fp32 once and
+// stored to a double-buffered LDS tile. A lane then reads four h of its own token with one 16-byte
+// read (row pitch padded by 4 floats, so 16 consecutive rows cover all banks) and the wave's EQ
+// weights of each h with 16-byte broadcast reads.
 constexpr int kLogitWaves = 4;
-constexpr int kTokPerWave = 4;
-constexpr int kTokPerBlock = kLogitWaves * kTokPerWave;
-
-template <typename TIn, int EQ>
-struct LogitTile {
-  static constexpr int EB = kWave * EQ;              // experts per workgroup
-  static constexpr int HB = EQ >= 4 ? 32 : 64;       // hidden chunk
-  static constexpr int VEC = 16 / sizeof(TIn);       // elements per 16-byte load
-  static constexpr int XCH = kTokPerBlock * HB / VEC;  // 16-byte chunks of the x tile
-  static constexpr int WCH = HB * EB / VEC;            // 16-byte chunks of the W tile
-  static constexpr int XPT = (XCH + 255) / 256;        // per thread
-  static constexpr int WPT = (WCH + 255) / 256;
-};
+constexpr int kLogitTok = kWave;  // tokens per workgroup
 
 template <typename TIn>
 __device__ __forceinline__ void widen(const uint4& v, float* f);
@@ -53,11 +43,11 @@ __device__ __forceinline__ void widen<float>(const uint4& v, float* f) {
   f[3] = __uint_as_float(v.w);
 }
 
-// 16 bytes (VEC elements) of row `row` from column `col`; columns >= ncols read as zero.
+// 16 bytes (VEC elements) of row `row` from column `col` without a vector load (rows not 16-byte
+// aligned); columns >= ncols read as zero.
 template <typename TIn>
-__device__ __forceinline__ uint4 load_chunk(const TIn* __restrict__ row, int col, int ncols, bool vec) {
+__device__ __forceinline__ uint4 load_chunk_scalar(const TIn* __restrict__ row, int col, int ncols) {
   constexpr int VEC = 16 / sizeof(TIn);
-  if (vec && col + VEC <= ncols) return *reinterpret_cast<const uint4*>(row + col);
   TIn tmp[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) tmp[i] = col + i < ncols ? row[col + i] : TIn(0);
@@ -66,129 +56,192 @@ __device__ __forceinline__ uint4 load_chunk(const TIn* __restrict__ row, int col
   return v;
 }
 
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data, offset addressing
+constexpr int kPastEnd = 0x7ffffff0;         // an offset past every descriptor's end: loads return zero
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <typename TIn, int EQ>
-__global__ __launch_bounds__(kLogitWaves * kWave) void router_logits_kernel(
+struct LogitTile {
+  static constexpr int EB = kLogitWaves * EQ;                     // experts per workgroup
+  static constexpr int HB = 32;                                   // hidden chunk
+  static constexpr int PITCH = HB + 4;                            // LDS row pitch of the x tile
+  static constexpr int DEPTH = 6;                                 // chunks in flight
+  static constexpr int G = 32 / EQ;                               // h per software-pipelined group
+  static constexpr int VEC = 16 / sizeof(TIn);                    // elements per 16-byte load
+  static constexpr int XCH = kLogitTok * HB / VEC;                // 16-byte chunks of the x tile
+  static constexpr int WCH = (HB * EB + VEC - 1) / VEC;           // and of the W tile
+  static constexpr int XPT = (XCH + kLogitWaves * kWave - 1) / (kLogitWaves * kWave);  // per thread
+  static constexpr int WPT = (WCH + kLogitWaves * kWave - 1) / (kLogitWaves * kWave);
+};
+
+template <typename TIn, int EQ>
+__global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_logits_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ wg, int T, int H, int E, float* __restrict__ logits, int vec_x,
     int vec_w) {
   using P = LogitTile<TIn, EQ>;
-  constexpr int EB = P::EB, HB = P::HB, VEC = P::VEC;
-  __shared__ __attribute__((aligned(16))) float xs[2][kTokPerBlock][HB];
+  constexpr int EB = P::EB, VEC = P::VEC, HB = P::HB, DEPTH = P::DEPTH;
+  static_assert(EQ % 4 == 0, "experts per wave come in 16-byte groups");
+  __shared__ __attribute__((aligned(16))) float xs[2][kLogitTok][P::PITCH];
   __shared__ __attribute__((aligned(16))) float ws[2][HB][EB];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int t0 = blockIdx.x * kTokPerBlock;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int t0 = blockIdx.x * kLogitTok;
   const int e0 = blockIdx.y * EB;
-  const int nh_chunks = (H + HB - 1) / HB;
+  const int nch = (H + HB - 1) / HB;
 
-  uint4 rx[P::XPT], rw[P::WPT];
-  auto load = [&](int hc) {
-    const int h0 = hc * HB;
+  // Global loads. With rows a multiple of 16 bytes (vec_x / vec_w) they are 16-byte buffer loads
+  // whose descriptors end at the last token of the workgroup and the last row of W_g; elements
+  // past H or E get an offset past the end and read as zero, so there is no branch per element.
+  const int rows = min(kLogitTok, T - t0);
+  const __amdgpu_buffer_rsrc_t rsx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)t0 * H), (short)0, rows * H * (int)sizeof(TIn), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wg, (short)0, H * E * (int)sizeof(TIn), kRawBufferWord3);
+  // register stage r holds chunk c with c % DEPTH == r
+  uint4 rx[DEPTH][P::XPT], rw[DEPTH][P::WPT];
+  auto load = [&](int c, uint4* px, uint4* pw) {
+    const int h0 = c * HB;
 #pragma unroll
     for (int i = 0; i < P::XPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < P::XCH) {
-        const int tt = c / (HB / VEC), hh = (c % (HB / VEC)) * VEC;
-        const int t = min(t0 + tt, T - 1);
-        rx[i] = load_chunk<TIn>(x + (int64_t)t * H, h0 + hh, H, vec_x);
+      const int q = tid + kLogitWaves * kWave * i;
+      if (q < P::XCH) {
+        const int tt = q / (HB / VEC), hh = h0 + (q % (HB / VEC)) * VEC;
+        if (vec_x)
+          px[i] = buffer_load16(rsx, hh < H ? (tt * H + hh) * (int)sizeof(TIn) : kPastEnd);
+        else
+          px[i] = load_chunk_scalar<TIn>(x + (int64_t)min(t0 + tt, T - 1) * H, hh, H);
       }
     }
 #pragma unroll
     for (int i = 0; i < P::WPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < P::WCH) {
-        const int hh = c / (EB / VEC), ee = (c % (EB / VEC)) * VEC;
-        const int h = min(h0 + hh, H - 1);
-        rw[i] = load_chunk<TIn>(wg + (int64_t)h * E, e0 + ee, E, vec_w);
+      const int q = tid + kLogitWaves * kWave * i;
+      if (q < P::WCH) {
+        const int h = h0 + q / (EB / VEC), ee = e0 + (q % (EB / VEC)) * VEC;
+        if (vec_w)
+          pw[i] = buffer_load16(rsw, (h < H && ee < E) ? (h * E + ee) * (int)sizeof(TIn) : kPastEnd);
+        else
+          pw[i] = load_chunk_scalar<TIn>(wg + (int64_t)min(h, H - 1) * E, ee, E);
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const uint4* px, const uint4* pw) {
 #pragma unroll
     for (int i = 0; i < P::XPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < P::XCH) {
-        const int tt = c / (HB / VEC), hh = (c % (HB / VEC)) * VEC;
+      const int q = tid + kLogitWaves * kWave * i;
+      if (q < P::XCH) {
+        const int tt = q / (HB / VEC), hh = (q % (HB / VEC)) * VEC;
         float f[VEC];
-        widen<TIn>(rx[i], f);
+        widen<TIn>(px[i], f);
 #pragma unroll
-        for (int q = 0; q < VEC; q += 4)
-          *reinterpret_cast<float4*>(&xs[buf][tt][hh + q]) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+        for (int v = 0; v < VEC; v += 4)
+          *reinterpret_cast<float4*>(&xs[buf][tt][hh + v]) = make_float4(f[v], f[v + 1], f[v + 2], f[v + 3]);
       }
     }
 #pragma unroll
     for (int i = 0; i < P::WPT; ++i) {
-      const int c = tid + 256 * i;
-      if (c < P::WCH) {
-        const int hh = c / (EB / VEC), ee = (c % (EB / VEC)) * VEC;
+      const int q = tid + kLogitWaves * kWave * i;
+      if (q < P::WCH) {
+        const int hh = q / (EB / VEC), ee = (q % (EB / VEC)) * VEC;
         float f[VEC];
-        widen<TIn>(rw[i], f);
+        widen<TIn>(pw[i], f);
 #pragma unroll
-        for (int q = 0; q < VEC; q += 4)
-          *reinterpret_cast<float4*>(&ws[buf][hh][ee + q]) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+        for (int v = 0; v < VEC; v += 4)
+          *reinterpret_cast<float4*>(&ws[buf][hh][ee + v]) = make_float4(f[v], f[v + 1], f[v + 2], f[v + 3]);
       }
     }
   };
 
-  float acc[kTokPerWave][EQ];
+  float acc[EQ];
 #pragma unroll
-  for (int i = 0; i < kTokPerWave; ++i)
-#pragma unroll
-    for (int q = 0; q < EQ; ++q) acc[i][q] = 0.0f;
+  for (int q = 0; q < EQ; ++q) acc[q] = 0.0f;
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int hc = 0; hc < nh_chunks; ++hc) {
-    const int buf = hc & 1;
-    if (hc + 1 < nh_chunks) load(hc + 1);
-    const int nh = min(HB, H - hc * HB);
-    const float* xw = &xs[buf][wave * kTokPerWave][0];
-    const float* wl = &ws[buf][0][lane * EQ];
-    // four h at a time: one broadcast float4 of x per token, EQ weights per lane per h
-    auto quad = [&](int hh) {
-      float4 xv[kTokPerWave];
+  // h = hh of the chunk in LDS buffer buf, for the lane's token and the wave's EQ experts
+  auto fma_h = [&](int buf, int hh, float xe) {
+    const float* wl = &ws[buf][hh][wave * EQ];
 #pragma unroll
-      for (int i = 0; i < kTokPerWave; ++i) xv[i] = *reinterpret_cast<const float4*>(xw + i * HB + hh);
+    for (int q = 0; q < EQ; q += 4) {
+      const float4 wv = *reinterpret_cast<const float4*>(wl + q);
+      acc[q + 0] = __builtin_fmaf(xe, wv.x, acc[q + 0]);
+      acc[q + 1] = __builtin_fmaf(xe, wv.y, acc[q + 1]);
+      acc[q + 2] = __builtin_fmaf(xe, wv.z, acc[q + 2]);
+      acc[q + 3] = __builtin_fmaf(xe, wv.w, acc[q + 3]);
+    }
+  };
+  auto compute = [&](int c) {
+    const int buf = c & 1;
+    const int nh = min(HB, H - c * HB);
+    const float* xl = &xs[buf][lane][0];
+    if (nh == HB) {
+      // groups of 8 h, software-pipelined: the LDS reads of group g+1 are issued before the
+      // arithmetic of group g
+      constexpr int G = P::G;
+      float4 xv[2][G / 4], wv[2][G][EQ / 4];
+      auto read = [&](int g0, float4* xg, float4 (*wgp)[EQ / 4]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float wv[EQ];
+        for (int j = 0; j < G / 4; ++j) xg[j] = *reinterpret_cast<const float4*>(xl + g0 + 4 * j);
 #pragma unroll
-        for (int q = 0; q < EQ; ++q) wv[q] = wl[(hh + u) * EB + q];
+        for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-        for (int i = 0; i < kTokPerWave; ++i) {
-          const float xe = u == 0 ? xv[i].x : u == 1 ? xv[i].y : u == 2 ? xv[i].z : xv[i].w;
+          for (int q = 0; q < EQ; q += 4)
+            wgp[hh][q / 4] = *reinterpret_cast<const float4*>(&ws[buf][g0 + hh][wave * EQ + q]);
+      };
+      read(0, xv[0], wv[0]);
 #pragma unroll
-          for (int q = 0; q < EQ; ++q) acc[i][q] = __builtin_fmaf(xe, wv[q], acc[i][q]);
+      for (int gi = 0; gi < HB / G; ++gi) {
+        const int cb = gi & 1;
+        if (gi + 1 < HB / G) read((gi + 1) * G, xv[cb ^ 1], wv[cb ^ 1]);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float4 x4 = xv[cb][hh / 4];
+          const float xe = (hh & 3) == 0 ? x4.x : (hh & 3) == 1 ? x4.y : (hh & 3) == 2 ? x4.z : x4.w;
+#pragma unroll
+          for (int q = 0; q < EQ; q += 4) {
+            acc[q + 0] = __builtin_fmaf(xe, wv[cb][hh][q / 4].x, acc[q + 0]);
+            acc[q + 1] = __builtin_fmaf(xe, wv[cb][hh][q / 4].y, acc[q + 1]);
+            acc[q + 2] = __builtin_fmaf(xe, wv[cb][hh][q / 4].z, acc[q + 2]);
+            acc[q + 3] = __builtin_fmaf(xe, wv[cb][hh][q / 4].w, acc[q + 3]);
+          }
         }
       }
-    };
-    int hh = 0;
-    if (nh == HB) {
-      // full chunk: unrolled so that the next reads are issued under the current FMAs
-#pragma unroll
-      for (int h4 = 0; h4 < HB; h4 += 4) quad(h4);
-      hh = HB;
     } else {
-      for (; hh + 4 <= nh; hh += 4) quad(hh);
+      for (int hh = 0; hh < nh; ++hh) fma_h(buf, hh, xl[hh]);
     }
-    for (; hh < nh; ++hh) {
+  };
+
+  // prologue: chunks 0 .. depth-1 in flight
 #pragma unroll
-      for (int i = 0; i < kTokPerWave; ++i) {
-        const float xe = xw[i * HB + hh];
+  for (int r = 0; r < DEPTH; ++r)
+    if (r < nch) load(r, rx[r], rw[r]);
+  // steady state, unrolled by the register depth so that every stage index is a constant
+  for (int c0 = 0; c0 < nch; c0 += DEPTH) {
 #pragma unroll
-        for (int q = 0; q < EQ; ++q) acc[i][q] = __builtin_fmaf(xe, wl[hh * EB + q], acc[i][q]);
+    for (int r = 0; r < DEPTH; ++r) {
+      const int c = c0 + r;
+      if (c < nch) {
+        store(c & 1, rx[r], rw[r]);
+        __syncthreads();
+        if (c + DEPTH < nch) load(c + DEPTH, rx[r], rw[r]);
+        compute(c);
       }
     }
-    if (hc + 1 < nh_chunks) store(buf ^ 1);
-    __syncthreads();
   }
+
+  const int t = t0 + lane;
+  if (t < T) {
+    float* out = logits + (int64_t)t * E + e0 + wave * EQ;
+    if (e0 + wave * EQ + EQ <= E && (E & 3) == 0) {
 #pragma unroll
-  for (int i = 0; i < kTokPerWave; ++i) {
-    const int t = t0 + wave * kTokPerWave + i;
-    if (t >= T) continue;
+      for (int q = 0; q < EQ; q += 4)
+        *reinterpret_cast<float4*>(out + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
+    } else {
 #pragma unroll
-    for (int q = 0; q < EQ; ++q) {
-      const int e = e0 + lane * EQ + q;
-      if (e < E) logits[(int64_t)t * E + e] = acc[i][q];
+      for (int q = 0; q < EQ; ++q)
+        if (e0 + wave * EQ + q < E) out[q] = acc[q];
     }
   }
 }
@@ -269,20 +322,21 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
 // ---------------------------------------------------------------------------------------------
 template <typename TIn, int EQ>
 static void launch_logits_t(const void* x, const void* w_gate, int T, int H, int E, float* logits, hipStream_t s) {
-  constexpr int EB = kWave * EQ;
+  constexpr int EB = kLogitWaves * EQ;
   const bool vec_x = H % (16 / sizeof(TIn)) == 0 && ((uintptr_t)x & 15) == 0;
   const bool vec_w = E % (16 / sizeof(TIn)) == 0 && ((uintptr_t)w_gate & 15) == 0;
-  dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock, (E + EB - 1) / EB);
+  dim3 grid((T + kLogitTok - 1) / kLogitTok, (E + EB - 1) / EB);
   hipLaunchKernelGGL((router_logits_kernel<TIn, EQ>), grid, dim3(kLogitWaves * kWave), 0, s, (const TIn*)x,
                      (const TIn*)w_gate, T, H, E, logits, (int)vec_x, (int)vec_w);
 }
 
+// Eight chains per lane when that still gives two workgroups per CU, else four (twice the
+// workgroups, twice the broadcast weight reads per multiply-add).
 template <typename TIn>
 static void launch_logits_dt(const void* x, const void* w_gate, int T, int H, int E, float* logits, hipStream_t s) {
-  if (E <= 64)
-    launch_logits_t<TIn, 1>(x, w_gate, T, H, E, logits, s);
-  else if (E <= 128)
-    launch_logits_t<TIn, 2>(x, w_gate, T, H, E, logits, s);
+  const int64_t blocks8 = (int64_t)((T + kLogitTok - 1) / kLogitTok) * ((E + 31) / 32);
+  if (blocks8 >= 512)
+    launch_logits_t<TIn, 8>(x, w_gate, T, H, E, logits, s);
   else
     launch_logits_t<TIn, 4>(x, w_gate, T, H, E, logits, s);
 }
