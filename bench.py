@@ -46,15 +46,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, rows: str):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel source with the same source of its rows; else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_gemm_gate_up_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("kernel_source_sha256_16") != kernel_source_hash() or d.get("gemm1_rows", "x_perm") != rows:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="forward: copy the rows to x_perm in the permute instead of gathering them in GEMM-1")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 512 MiB device copy before the warm-up (counter calibration)")
     args = ap.parse_args()
@@ -127,8 +129,11 @@ def main():
     d_out = dev(d["d_out"], torch) if "d_out" in d else None
     tdt = x.dtype
     I_sh = 0 if sh_gu is None else sh_gu.shape[1] // 2
+    # forward-only workloads fold the row copy of the permute into the first grouped matmul (it
+    # gathers its rows from x); a training step keeps x_perm, which the weight gradients read
+    gather = not wl.backward and not args.no_gather
     bufs = moe.LayerBuffers(T, H, I, E, k, tdt, x.device, logits=given_logits is None, gu_saved=wl.backward,
-                            I_shared=I_sh)
+                            I_shared=I_sh, x_perm=not gather)
     grads = moe.LayerGrads(T, H, I, E, k, tdt, x.device, I_shared=I_sh, router=w_gate is not None) if wl.backward else None
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
@@ -147,11 +152,21 @@ def main():
     logits = bufs.logits if given_logits is None else given_logits
     stages += [
         ("router_topk", lambda: moe.moe_router_topk(logits, k, True, bufs.topk_idx, bufs.topk_w)),
-        ("permute", lambda: moe.moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace)),
-        ("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu(bufs.x_perm, gate_up, bufs.plan.offsets, bufs.h,
-                                                             bufs.gu_saved)),
-        ("gemm_down", lambda: moe.moe_grouped_gemm_down(bufs.h, down, bufs.plan.offsets, bufs.y)),
     ]
+    if gather:
+        stages += [
+            ("permute", lambda: moe.moe_permute(x, bufs.topk_idx, E, None, bufs.plan, bufs.workspace, rows=False)),
+            ("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu_gather(x, bufs.plan.slot_of_row, k, gate_up,
+                                                                        bufs.plan.offsets, None, bufs.h,
+                                                                        bufs.gu_saved)),
+        ]
+    else:
+        stages += [
+            ("permute", lambda: moe.moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace)),
+            ("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu(bufs.x_perm, gate_up, bufs.plan.offsets, bufs.h,
+                                                                 bufs.gu_saved)),
+        ]
+    stages.append(("gemm_down", lambda: moe.moe_grouped_gemm_down(bufs.h, down, bufs.plan.offsets, bufs.y)))
     if sh is not None:
         stages.append(("shared_ffn", lambda: moe.moe_grouped_swiglu_ffn(x, sh_gu, sh_dn, sh["offsets"], sh["h"], sh["y"],
                                                                          sh["gu_saved"])))
@@ -217,10 +232,11 @@ def main():
     b = 2 if tdt == torch.bfloat16 else 4
     # algorithmic work of each call (what the method must read, write and compute)
     gu_flops = 2.0 * N * H * 2 * I
-    gu_bytes = n_active * H * 2 * I * b + N * H * b + N * I * b
+    # the gathering GEMM reads each token's row of x (once, algorithmically) instead of x_perm
+    gu_bytes = n_active * H * 2 * I * b + (T if gather else N) * H * b + N * I * b
     dn_flops = 2.0 * N * I * H
     dn_bytes = n_active * I * H * b + N * I * b + N * H * b
-    perm_bytes = T * H * b + N * H * b + T * k * 4 * 3 + E * 4 * 2
+    perm_bytes = (0 if gather else T * H * b + N * H * b) + T * k * 4 * 3 + E * 4 * 2
     comb_bytes = N * H * b + T * H * b + T * k * 8
     t_gu, t_dn = t_of["gemm_gate_up"], t_of["gemm_down"]
     peak_tf = PEAK_BF16_TFLOPS if tdt == torch.bfloat16 else PEAK_F32_TFLOPS
@@ -230,7 +246,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(gu_flops / t_gu / 1e12, 1), "peak": peak_tf, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = load_traffic(wl.name)
+    roof["traffic"] = load_traffic(wl.name, "gathered" if gather else "x_perm")
     roof["kernel"] = "grouped_gemm_bf16_kernel<true, false, 0, 0> (gate_up + SwiGLU)"
     roof["algorithmic_bytes"] = gu_bytes
     roof["algorithmic_flops"] = gu_flops
@@ -255,7 +271,8 @@ def main():
         "dtype": "bf16" if tdt == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "k": k, "renorm": True,
                    "router": "logits given" if given_logits is not None else "x @ W_g",
-                   "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward"},
+                   "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward",
+                   "gemm1_rows": "gathered from x" if gather else "x_perm"},
         "roofline": roof, "perf": perf,
     }
     if args.cpu_seconds > 0:

@@ -90,6 +90,8 @@ moe_status moe_router_topk(const float* logits, int T, int E, int k, int renorm,
  *   x [T, H] dt; topk_idx [T, k] int32; x_perm [T*k, H] dt (out); counts [E], offsets [E+1],
  *   row_of_slot [T*k], slot_of_row [T*k] int32 (out); workspace: device scratch of at least
  *   moe_permute_workspace_bytes(T, k, E) bytes (contents need no initialisation).
+ * x_perm may be NULL (then x may be too): only the plan (counts, offsets, row maps) is computed, for
+ * the gathering FFN below, which reads the rows from x through slot_of_row.
  * The (counts, offsets, row_of_slot) triple is the layout handle that the FFN and combine take.  */
 size_t moe_permute_workspace_bytes(int T, int k, int E);
 moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t* topk_idx, int k, int E,
@@ -119,6 +121,22 @@ moe_status moe_grouped_gemm_swiglu(const void* x_perm, const void* gate_up, moe_
                                    hipStream_t stream);
 moe_status moe_grouped_gemm_down(const void* h, const void* down, moe_dtype dt, int N, int H, int I, int E,
                                  const int32_t* expert_offsets, void* y, hipStream_t stream);
+
+/* Gathering variants ([FT 3] fused dispatcher: the permute folded into the grouped matmul, so the
+ * permuted copy of x is never written): grouped row r is token slot_of_row[r] / k of x, i.e.
+ *   x_perm[r, :] = x[slot_of_row[r] / k, :]
+ * and the result is bit-identical to moe_permute(x -> x_perm) followed by the calls above.
+ *   x [T, H] dt; slot_of_row [>= N] int32 from moe_permute (device; entries of rows below
+ *   offsets[E] must lie in [0, T*k)); other arguments as moe_grouped_swiglu_ffn. N <= T*k and
+ *   T*H*sizeof(dt) < 2 GiB (MOE_ERR_UNSUPPORTED otherwise).                                        */
+moe_status moe_grouped_gemm_swiglu_gather(const void* x, const int32_t* slot_of_row, int T, int k,
+                                          const void* gate_up, moe_dtype dt, int N, int H, int I, int E,
+                                          const int32_t* expert_offsets, void* h, void* gu_saved,
+                                          hipStream_t stream);
+moe_status moe_grouped_swiglu_ffn_gather(const void* x, const int32_t* slot_of_row, int T, int k,
+                                         const void* gate_up, const void* down, moe_dtype dt, int N, int H,
+                                         int I, int E, const int32_t* expert_offsets, void* h, void* gu_saved,
+                                         void* y, hipStream_t stream);
 
 /* ---- (5) unpermute + gate-weighted combine ---------------------------------------------------------
  * [DS Expert Parallelism] weighted sum of the expert outputs by the gate weights; [MM 8.3] unpermute.

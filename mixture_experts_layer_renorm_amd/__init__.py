@@ -50,6 +50,8 @@ def load_library() -> ctypes.CDLL:
             "moe_grouped_swiglu_ffn": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P]),
             "moe_grouped_gemm_swiglu": (I, [P, P, I, I, I, I, I, P, P, P, P]),
             "moe_grouped_gemm_down": (I, [P, P, I, I, I, I, I, P, P, P]),
+            "moe_grouped_gemm_swiglu_gather": (I, [P, P, I, I, P, I, I, I, I, I, P, P, P, P]),
+            "moe_grouped_swiglu_ffn_gather": (I, [P, P, I, I, P, P, I, I, I, I, I, P, P, P, P, P]),
             "moe_unpermute_combine": (I, [P, I, I, I, I, P, P, P, P, P]),
             "moe_unpermute_combine_bwd": (I, [P, P, I, I, I, I, P, P, P, P, P]),
             "moe_grouped_swiglu_ffn_bwd": (I, [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P]),
@@ -141,13 +143,16 @@ class Plan:
         self.counts, self.offsets, self.row_of_slot, self.slot_of_row = counts, offsets, row_of_slot, slot_of_row
 
 
-def moe_permute(x, topk_idx, E, x_perm=None, plan=None, workspace=None, stream=None):
+def moe_permute(x, topk_idx, E, x_perm=None, plan=None, workspace=None, stream=None, rows=True):
+    """rows=False computes the plan only (no x_perm; for the gathering FFN) and returns (None, plan)."""
     T, H = x.shape
     k = topk_idx.shape[1]
     _need(x, "x"), _need(topk_idx, "topk_idx", torch.int32, (T, k))
     dev = x.device
     N = T * k
-    if x_perm is None:
+    if not rows:
+        x_perm = None
+    elif x_perm is None:
         x_perm = torch.empty((N, H), dtype=x.dtype, device=dev)
     if plan is None:
         plan = Plan(torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
@@ -155,7 +160,8 @@ def moe_permute(x, topk_idx, E, x_perm=None, plan=None, workspace=None, stream=N
     ws_bytes = moe_permute_workspace_bytes(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    _check(load_library().moe_permute(_ptr(x), _dt(x), T, H, _ptr(topk_idx), k, E, _ptr(x_perm), _ptr(plan.counts),
+    _check(load_library().moe_permute(_ptr(x), _dt(x), T, H, _ptr(topk_idx), k, E, _ptr(x_perm) if rows else None,
+                                      _ptr(plan.counts),
                                       _ptr(plan.offsets), _ptr(plan.row_of_slot), _ptr(plan.slot_of_row),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "moe_permute")
@@ -178,6 +184,50 @@ def moe_grouped_swiglu_ffn(x_perm, gate_up, down, expert_offsets, h=None, y=None
     _check(load_library().moe_grouped_swiglu_ffn(_ptr(x_perm), _ptr(gate_up), _ptr(down), _dt(x_perm), N, H, I, E,
                                                  _ptr(expert_offsets), _ptr(h), _ptr(gu_saved), _ptr(y),
                                                  _stream(stream)), "moe_grouped_swiglu_ffn")
+    return y, h
+
+
+def moe_grouped_gemm_swiglu_gather(x, slot_of_row, k, gate_up, expert_offsets, N=None, h=None, gu_saved=None,
+                                   stream=None):
+    """First grouped matmul + SwiGLU with the grouped rows gathered from x: row r is token
+    slot_of_row[r] // k. N defaults to T*k."""
+    T, H = x.shape
+    N = T * k if N is None else N
+    E = gate_up.shape[0] // H
+    I = gate_up.shape[1] // 2
+    _need(x, "x"), _need(slot_of_row, "slot_of_row", torch.int32)
+    _need(gate_up, "gate_up", x.dtype, (E * H, 2 * I)), _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    if h is None:
+        h = torch.empty((N, I), dtype=x.dtype, device=x.device)
+    _need(h, "h", x.dtype, (N, I))
+    if gu_saved is not None:
+        _need(gu_saved, "gu_saved", x.dtype, (N, 2 * I))
+    _check(load_library().moe_grouped_gemm_swiglu_gather(_ptr(x), _ptr(slot_of_row), T, k, _ptr(gate_up), _dt(x), N, H,
+                                                         I, E, _ptr(expert_offsets), _ptr(h), _ptr(gu_saved),
+                                                         _stream(stream)), "moe_grouped_gemm_swiglu_gather")
+    return h
+
+
+def moe_grouped_swiglu_ffn_gather(x, slot_of_row, k, gate_up, down, expert_offsets, N=None, h=None, y=None,
+                                  gu_saved=None, stream=None):
+    """The grouped SwiGLU FFN with the grouped rows gathered from x (row r is token slot_of_row[r] // k)."""
+    T, H = x.shape
+    N = T * k if N is None else N
+    E = gate_up.shape[0] // H
+    I = gate_up.shape[1] // 2
+    _need(x, "x"), _need(slot_of_row, "slot_of_row", torch.int32), _need(gate_up, "gate_up", x.dtype, (E * H, 2 * I))
+    _need(down, "down", x.dtype, (E * I, H)), _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    if h is None:
+        h = torch.empty((N, I), dtype=x.dtype, device=x.device)
+    if y is None:
+        y = torch.empty((N, H), dtype=x.dtype, device=x.device)
+    _need(h, "h", x.dtype, (N, I)), _need(y, "y", x.dtype, (N, H))
+    if gu_saved is not None:
+        _need(gu_saved, "gu_saved", x.dtype, (N, 2 * I))
+    _check(load_library().moe_grouped_swiglu_ffn_gather(_ptr(x), _ptr(slot_of_row), T, k, _ptr(gate_up), _ptr(down),
+                                                        _dt(x), N, H, I, E, _ptr(expert_offsets), _ptr(h),
+                                                        _ptr(gu_saved), _ptr(y), _stream(stream)),
+           "moe_grouped_swiglu_ffn_gather")
     return y, h
 
 
@@ -315,12 +365,12 @@ class LayerBuffers:
     gu_saved keeps the expert pre-activations for the backward; I_shared > 0 adds the shared expert's
     buffers (its segment offsets {0, T} are copied to the device here, once)."""
 
-    def __init__(self, T, H, I, E, k, dtype, device, logits=True, gu_saved=False, I_shared=0):
+    def __init__(self, T, H, I, E, k, dtype, device, logits=True, gu_saved=False, I_shared=0, x_perm=True):
         N = T * k
         self.logits = torch.empty((T, E), dtype=torch.float32, device=device) if logits else None
         self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=device)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
-        self.x_perm = torch.empty((N, H), dtype=dtype, device=device)
+        self.x_perm = torch.empty((N, H), dtype=dtype, device=device) if x_perm else None
         self.plan = Plan(torch.empty(E, dtype=torch.int32, device=device),
                          torch.empty(E + 1, dtype=torch.int32, device=device),
                          torch.empty(N, dtype=torch.int32, device=device),
@@ -341,24 +391,33 @@ class LayerBuffers:
 
 
 def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True, residual=None, bufs=None,
-                      shared_gate_up=None, shared_down=None, save_for_backward=False, stream=None):
+                      shared_gate_up=None, shared_down=None, save_for_backward=False, stream=None, gather=False):
     """Router (logits unless given) -> top-k -> permute -> grouped SwiGLU FFN -> combine.
     With shared_gate_up / shared_down, the shared expert runs on every token as a one-segment grouped
-    FFN and its output is the combine's residual (a separate residual is then not accepted)."""
+    FFN and its output is the combine's residual (a separate residual is then not accepted).
+    gather=True: the permute computes the plan only and the first grouped matmul gathers its rows
+    from x (same result, bit for bit; x_perm is never written, so there is no backward from it)."""
     T, H = x.shape
     E = gate_up.shape[0] // H
     I = gate_up.shape[1] // 2
     I_sh = 0 if shared_gate_up is None else shared_gate_up.shape[1] // 2
     if I_sh and residual is not None:
         raise ValueError("moe_layer_forward: the shared expert's output is the residual; pass one or the other")
+    if gather and save_for_backward:
+        raise ValueError("moe_layer_forward: gather=True keeps no x_perm, which the backward needs")
     if bufs is None:
         bufs = LayerBuffers(T, H, I, E, k, x.dtype, x.device, logits=logits is None, gu_saved=save_for_backward,
-                            I_shared=I_sh)
+                            I_shared=I_sh, x_perm=not gather)
     if logits is None:
         logits = moe_router_logits(x, w_gate, bufs.logits, stream)
     moe_router_topk(logits, k, renorm, bufs.topk_idx, bufs.topk_w, stream)
-    moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace, stream)
-    moe_grouped_swiglu_ffn(bufs.x_perm, gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, bufs.gu_saved, stream)
+    if gather:
+        moe_permute(x, bufs.topk_idx, E, None, bufs.plan, bufs.workspace, stream, rows=False)
+        moe_grouped_swiglu_ffn_gather(x, bufs.plan.slot_of_row, k, gate_up, down, bufs.plan.offsets, None, bufs.h,
+                                      bufs.y, bufs.gu_saved, stream)
+    else:
+        moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace, stream)
+        moe_grouped_swiglu_ffn(bufs.x_perm, gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, bufs.gu_saved, stream)
     if I_sh:
         sh = bufs.shared
         moe_grouped_swiglu_ffn(x, shared_gate_up, shared_down, sh["offsets"], sh["h"], sh["y"], sh["gu_saved"], stream)

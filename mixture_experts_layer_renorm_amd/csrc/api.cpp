@@ -91,7 +91,8 @@ moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t*
     if (e == hipSuccess) e = moe::launch_fill_i32(offsets, E + 1, 0, stream);
     return hip_status(e, "moe_permute");
   }
-  REQUIRE(x && topk_idx && x_perm && row_of_slot && slot_of_row, MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+  REQUIRE(topk_idx && row_of_slot && slot_of_row, MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+  REQUIRE(!x_perm || x, MOE_ERR_INVALID_ARG, "moe_permute: x is NULL but x_perm is not");
   const size_t need = moe::permute_workspace_bytes(T, E);
   REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE,
           "moe_permute: workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
@@ -127,6 +128,55 @@ moe_status moe_grouped_gemm_swiglu(const void* x_perm, const void* gate_up, moe_
             MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   return hip_status(moe::launch_gemm_gate_up(x_perm, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream),
                     fn);
+}
+
+namespace {
+moe_status check_gather(const char* fn, moe_dtype dt, int T, int k, int N, int H) {
+  REQUIRE(T >= 0 && k >= 1 && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: T=%d k=%d (need T >= 0, 1 <= k <= %d)", fn, T, k,
+          kMaxK);
+  REQUIRE((int64_t)N <= (int64_t)T * k, MOE_ERR_INVALID_ARG, "%s: N=%d rows but only T*k=%lld slots", fn, N,
+          (long long)T * k);
+  REQUIRE((int64_t)T * H * (int64_t)moe::dtype_bytes((int)dt) < (1LL << 31), MOE_ERR_UNSUPPORTED, "%s: x [T=%d, H=%d] exceeds 2 GiB", fn, T,
+          H);
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_grouped_gemm_swiglu_gather(const void* x, const int32_t* slot_of_row, int T, int k, const void* gate_up,
+                                          moe_dtype dt, int N, int H, int I, int E, const int32_t* expert_offsets,
+                                          void* h, void* gu_saved, hipStream_t stream) {
+  const char* fn = "moe_grouped_gemm_swiglu_gather";
+  moe_status st = check_ffn(fn, dt, N, H, I, E);
+  if (st == MOE_OK) st = check_gather(fn, dt, T, k, N, H);
+  if (st != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE(x && slot_of_row && gate_up && expert_offsets && h, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (dt == MOE_BF16)
+    REQUIRE(!misaligned16(x) && !misaligned16(gate_up) && !misaligned16(h) && !misaligned16(gu_saved),
+            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
+  return hip_status(moe::launch_gemm_gate_up(x, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream,
+                                             slot_of_row, k, T),
+                    fn);
+}
+
+moe_status moe_grouped_swiglu_ffn_gather(const void* x, const int32_t* slot_of_row, int T, int k, const void* gate_up,
+                                         const void* down, moe_dtype dt, int N, int H, int I, int E,
+                                         const int32_t* expert_offsets, void* h, void* gu_saved, void* y,
+                                         hipStream_t stream) {
+  const char* fn = "moe_grouped_swiglu_ffn_gather";
+  moe_status st = check_ffn(fn, dt, N, H, I, E);
+  if (st == MOE_OK) st = check_gather(fn, dt, T, k, N, H);
+  if (st != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE(x && slot_of_row && gate_up && down && expert_offsets && h && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (dt == MOE_BF16)
+    REQUIRE(!misaligned16(x) && !misaligned16(gate_up) && !misaligned16(down) && !misaligned16(h) &&
+                !misaligned16(y) && !misaligned16(gu_saved),
+            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
+  hipError_t e = moe::launch_gemm_gate_up(x, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream,
+                                          slot_of_row, k, T);
+  if (e == hipSuccess) e = moe::launch_gemm_down(h, down, (int)dt, N, H, I, E, expert_offsets, y, stream);
+  return hip_status(e, fn);
 }
 
 moe_status moe_grouped_gemm_down(const void* h, const void* down, moe_dtype dt, int N, int H, int I, int E,

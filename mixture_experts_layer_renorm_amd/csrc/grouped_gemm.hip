@@ -128,6 +128,8 @@ struct GemmArgs {
   const uint16_t* gu;  // saved g|u [rows, 2*N] read by the SwiGLU-backward epilogue
   uint16_t* gu_out;    // optional g|u written by the SwiGLU epilogue [rows, 2*N]
   const int32_t* offsets;
+  const int32_t* a_slot;  // optional (row-grouped A): A row r is row a_slot[r] / a_div of A, i.e. the
+  int a_div;              // grouped rows are gathered from the token matrix through the slot map
   int E;
   int M, N, K;         // SchedRows: N output columns, K; SchedWgrad: M, N per expert (K from offsets)
   int lda, ldb, ldc;
@@ -237,8 +239,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     nt = ti.nt;
     n0 = nt * kBN;
     K = g.K;
-    abase = g.A + (int64_t)m0 * g.lda;       // rows [row0, row_end) of the grouped operand
-    a_records = mvalid * g.lda * 2;
+    if (g.a_slot) {                          // gathered: rows come from the token matrix
+      abase = g.A;
+      a_records = g.M * g.lda * 2;           // g.M = tokens
+    } else {
+      abase = g.A + (int64_t)m0 * g.lda;     // rows [row0, row_end) of the grouped operand
+      a_records = mvalid * g.lda * 2;
+    }
     bbase = g.B + (int64_t)e * g.b_expert;   // expert e's weight block
     b_records = g.b_rows * g.ldb * 2;
   } else {
@@ -278,8 +285,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       const int r = (wave * kDmaA + i) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ swz_a(r);
       a_kc[i] = c * 8;
-      a_ok[i] = true;
-      a_off[i] = (r * g.lda + c * 8) * 2;
+      a_ok[i] = r < mvalid;
+      const int src = g.a_slot ? (a_ok[i] ? g.a_slot[m0 + r] / g.a_div : 0) : r;
+      a_off[i] = (src * g.lda + c * 8) * 2;
     } else {
       const int kr = (wave * kDmaA + i) * 2 + (lane >> 5);
       const int cb = (lane & 31) ^ swz_b(kr);
@@ -320,11 +328,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   const int x_r = kBM + wave * 16 + (lane >> 2);
   const int x_c = (lane & 3) ^ swz_a(x_r);
   const int x_kc = x_c * 8;
-  const int x_off = (x_r * g.lda + x_c * 8) * 2;
+  const bool x_ok = x_real && x_r < mvalid;
+  const int x_src = (ROWS && g.a_slot) ? (x_ok ? g.a_slot[m0 + x_r] / g.a_div : 0) : x_r;
+  const int x_off = (x_src * g.lda + x_c * 8) * 2;
   auto dma = [&](int kt, uint8_t* sa, uint8_t* sb) {
     const int k0 = kt * kBK;
     if constexpr (ROWS) {
-      const int off = (x_real && k0 + x_kc < K) ? x_off + k0 * 2 : kOutOfRange;
+      const int off = (x_ok && k0 + x_kc < K) ? x_off + k0 * 2 : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(x_real ? sa + (kBM / 16 + wave) * 1024 : sSpare), 16,
                                                off, 0, 0, 0);
     }
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     for (int i = 0; i < kDmaA; ++i) {
       int off;
       if constexpr (A_ROWS)
-        off = (k0 + a_kc[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange;
+        off = (a_ok[i] && k0 + a_kc[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange;
       else
         off = a_ok[i] ? a_off[i] + k0 * g.lda * 2 : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + (wave * kDmaA + i) * 1024), 16, off, 0, 0, 0);
@@ -884,13 +894,14 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets
 
 __global__ __launch_bounds__(256) void grouped_ffn1_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
                                                                const int32_t* __restrict__ offsets, int E, int N, int K,
-                                                               int I, float* __restrict__ h, float* __restrict__ gu_saved) {
+                                                               int I, float* __restrict__ h, float* __restrict__ gu_saved,
+                                                               const int32_t* __restrict__ a_slot, int a_div) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)N * I) return;
   const int r = (int)(gid / I), j = (int)(gid % I);
   const int e = expert_of_row(offsets, E, r);
   if (e < 0) return;
-  const float* a = A + (int64_t)r * K;
+  const float* a = A + (int64_t)(a_slot ? a_slot[r] / a_div : r) * K;
   const float* w = W + (int64_t)e * K * 2 * I;
   float g = 0.0f, u = 0.0f;
   for (int k = 0; k < K; ++k) {
@@ -931,11 +942,17 @@ static void launch_generic(GemmArgs g, int64_t grid, hipStream_t s) {
 // worst-case row tiles over any distribution of N rows among E experts
 static inline int64_t row_tiles_bound(int N, int E) { return ((int64_t)N + (int64_t)E * (kBMX - 1)) / kBMX; }
 
+// x_perm [N, H] holds the grouped rows; or, with slot_of_row, x is the token matrix [T, H] and row r
+// is token slot_of_row[r] / k (the rows are gathered inside the GEMM)
 hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, int N, int H, int I, int E,
-                               const int32_t* offsets, void* h, void* gu_saved, hipStream_t s) {
+                               const int32_t* offsets, void* h, void* gu_saved, hipStream_t s,
+                               const int32_t* slot_of_row, int k, int T) {
   if (dt == kBF16) {
     GemmArgs g{};
     g.A = (const uint16_t*)x_perm;
+    g.a_slot = slot_of_row;
+    g.a_div = k;
+    g.M = T;
     g.B = (const uint16_t*)gate_up;
     g.C = (uint16_t*)h;
     g.gu_out = (uint16_t*)gu_saved;
@@ -953,7 +970,8 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
   } else {
     const int64_t n1 = (int64_t)N * I;
     hipLaunchKernelGGL(grouped_ffn1_f32_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s,
-                       (const float*)x_perm, (const float*)gate_up, offsets, E, N, H, I, (float*)h, (float*)gu_saved);
+                       (const float*)x_perm, (const float*)gate_up, offsets, E, N, H, I, (float*)h, (float*)gu_saved,
+                       slot_of_row, k);
   }
   return hipGetLastError();
 }

@@ -28,7 +28,8 @@ hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* to
 
 // grouped_gemm.hip
 hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, int N, int H, int I, int E,
-                               const int32_t* offsets, void* h, void* gu_saved, hipStream_t s);
+                               const int32_t* offsets, void* h, void* gu_saved, hipStream_t s,
+                               const int32_t* slot_of_row = nullptr, int k = 1, int T = 0);
 hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int H, int I, int E, const int32_t* offsets,
                             void* y, hipStream_t s);
 hipError_t launch_gemm_down_bwd(const void* d_y, const void* down, const void* gu_saved, int N, int H, int I, int E,

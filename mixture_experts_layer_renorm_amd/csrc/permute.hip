@@ -159,8 +159,10 @@ hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* to
   hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(kPlanThreads), 0, s, topk_idx, T, k, E, chunk_counts);
   hipLaunchKernelGGL(permute_plan_kernel, dim3(nchunks), dim3(kPlanThreads), 0, s, topk_idx, T, k, E, chunk_counts,
                      nchunks, counts, offsets, row_of_slot, slot_of_row);
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3((T + kScatterWaves - 1) / kScatterWaves), dim3(kScatterWaves * kWave),
-                     0, s, (const uint8_t*)x, T, row_bytes, k, row_of_slot, (uint8_t*)x_perm, vec16);
+  if (x_perm)  // else the plan only: a gathering GEMM reads the rows from x itself
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3((T + kScatterWaves - 1) / kScatterWaves),
+                       dim3(kScatterWaves * kWave), 0, s, (const uint8_t*)x, T, row_bytes, k, row_of_slot,
+                       (uint8_t*)x_perm, vec16);
   return hipGetLastError();
 }
 
