@@ -25,7 +25,11 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   }
 }
 
-// bf16, H % 8 == 0, 16-byte aligned rows
+// bf16, H % 8 == 0, 16-byte aligned rows. The loads of up to kCombineBatch rows are all issued
+// before the multiply-adds that consume them (a dropped slot loads row 0 and skips its
+// multiply-add), so each lane keeps 2 * kCombineBatch 16-byte loads in flight.
+constexpr int kCombineBatch = 8;
+
 __global__ __launch_bounds__(kCombineWaves * kWave) void combine_bf16_kernel(
     const uint16_t* __restrict__ y, int T, int H, int k, const int32_t* __restrict__ row_of_slot,
     const float* __restrict__ topk_w, const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
@@ -50,18 +54,31 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_bf16_kernel(
         for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
       }
     }
-    for (int j = 0; j < k; ++j) {
-      const int r = __shfl(my_row, j, kWave);
-      const float w = __shfl(my_w, j, kWave);
-      if (r < 0) continue;
+    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+      uint4 buf[kCombineBatch][2];
+      int rows[kCombineBatch];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int v = v0 + u * kWave + lane;
-        if (live[u]) {
-          float f[8];
-          unpack8(y4[(int64_t)r * nvec + v], f);
+      for (int jj = 0; jj < kCombineBatch; ++jj) {
+        rows[jj] = j0 + jj < k ? __shfl(my_row, j0 + jj, kWave) : -1;
+        const int64_t rr = max(rows[jj], 0);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[u][i] = __builtin_fmaf(w, f[i], acc[u][i]);
+        for (int u = 0; u < 2; ++u) {
+          const int v = v0 + u * kWave + lane;
+          if (j0 + jj < k && live[u]) buf[jj][u] = y4[rr * nvec + v];
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kCombineBatch; ++jj) {
+        if (rows[jj] < 0) continue;  // also j >= k
+        const float w = __shfl(my_w, j0 + jj, kWave);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (live[u]) {
+            float f[8];
+            unpack8(buf[jj][u], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = __builtin_fmaf(w, f[i], acc[u][i]);
+          }
         }
       }
     }

@@ -46,8 +46,21 @@ __global__ __launch_bounds__(kPlanThreads) void permute_plan_kernel(
   __shared__ int wave_tot[kPlanThreads / kWave];
   const int c = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += kPlanThreads) {
+    // the chunk counts of expert e, sixteen independent loads at a time (one at a time, the loop
+    // is a chain of L2 round trips)
     int tot = 0, before = 0;
-    for (int cc = 0; cc < nchunks; ++cc) {
+    int cc = 0;
+    for (; cc + 16 <= nchunks; cc += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = chunk_counts[(int64_t)(cc + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        tot += v[u];
+        if (cc + u < c) before += v[u];
+      }
+    }
+    for (; cc < nchunks; ++cc) {
       const int v = chunk_counts[(int64_t)cc * E + e];
       tot += v;
       if (cc < c) before += v;
