@@ -96,6 +96,20 @@ def router_topk(logits: np.ndarray, k: int, renorm: bool = True):
     return idx, w
 
 
+def router_stats(logits: np.ndarray, topk_idx: np.ndarray, want_probs: bool = True):
+    """(probs [T,E] or None, mean_prob [E], load [E]) in fp64 / int64: the full softmax per token,
+    its mean over tokens, and how many (token, slot) pairs chose each expert."""
+    logits = _c(logits, np.float32)
+    topk_idx = _c(topk_idx, np.int32)
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    probs = np.empty((T, E), np.float64) if want_probs else None
+    mean = np.empty(E, np.float64)
+    load = np.empty(E, np.int64)
+    _call("orc_router_stats", _p(logits), _p(topk_idx), I64(T), I64(E), I64(k), _p(probs), _p(mean), _p(load))
+    return probs, mean, load
+
+
 def permute_plan(topk_idx: np.ndarray, E: int):
     topk_idx = _c(topk_idx, np.int32)
     T, k = topk_idx.shape

@@ -93,6 +93,42 @@ int orc_router_topk(const float* logits, int64_t T, int64_t E, int64_t k, int re
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* Router statistics: the full softmax per token, its mean over tokens, and the expert load.   */
+int orc_router_stats(const float* logits, const int32_t* topk_idx, int64_t T, int64_t E, int64_t k,
+                     double* probs, double* mean_prob, int64_t* load) {
+    if (!logits || !topk_idx || !mean_prob || !load || T < 0 || E < 1 || k < 1) return -1;
+    for (int64_t e = 0; e < E; ++e) {
+        mean_prob[e] = 0.0;
+        load[e] = 0;
+    }
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        double m = (double)l[0];
+        for (int64_t e = 1; e < E; ++e)
+            if ((double)l[e] > m) m = (double)l[e];
+        double den = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - m);
+            den += p[e];
+        }
+        for (int64_t e = 0; e < E; ++e) {
+            p[e] /= den;
+            mean_prob[e] += p[e];
+            if (probs) probs[t * E + e] = p[e];
+        }
+        for (int64_t j = 0; j < k; ++j) {
+            const int32_t e = topk_idx[t * k + j];
+            if (e >= 0 && e < E) load[e] += 1;
+        }
+    }
+    free(p);
+    if (T > 0)
+        for (int64_t e = 0; e < E; ++e) mean_prob[e] /= (double)T;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Permute plan: rows grouped by expert, tokens ascending inside each expert.                  */
 int orc_permute_plan(const int32_t* topk_idx, int64_t T, int64_t k, int64_t E, int32_t* counts,
                      int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row) {

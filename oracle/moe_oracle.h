@@ -34,6 +34,15 @@ enum { ORC_F32 = 0, ORC_BF16 = 1 };
 int orc_router_logits(const void* x, const void* w_gate, int dt, int64_t T, int64_t H, int64_t E,
                       float* logits);
 
+/* Router statistics for an auxiliary load-balance loss (the practice doc's section 8.1 names an
+ * auxiliary-loss capture; the DeepSeek guide's Automodel section keeps the full softmax):
+ *   probs[t*E+e]  = exp(l_e - m) / sum_{e'} exp(l_e' - m)      (m = max_e l_e; full softmax)
+ *   mean_prob[e]  = (1/T) sum_t probs[t*E+e]
+ *   load[e]       = #{(t, j) : topk_idx[t*k+j] == e}          (indices outside [0, E) ignored)
+ * probs may be NULL. */
+int orc_router_stats(const float* logits, const int32_t* topk_idx, int64_t T, int64_t E, int64_t k,
+                     double* probs, double* mean_prob, int64_t* load);
+
 /* Top-k by (logit descending, expert index ascending); slot j = rank j.
  * renorm=1: w_j = exp(l_j - m) / sum_{i in S} exp(l_i - m)   (softmax renormalised over S)
  * renorm=0: w_j = exp(l_j - m) / sum_{all e} exp(l_e - m)     (raw softmax probability) */

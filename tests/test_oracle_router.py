@@ -157,3 +157,36 @@ def test_bf16_rounding_of_inputs_is_nearest_even():
     assert abs(back[4] + 3.140625) == 0.0
     for v, b in zip(vals, back):
         assert abs(float(v) - float(b)) <= abs(float(v)) * 2.0 ** -8
+
+
+# ---- router statistics ------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (300, 128, 8), (17, 5, 5), (1, 1, 1)])
+def test_router_stats_against_scipy_and_bincount(T, E, k):
+    g = np.random.default_rng(1234 + T)
+    logits = (g.standard_normal((T, E)) * 2).astype(np.float32)
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    probs, mean, load = oracle.router_stats(logits, idx)
+    ref = softmax(logits.astype(np.float64), axis=1)
+    assert np.max(np.abs(probs - ref)) <= 1e-15
+    assert np.max(np.abs(mean - ref.mean(axis=0))) <= 1e-15
+    assert np.array_equal(load, np.bincount(idx.ravel(), minlength=E))
+    assert load.sum() == T * k
+    assert abs(mean.sum() - 1.0) <= 1e-12
+
+
+def test_router_stats_closed_forms_and_dropped_slots():
+    T, E, k = 10, 16, 4
+    probs, mean, load = oracle.router_stats(np.zeros((T, E), np.float32), np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+    assert np.all(probs == 1.0 / E) and np.all(mean == 1.0 / E)
+    assert list(load) == [T] * k + [0] * (E - k)
+    idx = np.array([[0, -1, E, 3]] * T, np.int32)           # out-of-range indices are not counted
+    _, _, load = oracle.router_stats(np.zeros((T, E), np.float32), idx, want_probs=False)
+    assert load[0] == T and load[3] == T and load.sum() == 2 * T
+
+
+def test_router_stats_match_raw_softmax_weights():
+    g = np.random.default_rng(99)
+    logits = (g.standard_normal((50, 32)) * 3).astype(np.float32)
+    idx, w = oracle.router_topk(logits, 6, renorm=False)
+    probs, _, _ = oracle.router_stats(logits, idx)
+    assert np.max(np.abs(np.take_along_axis(probs, idx.astype(np.int64), axis=1) - w)) <= 1e-15
