@@ -81,6 +81,19 @@ moe_status moe_router_logits(const void* x, const void* w_gate, moe_dtype dt, in
 moe_status moe_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
                            float* topk_w, hipStream_t stream);
 
+/* Router statistics for an auxiliary load-balance loss ([MM 8.1]: the trainer installs an
+ * auxiliary-loss capture; [DS Automodel] keeps the full softmax probabilities):
+ *   probs[t, e]  = exp(l[t,e] - m_t) / sum_e' exp(l[t,e'] - m_t)    (full softmax, fp32; may be NULL)
+ *   mean_prob[e] = (1/T) sum_t probs[t, e]                           (fp32, fixed summation order)
+ *   load[e]      = #{(t, j) : topk_idx[t, j] == e}                   (int32; indices outside [0, E)
+ *                                                                      are not counted)
+ *   logits [T, E] fp32 (finite); topk_idx [T, k] int32; workspace: device scratch of at least
+ *   moe_router_stats_workspace_bytes(T, E) bytes (no initialisation needed). T = 0 gives zeros.   */
+size_t moe_router_stats_workspace_bytes(int T, int E);
+moe_status moe_router_stats(const float* logits, const int32_t* topk_idx, int T, int E, int k, float* probs,
+                            float* mean_prob, int32_t* load, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* ---- (3) permute ----------------------------------------------------------------------------------
  * [DS VeOmni] group the N = T*k rows by expert: counts[e] = #slots choosing e, offsets = exclusive
  * scan (offsets[E] = number of valid slots), rows ordered by (expert, token) ascending:

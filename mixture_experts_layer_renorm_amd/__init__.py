@@ -45,6 +45,8 @@ def load_library() -> ctypes.CDLL:
             "moe_abi_version": (I, []),
             "moe_router_logits": (I, [P, P, I, I, I, I, P, P]),
             "moe_router_topk": (I, [P, I, I, I, I, P, P, P]),
+            "moe_router_stats_workspace_bytes": (Z, [I, I]),
+            "moe_router_stats": (I, [P, P, I, I, I, P, P, P, P, Z, P]),
             "moe_permute_workspace_bytes": (Z, [I, I, I]),
             "moe_permute": (I, [P, I, I, I, P, I, I, P, P, P, P, P, P, Z, P]),
             "moe_grouped_swiglu_ffn": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P]),
@@ -141,6 +143,31 @@ class Plan:
 
     def __init__(self, counts, offsets, row_of_slot, slot_of_row):
         self.counts, self.offsets, self.row_of_slot, self.slot_of_row = counts, offsets, row_of_slot, slot_of_row
+
+
+def moe_router_stats(logits, topk_idx, want_probs=True, probs=None, mean_prob=None, load=None, workspace=None,
+                     stream=None):
+    """Full softmax per token (optional), its mean over tokens and the per-expert load, for an
+    auxiliary load-balance loss. Returns (probs or None, mean_prob [E] fp32, load [E] int32)."""
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    _need(logits, "logits", torch.float32, (T, E)), _need(topk_idx, "topk_idx", torch.int32, (T, k))
+    dev = logits.device
+    if want_probs and probs is None:
+        probs = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if not want_probs:
+        probs = None
+    if mean_prob is None:
+        mean_prob = torch.empty(E, dtype=torch.float32, device=dev)
+    if load is None:
+        load = torch.empty(E, dtype=torch.int32, device=dev)
+    ws = int(load_library().moe_router_stats_workspace_bytes(T, E))
+    if workspace is None:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(load_library().moe_router_stats(_ptr(logits), _ptr(topk_idx), T, E, k, _ptr(probs), _ptr(mean_prob),
+                                           _ptr(load), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_router_stats")
+    return probs, mean_prob, load
 
 
 def moe_permute(x, topk_idx, E, x_perm=None, plan=None, workspace=None, stream=None, rows=True):

@@ -69,6 +69,31 @@ moe_status moe_router_topk(const float* logits, int T, int E, int k, int renorm,
   return hip_status(moe::launch_router_topk(logits, T, E, k, renorm, topk_idx, topk_w, stream), "moe_router_topk");
 }
 
+size_t moe_router_stats_workspace_bytes(int T, int E) {
+  if (T <= 0 || E <= 0) return 0;
+  return moe::router_stats_workspace_bytes(T, E);
+}
+
+moe_status moe_router_stats(const float* logits, const int32_t* topk_idx, int T, int E, int k, float* probs,
+                            float* mean_prob, int32_t* load, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  const char* fn = "moe_router_stats";
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "%s: T=%d must be >= 0", fn, T);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  REQUIRE(k >= 1 && k <= E && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, min(E=%d, %d)]", fn, k, E, kMaxK);
+  REQUIRE(mean_prob && load, MOE_ERR_INVALID_ARG, "%s: null mean_prob/load", fn);
+  if (T == 0) {  // no tokens: zero statistics (fill kernels; 0.0f is all-zero bits)
+    hipError_t e = moe::launch_fill_i32((int32_t*)mean_prob, E, 0, stream);
+    if (e == hipSuccess) e = moe::launch_fill_i32(load, E, 0, stream);
+    return hip_status(e, fn);
+  }
+  REQUIRE(logits && topk_idx, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  const size_t need = moe::router_stats_workspace_bytes(T, E);
+  REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+          workspace ? workspace_bytes : (size_t)0, need);
+  return hip_status(moe::launch_router_stats(logits, topk_idx, T, E, k, probs, mean_prob, load, workspace, stream), fn);
+}
+
 size_t moe_permute_workspace_bytes(int T, int k, int E) {
   (void)k;
   if (T <= 0 || E <= 0) return 0;

@@ -14,6 +14,9 @@ inline size_t dtype_bytes(int dt) { return dt == kF32 ? 4 : 2; }
 // router.hip
 hipError_t launch_router_logits(const void* x, const void* w_gate, int dt, int T, int H, int E, float* logits,
                                 hipStream_t s);
+size_t router_stats_workspace_bytes(int T, int E);
+hipError_t launch_router_stats(const float* logits, const int32_t* topk_idx, int T, int E, int k, float* probs,
+                               float* mean_prob, int32_t* load, void* workspace, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w,
                               hipStream_t s);
 

@@ -320,6 +320,137 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// Router statistics for an auxiliary load-balance loss: the full softmax per token (probs), its
+// sum over tokens, and the expert load (how many (token, slot) pairs chose each expert).
+// Stage 1: a workgroup of 4 waves owns kStatsTok tokens, a wave a contiguous run of them in
+// ascending order; lane j holds experts j, j+64, ... Each wave sums its tokens' probabilities,
+// the workgroup adds the four wave sums in wave order and writes one partial row per workgroup,
+// and counts its slots' experts in LDS (integers). Stage 2 adds the partial rows in workgroup
+// order. No floating-point atomics, so the result is the same on every run.
+constexpr int kStatsWaves = 4;
+constexpr int kStatsTok = 128;
+constexpr int kStatsMaxE = 1024;
+
+size_t router_stats_workspace_bytes(int T, int E) {
+  const int64_t nblk = ((int64_t)T + kStatsTok - 1) / kStatsTok;
+  return (size_t)(nblk * E * (int64_t)(sizeof(float) + sizeof(int32_t)));
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kStatsWaves * kWave) void router_stats_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx, int T, int E, int k,
+    float* __restrict__ probs, float* __restrict__ part_p, int32_t* __restrict__ part_load) {
+  __shared__ float wsum[kStatsWaves][VPL * kWave];
+  __shared__ int cnt[kStatsMaxE];
+  const int lane = lane_id(), wave = (int)(threadIdx.x / kWave);
+  const int blk = blockIdx.x;
+  const int t0 = blk * kStatsTok;
+  for (int e = threadIdx.x; e < E; e += kStatsWaves * kWave) cnt[e] = 0;
+  float acc[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) acc[q] = 0.0f;
+  constexpr int TPW = kStatsTok / kStatsWaves;
+  for (int i = 0; i < TPW; ++i) {
+    const int t = t0 + wave * TPW + i;
+    if (t >= T) break;
+    const float* l = logits + (int64_t)t * E;
+    float v[VPL];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      const int e = q * kWave + lane;
+      v[q] = e < E ? l[e] : -INFINITY;
+      m = fmaxf(m, v[q]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    float ex[VPL], se = 0.0f;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      ex[q] = q * kWave + lane < E ? expf(v[q] - m) : 0.0f;
+      se += ex[q];
+    }
+    const float den = wave_sum(se);
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      const int e = q * kWave + lane;
+      const float p = ex[q] / den;
+      acc[q] += p;
+      if (probs && e < E) probs[(int64_t)t * E + e] = p;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) wsum[wave][q * kWave + lane] = acc[q];
+  __syncthreads();
+  const int64_t s0 = (int64_t)t0 * k, s1 = (int64_t)min(T, t0 + kStatsTok) * k;
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += kStatsWaves * kWave) {
+    const int e = topk_idx[s];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kStatsWaves * kWave) {
+    part_p[(int64_t)blk * E + e] = ((wsum[0][e] + wsum[1][e]) + wsum[2][e]) + wsum[3][e];
+    part_load[(int64_t)blk * E + e] = cnt[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void router_stats_reduce_kernel(const float* __restrict__ part_p,
+                                                                  const int32_t* __restrict__ part_load, int nblk,
+                                                                  int E, int T, float* __restrict__ mean_prob,
+                                                                  int32_t* __restrict__ load) {
+  const int e = blockIdx.x * 256 + (int)threadIdx.x;
+  if (e >= E) return;
+  float sp = 0.0f;
+  int sl = 0;
+  int b = 0;
+  for (; b + 8 <= nblk; b += 8) {  // eight independent loads at a time, added in block order
+    float vp[8];
+    int vl[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      vp[u] = part_p[(int64_t)(b + u) * E + e];
+      vl[u] = part_load[(int64_t)(b + u) * E + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sp += vp[u];
+      sl += vl[u];
+    }
+  }
+  for (; b < nblk; ++b) {
+    sp += part_p[(int64_t)b * E + e];
+    sl += part_load[(int64_t)b * E + e];
+  }
+  mean_prob[e] = sp / (float)T;
+  load[e] = sl;
+}
+
+hipError_t launch_router_stats(const float* logits, const int32_t* topk_idx, int T, int E, int k, float* probs,
+                               float* mean_prob, int32_t* load, void* workspace, hipStream_t s) {
+  const int nblk = (T + kStatsTok - 1) / kStatsTok;
+  float* part_p = (float*)workspace;
+  int32_t* part_load = (int32_t*)(part_p + (int64_t)nblk * E);
+  const int vpl = (E + kWave - 1) / kWave;
+  dim3 grid(nblk), block(kStatsWaves * kWave);
+#define MOE_STATS_CASE(V)                                                                                     \
+  case V:                                                                                                    \
+    hipLaunchKernelGGL(router_stats_kernel<V>, grid, block, 0, s, logits, topk_idx, T, E, k, probs, part_p, \
+                       part_load);                                                                           \
+    break;
+  switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : 16) {
+    MOE_STATS_CASE(1)
+    MOE_STATS_CASE(2)
+    MOE_STATS_CASE(4)
+    MOE_STATS_CASE(8)
+    MOE_STATS_CASE(16)
+  }
+#undef MOE_STATS_CASE
+  hipLaunchKernelGGL(router_stats_reduce_kernel, dim3((E + 255) / 256), dim3(256), 0, s, part_p, part_load, nblk, E, T,
+                     mean_prob, load);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
 template <typename TIn, int EQ>
 static void launch_logits_t(const void* x, const void* w_gate, int T, int H, int E, float* logits, hipStream_t s) {
   constexpr int EB = kLogitWaves * EQ;

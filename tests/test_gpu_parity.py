@@ -55,6 +55,30 @@ def test_router_topk(T, E, k, renorm):
     assert rel_err(host(w), rw) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1000, 128, 8), (77, 256, 8), (50, 1024, 32), (10, 5, 5),
+                                   (4096, 128, 8), (300, 100, 7)])
+def test_router_stats(T, E, k):
+    g = generator((963, T, E, k))
+    logits = (g.standard_normal((T, E)) * 2).astype(np.float32)
+    idx = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if T >= 10:
+        idx[3, 0] = -1          # a dropped slot and an out-of-range index are not counted
+        idx[5, k - 1] = E
+    probs, mean, load = moe.moe_router_stats(dev(logits), dev(idx))
+    rp, rm, rl = oracle.router_stats(logits, idx)
+    assert rel_err(host(probs), rp) <= TOL["f32"]
+    assert rel_err(host(mean), rm) <= TOL["f32"]
+    assert np.array_equal(host(load), rl)
+    _, mean2, _ = moe.moe_router_stats(dev(logits), dev(idx), want_probs=False)
+    assert np.array_equal(host(mean).view(np.uint32), host(mean2).view(np.uint32))   # deterministic
+
+
+def test_router_stats_no_tokens():
+    _, mean, load = moe.moe_router_stats(torch.zeros((0, 16), device="cuda"),
+                                         torch.zeros((0, 4), dtype=torch.int32, device="cuda"))
+    assert torch.all(mean == 0) and torch.all(load == 0)
+
+
 # ---- permute ----------------------------------------------------------------------------------
 @pytest.mark.parametrize("T,H,E,k,dtype,skew", [
     (64, 64, 8, 2, "f32", None), (1000, 136, 16, 4, "bf16", None), (257, 2048, 128, 8, "bf16", None),
