@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
+    ap.add_argument("--chunks", type=int, default=1,
+                    help="forward only: split the tokens in N chunks and route chunk c+1 on a side stream while "
+                         "chunk c's experts run (Domino-style overlap); the step time is the chunked one")
     ap.add_argument("--no-gather", action="store_true",
                     help="forward: copy the rows to x_perm in the permute instead of gathering them in GEMM-1")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -224,6 +227,28 @@ def main():
         total_ev += evs[0].elapsed_time(evs[ns])
     seg /= args.steps
     ms_per_step = max(wall * 1e3 / args.steps, total_ev / args.steps)
+    unchunked_ms = ms_per_step
+    if args.chunks > 1:
+        # the timed step is the chunked, two-stream forward; the per-kernel figures above (and the
+        # roofline of the dominant kernel) come from the one-shot stages
+        if wl.backward or sh is not None:
+            print("bench.py: --chunks applies to forward-only workloads without a shared expert", file=sys.stderr)
+            sys.exit(2)
+        cf = moe.ChunkedForward(T, H, I, E, k, tdt, x.device, chunks=args.chunks, logits=given_logits is None,
+                                gather=gather)
+        run = lambda: cf(x, gate_up, down, w_gate=w_gate, logits=given_logits)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = max(wall * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps)
     tokens_per_s = T / (ms_per_step / 1e3)
     t_of = {n: seg[i] * 1e-3 for i, n in enumerate(names)}
 
@@ -264,6 +289,8 @@ def main():
         "combine_hbm_gbs": round(comb_bytes / t_of["combine"] / 1e9, 1),
         "active_experts": n_active,
     }
+    if args.chunks > 1:
+        perf["one_shot_ms_per_step"] = round(unchunked_ms, 4)
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -272,7 +299,7 @@ def main():
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "k": k, "renorm": True,
                    "router": "logits given" if given_logits is not None else "x @ W_g",
                    "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward",
-                   "gemm1_rows": "gathered from x" if gather else "x_perm"},
+                   "gemm1_rows": "gathered from x" if gather else "x_perm", "chunks": args.chunks},
         "roofline": roof, "perf": perf,
     }
     if args.cpu_seconds > 0:

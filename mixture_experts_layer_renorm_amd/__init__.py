@@ -453,6 +453,51 @@ def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True
     return bufs.out, bufs
 
 
+class ChunkedForward:
+    """Domino-style forward on one GPU: the tokens are split into `chunks` contiguous chunks; the
+    routing of each chunk (router logits, top-k, permute plan: the stand-in for its dispatch) runs
+    on a side stream, and chunk c's grouped FFN and combine run on the calling stream as soon as
+    chunk c is routed, so the routing of chunk c+1 overlaps chunk c's expert matmuls. An event per
+    chunk orders the two streams. Every chunk has its own buffers, allocated here once; the output
+    rows of chunk c are written straight into out[rows of c]. Per token the result is bit-identical
+    to moe_layer_forward (routing and the FFN rows do not depend on the other tokens).
+    overlap=False issues the same calls on one stream (for comparison)."""
+
+    def __init__(self, T, H, I, E, k, dtype, device, chunks=2, logits=True, gather=True):
+        if chunks < 1 or chunks > T:
+            raise ValueError(f"ChunkedForward: chunks={chunks} must be in [1, T={T}]")
+        self.T, self.H, self.E, self.k, self.gather = T, H, E, k, gather
+        self.bounds = [T * c // chunks for c in range(chunks + 1)]
+        self.bufs = [LayerBuffers(self.bounds[c + 1] - self.bounds[c], H, I, E, k, dtype, device, logits=logits,
+                                  x_perm=not gather) for c in range(chunks)]
+        self.side = torch.cuda.Stream(device=device)          # default priority
+        self.routed = [torch.cuda.Event() for _ in range(chunks)]
+        self.out = torch.empty((T, H), dtype=dtype, device=device)
+
+    def __call__(self, x, gate_up, down, w_gate=None, logits=None, renorm=True, overlap=True, stream=None):
+        main = torch.cuda.current_stream() if stream is None else stream
+        side = self.side if overlap else main
+        if overlap:
+            side.wait_stream(main)   # x ready, and the previous call's chunks done with their buffers
+        k, E = self.k, self.E
+        for c, b in enumerate(self.bufs):
+            t0, t1 = self.bounds[c], self.bounds[c + 1]
+            xc = x[t0:t1]
+            lg = logits[t0:t1] if logits is not None else moe_router_logits(xc, w_gate, b.logits, side)
+            moe_router_topk(lg, k, renorm, b.topk_idx, b.topk_w, side)
+            moe_permute(xc, b.topk_idx, E, b.x_perm, b.plan, b.workspace, side, rows=not self.gather)
+            if overlap:
+                self.routed[c].record(side)
+                main.wait_event(self.routed[c])
+            if self.gather:
+                moe_grouped_swiglu_ffn_gather(xc, b.plan.slot_of_row, k, gate_up, down, b.plan.offsets, None, b.h,
+                                              b.y, None, main)
+            else:
+                moe_grouped_swiglu_ffn(b.x_perm, gate_up, down, b.plan.offsets, b.h, b.y, None, main)
+            moe_unpermute_combine(b.y, b.plan.row_of_slot, b.topk_w, None, self.out[t0:t1], main)
+        return self.out
+
+
 class LayerGrads:
     """Gradient buffers of one layer backward (allocated once, reused)."""
 
