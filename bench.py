@@ -95,6 +95,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
+    ap.add_argument("--ffn-groups", type=int, default=0,
+                    help="forward only: the routed FFN as this many expert groups on their own streams in the timed "
+                         "step (1 = one stream; 0 = 2 when experts average at most 320 rows, where one launch's "
+                         "tile list is about 3 waves and its tail matters, else 1); per-kernel figures come from a "
+                         "one-stream pass")
     ap.add_argument("--chunks", type=int, default=1,
                     help="forward only: split the tokens in N chunks and route chunk c+1 on a side stream while "
                          "chunk c's experts run (Domino-style overlap); the step time is the chunked one")
@@ -227,6 +232,47 @@ def main():
         total_ev += evs[0].elapsed_time(evs[ns])
     seg /= args.steps
     ms_per_step = max(wall * 1e3 / args.steps, total_ev / args.steps)
+    one_stream_ms = ms_per_step
+    step_us = None
+    ffn_groups = args.ffn_groups if args.ffn_groups > 0 else (2 if N <= 320 * E else 1)
+    if wl.backward or sh is not None:
+        ffn_groups = 1
+    if ffn_groups > 1 and args.chunks == 1:
+        # the timed step: the same stages, with the routed FFN as expert groups on their own streams
+        fgs = moe.ExpertGroupsFfn(ffn_groups, device=x.device)
+        ffn = lambda: fgs(gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, x_perm=bufs.x_perm,
+                          x=x if gather else None, slot_of_row=bufs.plan.slot_of_row, k=k)
+        st2 = [(n, f) for n, f in stages if n not in ("gemm_gate_up", "gemm_down")]
+        pos = [n for n, _ in stages].index("gemm_gate_up")
+        st2.insert(pos, ("ffn_expert_groups", ffn))
+        n2 = len(st2)
+
+        def step2(evs=None):
+            for i, (_, fn) in enumerate(st2):
+                if evs is not None:
+                    evs[i].record(stream)
+                fn()
+            if evs is not None:
+                evs[n2].record(stream)
+
+        for _ in range(args.warmup):
+            step2()
+        torch.cuda.synchronize()
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(n2 + 1)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            step2(ev2[s_])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        seg2 = np.zeros(n2)
+        tot2 = 0.0
+        for evs in ev2:
+            for i in range(n2):
+                seg2[i] += evs[i].elapsed_time(evs[i + 1])
+            tot2 += evs[0].elapsed_time(evs[n2])
+        seg2 /= args.steps
+        ms_per_step = max(wall * 1e3 / args.steps, tot2 / args.steps)
+        step_us = {n: round(seg2[i] * 1e3, 2) for i, (n, _) in enumerate(st2)}
     unchunked_ms = ms_per_step
     if args.chunks > 1:
         # the timed step is the chunked, two-stream forward; the per-kernel figures above (and the
@@ -291,6 +337,9 @@ def main():
     }
     if args.chunks > 1:
         perf["one_shot_ms_per_step"] = round(unchunked_ms, 4)
+    if step_us is not None:
+        perf["timed_step_us"] = step_us
+        perf["one_stream_ms_per_step"] = round(one_stream_ms, 4)
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -299,7 +348,8 @@ def main():
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "k": k, "renorm": True,
                    "router": "logits given" if given_logits is not None else "x @ W_g",
                    "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward",
-                   "gemm1_rows": "gathered from x" if gather else "x_perm", "chunks": args.chunks},
+                   "gemm1_rows": "gathered from x" if gather else "x_perm", "chunks": args.chunks,
+                   "ffn_expert_groups": ffn_groups if args.chunks == 1 else 1},
         "roofline": roof, "perf": perf,
     }
     if args.cpu_seconds > 0:

@@ -418,12 +418,15 @@ class LayerBuffers:
 
 
 def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True, residual=None, bufs=None,
-                      shared_gate_up=None, shared_down=None, save_for_backward=False, stream=None, gather=False):
+                      shared_gate_up=None, shared_down=None, save_for_backward=False, stream=None, gather=False,
+                      ffn_groups=None):
     """Router (logits unless given) -> top-k -> permute -> grouped SwiGLU FFN -> combine.
     With shared_gate_up / shared_down, the shared expert runs on every token as a one-segment grouped
     FFN and its output is the combine's residual (a separate residual is then not accepted).
     gather=True: the permute computes the plan only and the first grouped matmul gathers its rows
-    from x (same result, bit for bit; x_perm is never written, so there is no backward from it)."""
+    from x (same result, bit for bit; x_perm is never written, so there is no backward from it).
+    ffn_groups: an ExpertGroupsFfn; the routed FFN then runs as expert groups on its streams (same
+    result, bit for bit)."""
     T, H = x.shape
     E = gate_up.shape[0] // H
     I = gate_up.shape[1] // 2
@@ -440,10 +443,15 @@ def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True
     moe_router_topk(logits, k, renorm, bufs.topk_idx, bufs.topk_w, stream)
     if gather:
         moe_permute(x, bufs.topk_idx, E, None, bufs.plan, bufs.workspace, stream, rows=False)
+    else:
+        moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace, stream)
+    if ffn_groups is not None:
+        ffn_groups(gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, x_perm=bufs.x_perm, x=x if gather else None,
+                   slot_of_row=bufs.plan.slot_of_row, k=k, gu_saved=bufs.gu_saved, stream=stream)
+    elif gather:
         moe_grouped_swiglu_ffn_gather(x, bufs.plan.slot_of_row, k, gate_up, down, bufs.plan.offsets, None, bufs.h,
                                       bufs.y, bufs.gu_saved, stream)
     else:
-        moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace, stream)
         moe_grouped_swiglu_ffn(bufs.x_perm, gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, bufs.gu_saved, stream)
     if I_sh:
         sh = bufs.shared
@@ -451,6 +459,51 @@ def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True
         residual = sh["y"]
     moe_unpermute_combine(bufs.y, bufs.plan.row_of_slot, bufs.topk_w, residual, bufs.out, stream)
     return bufs.out, bufs
+
+
+class ExpertGroupsFfn:
+    """The grouped SwiGLU FFN as G groups of consecutive experts on G streams (default priority):
+    group i runs its gate_up matmul then its down matmul on stream i, each group starting after the
+    work already queued on the calling stream, and the calling stream waits for all of them. One
+    launch leaves the tail of its tile list to a few CUs; here the other groups' tiles (and group i's
+    down matmul as soon as its gate_up is done) fill it. The groups are plain sub-ranges of the
+    experts (weights and offsets sliced, rows addressed absolutely), so the result is bit-identical
+    to the one-stream FFN."""
+
+    def __init__(self, groups=2, device=None):
+        if groups < 1:
+            raise ValueError("ExpertGroupsFfn: groups must be >= 1")
+        self.groups = groups
+        self.streams = [torch.cuda.Stream(device=device) for _ in range(groups)]
+        self.done = [torch.cuda.Event() for _ in range(groups)]
+
+    def __call__(self, gate_up, down, expert_offsets, h, y, x_perm=None, x=None, slot_of_row=None, k=None,
+                 gu_saved=None, stream=None):
+        """Rows from x_perm, or gathered from x through slot_of_row (row r = token slot_of_row[r] // k)."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        E = expert_offsets.shape[0] - 1
+        H = gate_up.shape[0] // E
+        I = gate_up.shape[1] // 2
+        N = h.shape[0]
+        bounds = [E * i // self.groups for i in range(self.groups + 1)]
+        for s in self.streams:
+            s.wait_stream(main)
+        for i, s in enumerate(self.streams):   # all gate_up launches first, so that they start together
+            e0, e1 = bounds[i], bounds[i + 1]
+            if e1 == e0:
+                continue
+            gu_i, off_i = gate_up[e0 * H:e1 * H], expert_offsets[e0:e1 + 1]
+            if x_perm is None:
+                moe_grouped_gemm_swiglu_gather(x, slot_of_row, k, gu_i, off_i, N, h, gu_saved, s)
+            else:
+                moe_grouped_gemm_swiglu(x_perm, gu_i, off_i, h, gu_saved, s)
+        for i, s in enumerate(self.streams):
+            e0, e1 = bounds[i], bounds[i + 1]
+            if e1 > e0:
+                moe_grouped_gemm_down(h, down[e0 * I:e1 * I], expert_offsets[e0:e1 + 1], y, s)
+            self.done[i].record(s)
+            main.wait_event(self.done[i])
+        return y, h
 
 
 class ChunkedForward:

@@ -1,7 +1,8 @@
-"""GPU parity of the Domino-style chunked forward: the routing of chunk c+1 runs on a side stream
-while chunk c's grouped FFN runs on the main stream. Per token the output must equal, bit for bit,
-the one-shot layer forward (and hence the oracle within tolerance), on every call of a reused
-schedule, with or without the overlap. Inputs are seeded and synthetic."""
+"""GPU parity of the multi-stream schedules. The Domino-style chunked forward routes chunk c+1 on a
+side stream while chunk c's grouped FFN runs on the main stream; the expert-group FFN runs groups of
+experts on their own streams. Per token the output must equal, bit for bit, the one-shot layer
+forward (and hence the oracle within tolerance), on every call of a reused schedule. Inputs are
+seeded and synthetic."""
 import numpy as np
 import pytest
 import torch
@@ -44,5 +45,21 @@ def test_chunked_forward_given_logits():
     ref = ref.clone()
     cf = moe.ChunkedForward(T, H, I, E, k, x.dtype, x.device, chunks=2, logits=False)
     out = cf(x, gu, dn, logits=lg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,groups,gather", [
+    (1000, 256, 128, 16, 4, 2, True), (1000, 256, 128, 16, 4, 3, False), (300, 136, 40, 5, 2, 5, True),
+    (513, 2048, 768, 128, 8, 2, True)])
+def test_expert_groups_ffn_equals_one_stream(T, H, I, E, k, groups, gather):
+    d = make_layer_inputs(T, H, I, E, k, "bf16", (982, T, E), w_std=0.08, wg_std=0.3)
+    x, gu, dn, wg = dev(d["x"]), dev(d["gate_up"]), dev(d["down"]), dev(d["w_gate"])
+    ref, _ = moe.moe_layer_forward(x, gu, dn, k, w_gate=wg, gather=gather)
+    ref = ref.clone()
+    fg = moe.ExpertGroupsFfn(groups, device=x.device)
+    bufs = None
+    for _ in range(3):
+        out, bufs = moe.moe_layer_forward(x, gu, dn, k, w_gate=wg, gather=gather, ffn_groups=fg, bufs=bufs)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
