@@ -65,6 +65,74 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// acc[q] = fma(w[h][q], x[h], acc[q]) for h = 0..3 in order, q = 0..EQ-1: register w[r] holds, in
+// lane j of every 16-lane row, the weight of h = r * (16 / EQ) + j / EQ and expert j % EQ, and
+// v_fmac_f32_dpp with row_newbcast:j hands lane j's value of its row to all 16 lanes. (The fused
+// multiply-add is the same IEEE operation as fmaf; only the operand's lane changes.) The leading
+// s_nop covers the wait states a DPP read needs after a vector-ALU write of its source.
+template <int EQ>
+__device__ __forceinline__ void fmac4(float* acc, const float* w, const float4& x);
+template <>
+__device__ __forceinline__ void fmac4<4>(float* acc, const float* w, const float4& x) {
+  asm("s_nop 1\n\t"
+               "v_fmac_f32_dpp %[a0], %[w0], %[x0] row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w0], %[x0] row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w0], %[x0] row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w0], %[x0] row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a0], %[w0], %[x1] row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w0], %[x1] row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w0], %[x1] row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w0], %[x1] row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a0], %[w0], %[x2] row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w0], %[x2] row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w0], %[x2] row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w0], %[x2] row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a0], %[w0], %[x3] row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w0], %[x3] row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w0], %[x3] row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w0], %[x3] row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+               : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3])
+               : [w0] "v"(w[0]), [x0] "v"(x.x), [x1] "v"(x.y), [x2] "v"(x.z), [x3] "v"(x.w));
+}
+template <>
+__device__ __forceinline__ void fmac4<8>(float* acc, const float* w, const float4& x) {
+  asm("s_nop 1\n\t"
+               "v_fmac_f32_dpp %[a0], %[w0], %[x0] row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w0], %[x0] row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w0], %[x0] row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w0], %[x0] row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a4], %[w0], %[x0] row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a5], %[w0], %[x0] row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a6], %[w0], %[x0] row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a7], %[w0], %[x0] row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a0], %[w0], %[x1] row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w0], %[x1] row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w0], %[x1] row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w0], %[x1] row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a4], %[w0], %[x1] row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a5], %[w0], %[x1] row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a6], %[w0], %[x1] row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a7], %[w0], %[x1] row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a0], %[w1], %[x2] row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w1], %[x2] row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w1], %[x2] row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w1], %[x2] row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a4], %[w1], %[x2] row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a5], %[w1], %[x2] row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a6], %[w1], %[x2] row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a7], %[w1], %[x2] row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a0], %[w1], %[x3] row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a1], %[w1], %[x3] row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a2], %[w1], %[x3] row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a3], %[w1], %[x3] row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a4], %[w1], %[x3] row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a5], %[w1], %[x3] row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a6], %[w1], %[x3] row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+               "v_fmac_f32_dpp %[a7], %[w1], %[x3] row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+               : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3]), [a4] "+v"(acc[4]), [a5] "+v"(acc[5]), [a6] "+v"(acc[6]), [a7] "+v"(acc[7])
+               : [w0] "v"(w[0]), [w1] "v"(w[1]), [x0] "v"(x.x), [x1] "v"(x.y), [x2] "v"(x.z), [x3] "v"(x.w));
+}
+
 template <typename TIn, int EQ>
 struct LogitTile {
   static constexpr int EB = kLogitWaves * EQ;                     // experts per workgroup
@@ -172,41 +240,28 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
       acc[q + 3] = __builtin_fmaf(xe, wv.w, acc[q + 3]);
     }
   };
+  const int wrow = (lane & 15) / EQ, wcol = (lane & 15) % EQ;  // the lane's value in a W register
   auto compute = [&](int c) {
     const int buf = c & 1;
     const int nh = min(HB, H - c * HB);
     const float* xl = &xs[buf][lane][0];
     if (nh == HB) {
-      // groups of 8 h, software-pipelined: the LDS reads of group g+1 are issued before the
-      // arithmetic of group g
-      constexpr int G = P::G;
-      float4 xv[2][G / 4], wv[2][G][EQ / 4];
-      auto read = [&](int g0, float4* xg, float4 (*wgp)[EQ / 4]) {
+      // four h at a time: the lane's x for them (one 16-byte read) and the wave's weights for them
+      // (16 values per register, replicated over the four 16-lane rows), consumed by fmac with a
+      // row_newbcast operand; the reads of the next four h are issued before this group's fmacs
+      float4 xv[2];
+      float wv[2][EQ / 4];
+      auto rd = [&](int h4, int slot) {
+        xv[slot] = *reinterpret_cast<const float4*>(xl + h4);
 #pragma unroll
-        for (int j = 0; j < G / 4; ++j) xg[j] = *reinterpret_cast<const float4*>(xl + g0 + 4 * j);
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-          for (int q = 0; q < EQ; q += 4)
-            wgp[hh][q / 4] = *reinterpret_cast<const float4*>(&ws[buf][g0 + hh][wave * EQ + q]);
+        for (int r = 0; r < EQ / 4; ++r) wv[slot][r] = ws[buf][h4 + r * (16 / EQ) + wrow][wave * EQ + wcol];
       };
-      read(0, xv[0], wv[0]);
+      rd(0, 0);
 #pragma unroll
-      for (int gi = 0; gi < HB / G; ++gi) {
-        const int cb = gi & 1;
-        if (gi + 1 < HB / G) read((gi + 1) * G, xv[cb ^ 1], wv[cb ^ 1]);
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float4 x4 = xv[cb][hh / 4];
-          const float xe = (hh & 3) == 0 ? x4.x : (hh & 3) == 1 ? x4.y : (hh & 3) == 2 ? x4.z : x4.w;
-#pragma unroll
-          for (int q = 0; q < EQ; q += 4) {
-            acc[q + 0] = __builtin_fmaf(xe, wv[cb][hh][q / 4].x, acc[q + 0]);
-            acc[q + 1] = __builtin_fmaf(xe, wv[cb][hh][q / 4].y, acc[q + 1]);
-            acc[q + 2] = __builtin_fmaf(xe, wv[cb][hh][q / 4].z, acc[q + 2]);
-            acc[q + 3] = __builtin_fmaf(xe, wv[cb][hh][q / 4].w, acc[q + 3]);
-          }
-        }
+      for (int h4 = 0; h4 < HB; h4 += 4) {
+        const int cs = (h4 / 4) & 1;
+        if (h4 + 4 < HB) rd(h4 + 4, cs ^ 1);
+        fmac4<EQ>(acc, wv[cs], xv[cs]);
       }
     } else {
       for (int hh = 0; hh < nh; ++hh) fma_h(buf, hh, xl[hh]);
