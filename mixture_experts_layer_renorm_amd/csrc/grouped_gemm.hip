@@ -840,7 +840,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmA
             const u32x4 v = *reinterpret_cast<const u32x4*>((r < 32 ? sA3 : sB3) + (r & 31) * 512 + ((c ^ (r & 31)) << 4));
             const int m = w.m0 + qb * 64 + r, col = w.n0 + c * 8;
             const int off = (m < g.M && col < g.N) ? (m * g.ldc + col) * 2 : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 2);  // nt: gradients are not re-read
           }
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
