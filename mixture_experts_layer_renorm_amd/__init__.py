@@ -145,6 +145,10 @@ class Plan:
         self.counts, self.offsets, self.row_of_slot, self.slot_of_row = counts, offsets, row_of_slot, slot_of_row
 
 
+def moe_router_stats_workspace_bytes(T, E):
+    return int(load_library().moe_router_stats_workspace_bytes(T, E))
+
+
 def moe_router_stats(logits, topk_idx, want_probs=True, probs=None, mean_prob=None, load=None, workspace=None,
                      stream=None):
     """Full softmax per token (optional), its mean over tokens and the per-expert load, for an
@@ -161,7 +165,7 @@ def moe_router_stats(logits, topk_idx, want_probs=True, probs=None, mean_prob=No
         mean_prob = torch.empty(E, dtype=torch.float32, device=dev)
     if load is None:
         load = torch.empty(E, dtype=torch.int32, device=dev)
-    ws = int(load_library().moe_router_stats_workspace_bytes(T, E))
+    ws = moe_router_stats_workspace_bytes(T, E)
     if workspace is None:
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
     _check(load_library().moe_router_stats(_ptr(logits), _ptr(topk_idx), T, E, k, _ptr(probs), _ptr(mean_prob),

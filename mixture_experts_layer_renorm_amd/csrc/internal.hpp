@@ -21,7 +21,7 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int reno
                               hipStream_t s);
 
 // permute.hip
-constexpr int kPermuteChunk = 256;  // tokens per plan chunk
+constexpr int kPermuteChunk = 64;   // tokens per plan chunk (64 measured faster than 128 or 256)
 inline int permute_nchunks(int T) { return (T + kPermuteChunk - 1) / kPermuteChunk; }
 inline size_t permute_workspace_bytes(int T, int E) { return (size_t)permute_nchunks(T) * (size_t)E * sizeof(int32_t); }
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);

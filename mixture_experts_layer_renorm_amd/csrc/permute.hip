@@ -5,7 +5,7 @@
 // tokens stay in ascending order; per-expert counts come from summing the routing mask.
 //
 // Three kernels, no host synchronisation and no atomics that decide an order:
-//  1. count : per chunk of 256 tokens, an LDS histogram of the chunk's expert choices.
+//  1. count : per chunk of kPermuteChunk tokens, an LDS histogram of the chunk's expert choices.
 //  2. plan  : per chunk, global bases = exclusive scan over experts of the totals + the counts of
 //             earlier chunks; in-chunk ranks from per-expert token bitmaps (popcount of the
 //             tokens before this one). Writes counts, offsets, row_of_slot, slot_of_row.
