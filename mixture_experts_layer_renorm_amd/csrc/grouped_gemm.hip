@@ -630,36 +630,66 @@ __device__ __forceinline__ void dma_16(const i32x4& rsrc, int voff, uint32_t lds
                : "memory", "m0");
 }
 
+constexpr int kResSteps = 5;             // K steps of a P slice kept in LDS
+constexpr int kResK = kResSteps * kBK;   // experts with up to this many rows use the resident kernel
+
+// Loads the expert offsets into s_off, sets s_pref[e] to the exclusive prefix over experts of
+// units(K_e) (units of work the calling kernel does for expert e) and returns the total.
+template <typename F>
+__device__ int wgrad_units(const GemmArgs& g, int* s_off, int* s_pref, int* s_wtot, F units) {
+  for (int i = threadIdx.x; i <= g.E; i += kGemmThreads) s_off[i] = g.offsets[i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < g.E; e += kGemmThreads) s_pref[e] = units(max(0, s_off[e + 1] - s_off[e]));
+  __syncthreads();
+  block_exclusive_scan<kGemmThreads>(s_pref, g.E, s_wtot);
+  return __builtin_amdgcn_readfirstlane(s_pref[g.E]);
+}
+// the expert whose units contain unit u (s_pref[e] <= u < s_pref[e + 1]; experts with no units skipped)
+__device__ __forceinline__ int unit_expert(const int* s_pref, int E, int u) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= u)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return __builtin_amdgcn_readfirstlane(lo);
+}
+
 struct WgTile {
   const uint16_t* a;  // P rows of the expert, from its first row
   const uint16_t* b;  // Q rows of the expert
   int e, m0, n0, K, KT4;
 };
 
-__global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmArgs g, int total) {
+__global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA], sA1[kTileA], sA2[kTileA], sA3[kTileA];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
   __shared__ int s_off[kMaxExperts + 1];  // expert offsets, read once (LDS reads do not touch vmcnt)
+  __shared__ int s_pref[kMaxExperts + 1];
+  __shared__ int s_wtot[kGemmThreads / kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = (wave >> 1) & 3, wn = wave & 1;
   const int b = blockIdx.x;
+  // this kernel takes the experts with more than kResK rows (the others keep their P slice in LDS,
+  // grouped_wgrad_res_kernel); tiles are numbered over those experts only
+  const int per_e = g.ntiles_m * g.ntiles_n;
+  const int total = wgrad_units(g, s_off, s_pref, s_wtot, [&](int K) { return K > kResK ? per_e : 0; });
   const int Q = (total + 7) >> 3;
   const int t_end = min(((b & 7) + 1) * Q, total);
   const int stride = gridDim.x >> 3;
   const int t0 = (b & 7) * Q + (b >> 3);
   if (t0 >= t_end) return;
-  for (int i = tid; i <= g.E; i += kGemmThreads) s_off[i] = g.offsets[i];
-  __syncthreads();
 
   // tile tt -> expert, output origin, K rows and operand rows. A tile past the end has K = 0.
   auto setup = [&](int tt, WgTile& w) {
     const bool real = tt < t_end;
-    const int per_e = g.ntiles_m * g.ntiles_n;
-    const int e = real ? tt / per_e : 0;
-    const int rem = tt - e * per_e;
+    const int e = real ? unit_expert(s_pref, g.E, tt) : 0;
+    const int rem = real ? tt - s_pref[e] : 0;
     const int mt = rem / g.ntiles_n;
     w.e = e;
     w.m0 = mt * kBM;
@@ -878,6 +908,224 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmA
 }
 
 // ---------------------------------------------------------------------------------------------
+// Weight gradients of experts with at most kResK rows, P slice resident. A unit of work is (expert
+// e, 256-row block mt of dW_e): its P slice (K x 256, at most kResSteps K steps) is loaded into LDS
+// once, and the workgroup then computes all ntiles_n column tiles of that block, streaming only
+// Q (K x 256 per tile) through a 4-slot ring; per K step that is 16 KB of global -> LDS traffic
+// instead of 32. The Q steps of the unit form one sequence (tile nt, step kt -> nt * KT + kt),
+// prefetched three steps ahead across tile boundaries, except that a tile's last step prefetches
+// only two ahead: the epilogue then has two free ring slots (the step just read and the one not yet
+// loaded) for staging 64 output rows at a time, and the next tile's first step issues two steps
+// to catch up. Roles as in grouped_wgrad_kernel: waves 0-3 issue the DMAs, waves 4-7 the stores.
+__global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_res_kernel(const GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sR0[kTileA], sR1[kTileA], sR2[kTileA], sR3[kTileA], sR4[kTileA];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_pref[kMaxExperts + 1];
+  __shared__ int s_wtot[kGemmThreads / kWave];
+  static_assert(kResSteps == 5, "five resident slots");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = (wave >> 1) & 3, wn = wave & 1;
+  const int b = blockIdx.x;
+  const int total = wgrad_units(g, s_off, s_pref, s_wtot, [&](int K) { return K <= kResK ? g.ntiles_m : 0; });
+  const int Q = (total + 7) >> 3;
+  const int u_end = min(((b & 7) + 1) * Q, total);
+  const int stride = gridDim.x >> 3;
+  const int u0 = (b & 7) * Q + (b >> 3);
+  if (u0 >= u_end) return;
+
+  auto rslot = [&](int kt) -> uint8_t* { return kt == 0 ? sR0 : kt == 1 ? sR1 : kt == 2 ? sR2 : kt == 3 ? sR3 : sR4; };
+  auto bslot = [&](int s4) -> uint8_t* { return s4 == 0 ? sB0 : s4 == 1 ? sB1 : s4 == 2 ? sB2 : sB3; };
+
+  const int q = lane >> 4, sl = lane & 15;
+  auto krow_rd = [&](int col32, int kk, int ri) {
+    const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
+    const int col = col32 + (q & 1) * 16 + 4 * (sl & 3);
+    return kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+  };
+  int a_rd[2][2][2], b_rd[2][4][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int ri = 0; ri < 2; ++ri) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) a_rd[kk][mb][ri] = krow_rd(wm * 64 + mb * 32, kk, ri);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) b_rd[kk][nb][ri] = krow_rd(wn * 128 + nb * 32, kk, ri);
+    }
+  auto frag = [&](const uint8_t* base, const int* rd) -> bf16x8 {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[1]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  f32x16 acc[2][4];
+
+  auto walk = [&](auto loader_tag) {
+    constexpr bool LOADER = decltype(loader_tag)::value;
+    const int lw = wave & (kWgLoaders - 1);
+    int a_lane[kWgDmaA], b_lane[kWgDmaB];
+#pragma unroll
+    for (int i = 0; i < kWgDmaA; ++i) {
+      const int kr = (lw * kWgDmaA + i) * 2 + (lane >> 5);
+      a_lane[i] = kr * g.lda * 2 + (((lane & 31) ^ swz_b(kr)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kWgDmaB; ++i) {
+      const int kr = (lw * kWgDmaB + i) * 2 + (lane >> 5);
+      b_lane[i] = kr * g.ldb * 2 + (((lane & 31) ^ swz_b(kr)) * 16);
+    }
+    // the unit being computed
+    int e = 0, m0 = 0, K = 0, KT = 0, G = 0;
+    const uint16_t* pa = g.A;
+    const uint16_t* pb = g.B;
+    // P step kt into its resident slot; Q step j of the unit's sequence into ring slot j % 4
+    // (descriptors from the step's first k-row to the expert's last row: rows past K read zero)
+    auto dma_a = [&](int kt) {
+      if constexpr (LOADER) {
+        const int k0 = kt * kBK;
+        const i32x4 rs = buffer_rsrc(pa + (int64_t)k0 * g.lda, max(0, K - k0) * g.lda * 2);
+        const uint32_t d = lds_addr(rslot(kt)) + lw * kWgDmaA * 1024;
+#pragma unroll
+        for (int i = 0; i < kWgDmaA; ++i) dma_16(rs, a_lane[i] + m0 * 2, d + i * 1024);
+      }
+    };
+    auto dma_b = [&](int j) {
+      if constexpr (LOADER) {
+        const int nt = j / KT, k0 = (j - nt * KT) * kBK;
+        const i32x4 rs = buffer_rsrc(pb + (int64_t)k0 * g.ldb, max(0, K - k0) * g.ldb * 2);
+        const uint32_t d = lds_addr(bslot(j & 3)) + lw * kWgDmaB * 1024;
+#pragma unroll
+        for (int i = 0; i < kWgDmaB; ++i) dma_16(rs, b_lane[i] + nt * kBN * 2, d + i * 1024);
+      }
+    };
+    // loaders wait until at most n Q steps (n = 0, 1, 2) issued after the one needed are pending
+    auto meet = [&](int n) {
+      if constexpr (LOADER) {
+        if (n >= 2)
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kWgDmaB) : "memory");
+        else if (n == 1)
+          asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWgDmaB) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      } else {
+        asm volatile("s_barrier" ::: "memory");
+      }
+    };
+    // epilogue of tile nt into staging slots st0 (rows 0-31 of a 64-row quarter), st1 (32-63)
+    auto store = [&](int nt, uint8_t* st0, uint8_t* st1) {
+      int z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      const int lr = (lane & 31) + z;
+      const int wr_lo = lr * 512 + (lane >> 5) * 8;
+      const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(g.C + (int64_t)e * g.c_expert), (short)0, g.M * g.N * 2, kBufferWord3);
+      if constexpr (!LOADER) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      uint2 pk[2][4][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            pk[mb][nb][gq] = make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                                        pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
+      const int n0 = nt * kBN;
+#pragma unroll 1
+      for (int qb = 0; qb < 4; ++qb) {
+        if (wm == qb) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            uint8_t* rowp = (mb == 0 ? st0 : st1) + wr_lo;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int chunk = (wn * 16 + nb * 4 + gq) ^ lr;
+                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = pk[mb][nb][gq];
+              }
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if constexpr (!LOADER) {
+#pragma unroll
+          for (int j = 0; j < kWgRowsPerStore; ++j) {
+            const int r = ((wave - kWgLoaders) * kWgRowsPerStore + j) * 2 + (lane >> 5) + z;
+            const int c = lane & 31;
+            const u32x4 v = *reinterpret_cast<const u32x4*>((r < 32 ? st0 : st1) + (r & 31) * 512 + ((c ^ (r & 31)) << 4));
+            const int m = m0 + qb * 64 + r, col = n0 + c * 8;
+            const int off = (m < g.M && col < g.N) ? (m * g.ldc + col) * 2 : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 2);  // nt: gradients are not re-read
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    };
+
+    for (int u = u0; u < u_end; u += stride) {
+      e = unit_expert(s_pref, g.E, u);
+      const int mt = u - s_pref[e];
+      m0 = mt * kBM;
+      const int r0 = __builtin_amdgcn_readfirstlane(s_off[e]);
+      K = __builtin_amdgcn_readfirstlane(max(0, s_off[e + 1] - r0));
+      KT = (K + kBK - 1) / kBK;  // 0 .. kResSteps
+      G = g.ntiles_n * KT;
+      pa = g.A + (int64_t)r0 * g.lda;
+      pb = g.B + (int64_t)r0 * g.ldb;
+      // prologue: the resident P steps, then the first Q steps; wait for all of P and Q step 0
+      for (int kt = 0; kt < KT; ++kt) dma_a(kt);
+      int issued = min(3, G);
+      for (int j = 0; j < issued; ++j) dma_b(j);
+      meet(issued - 1);
+      int s = 0;  // Q step being computed
+      for (int nt = 0; nt < g.ntiles_n; ++nt) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
+        for (int kt = 0; kt < KT; ++kt, ++s) {
+          const uint8_t* sa = rslot(kt);
+          const uint8_t* sb = bslot(s & 3);
+          bf16x8 fa[2][2], fb[2][4];
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) fb[kk][nb] = frag(sb, b_rd[kk][nb]);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) fa[kk][mb] = frag(sa, a_rd[kk][mb]);
+          }
+          // prefetch: up to s + 3 (s + 2 on the tile's last step), never past the unit
+          const int target = min(G - 1, kt == KT - 1 ? s + 2 : s + 3);
+          for (; issued <= target; ++issued) dma_b(issued);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][nb], fa[kk][mb], acc[mb][nb], 0, 0, 0);
+          // step s + 1 must have landed: at most issued - (s + 2) later steps may stay pending
+          meet(issued - (s + 2));
+        }
+        // staging: the slot of the step just computed and the slot of step s + 2 (not yet loaded;
+        // its predecessor in the slot, step s - 2, is done). With no steps, every slot is free.
+        const int sl0 = KT > 0 ? (s - 1) & 3 : 0, sl1 = KT > 0 ? (s + 2) & 3 : 1;
+        store(nt, bslot(sl0), bslot(sl1));
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  if (wave < kWgLoaders)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
+}
+
+// ---------------------------------------------------------------------------------------------
 // fp32 path: one thread per output element, fp32 fused multiply-add over k ascending.
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E, int r) {
   int lo = 0, hi = E;  // find e with offsets[e] <= r < offsets[e+1]
@@ -1067,7 +1315,9 @@ hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E,
   g.ntiles_m = (M + kBM - 1) / kBM;
   g.ntiles_n = (Nq + kBN - 1) / kBN;
   const int64_t total = (int64_t)E * g.ntiles_m * g.ntiles_n;
-  // one workgroup per CU (each holds 128 KB of LDS and a full register file)
+  // one workgroup per CU (each holds most of the LDS and a full register file); the experts with
+  // at most kResK rows go to the resident kernel, the others to the streaming one (each kernel
+  // counts its own work on the device, and a workgroup without any exits at once)
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -1075,8 +1325,10 @@ hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E,
                                                  hipSuccess || cus <= 0)
       cus = 256;
   }
+  const int64_t grid_res = std::min<int64_t>(round_up8((int64_t)E * g.ntiles_m), (int64_t)round_up8(cus));
   const int64_t grid = std::min<int64_t>(round_up8(total), (int64_t)round_up8(cus));
-  hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g, (int)total);
+  hipLaunchKernelGGL(grouped_wgrad_res_kernel, dim3((unsigned)grid_res), dim3(kGemmThreads), 0, s, g);
+  hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
   return hipGetLastError();
 }
 
