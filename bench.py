@@ -103,6 +103,10 @@ def main():
     ap.add_argument("--chunks", type=int, default=1,
                     help="forward only: split the tokens in N chunks and route chunk c+1 on a side stream while "
                          "chunk c's experts run (Domino-style overlap); the step time is the chunked one")
+    ap.add_argument("--bwd-wgrad-cus", type=int, default=0,
+                    help="backward workloads: time the step with the backward on three streams and the weight "
+                         "gradients capped to this many CUs (0 = one stream); per-kernel figures come from a "
+                         "one-stream pass")
     ap.add_argument("--no-gather", action="store_true",
                     help="forward: copy the rows to x_perm in the permute instead of gathering them in GEMM-1")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -237,6 +241,7 @@ def main():
     ffn_groups = args.ffn_groups if args.ffn_groups > 0 else (2 if N <= 320 * E else 1)
     if wl.backward or sh is not None:
         ffn_groups = 1
+    st2 = None
     if ffn_groups > 1 and args.chunks == 1:
         # the timed step: the same stages, with the routed FFN as expert groups on their own streams
         fgs = moe.ExpertGroupsFfn(ffn_groups, device=x.device)
@@ -245,6 +250,15 @@ def main():
         st2 = [(n, f) for n, f in stages if n not in ("gemm_gate_up", "gemm_down")]
         pos = [n for n, _ in stages].index("gemm_gate_up")
         st2.insert(pos, ("ffn_expert_groups", ffn))
+    if wl.backward and args.bwd_wgrad_cus > 0:
+        # the timed step: the same forward, then the backward with its independent products on three
+        # streams (weight gradients capped to --bwd-wgrad-cus CUs)
+        ob = moe.OverlappedBackward(device=x.device, wgrad_cus=args.bwd_wgrad_cus)
+        bwd = lambda: ob(d_out, x, gate_up, down, bufs, w_gate=w_gate, logits=given_logits, renorm=True,
+                         shared_gate_up=sh_gu, shared_down=sh_dn, grads=grads)
+        bwd_names = ("combine_bwd", "ffn_bwd", "shared_ffn_bwd", "router_topk_bwd", "router_logits_bwd", "permute_bwd")
+        st2 = [(n, f) for n, f in stages if n not in bwd_names] + [("backward_overlapped", bwd)]
+    if st2 is not None:
         n2 = len(st2)
 
         def step2(evs=None):
@@ -349,7 +363,8 @@ def main():
                    "router": "logits given" if given_logits is not None else "x @ W_g",
                    "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward",
                    "gemm1_rows": "gathered from x" if gather else "x_perm", "chunks": args.chunks,
-                   "ffn_expert_groups": ffn_groups if args.chunks == 1 else 1},
+                   "ffn_expert_groups": ffn_groups if args.chunks == 1 else 1,
+                   "backward_wgrad_cus": args.bwd_wgrad_cus if wl.backward else None},
         "roofline": roof, "perf": perf,
     }
     if args.cpu_seconds > 0:

@@ -187,6 +187,24 @@ moe_status moe_grouped_swiglu_ffn_bwd(const void* d_y, const void* x_perm, const
                                       const int32_t* expert_offsets, void* d_x_perm, void* d_gate_up, void* d_down,
                                       void* d_gu, hipStream_t stream);
 
+/* ---- (7a-c) the products of (7) one at a time, for callers that put them on streams of their own ---
+ * moe_grouped_swiglu_ffn_bwd(...) == 7a, 7b, then 7c for (h, d_y) -> d_down and (x_perm, d_gu) -> d_gate_up.
+ *   7a  d_gu = dg | du from d_y, down and gu_saved as in (7)           (layouts as in (7))
+ *   7b  d_x_perm = d_gu @ gate_up_e^T
+ *   7c  d_w_e = P_e^T @ Q_e over the rows of expert e, for every expert (zeros without rows):
+ *       P [N, M] and Q [N, Nq] row-major with the rows grouped by expert; d_w [E*M, Nq].
+ *       max_workgroups > 0 caps the product's workgroups (rounded down to a multiple of 8, at least 8;
+ *       each holds one CU until the product ends), leaving the other CUs to kernels on other streams;
+ *       0 = one per CU. M and Nq multiples of 8; N*max(M, Nq)*2 and M*Nq*2 below 2^31, else
+ *       MOE_ERR_UNSUPPORTED. All bf16 (fp32: MOE_ERR_UNSUPPORTED), 16-byte aligned.                 */
+moe_status moe_grouped_gemm_down_bwd(const void* d_y, const void* down, const void* gu_saved, moe_dtype dt, int N,
+                                     int H, int I, int E, const int32_t* expert_offsets, void* d_gu,
+                                     hipStream_t stream);
+moe_status moe_grouped_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, moe_dtype dt, int N, int H, int I,
+                                        int E, const int32_t* expert_offsets, void* d_x_perm, hipStream_t stream);
+moe_status moe_grouped_gemm_wgrad(const void* P, const void* Q, moe_dtype dt, int N, int M, int Nq, int E,
+                                  const int32_t* expert_offsets, void* d_w, int max_workgroups, hipStream_t stream);
+
 /* ---- (8) permute backward (gather-sum of a token's k rows) ----------------------------------------
  *   d_x[t] = d_x_add[t] + sum_{j<k} d_x_perm[row_of_slot[t*k+j]]   (fp32, rounded once; d_x_add may
  *   be NULL; slots with row_of_slot < 0 are skipped).  d_x_perm [N,H], d_x_add, d_x [T,H] dt.         */

@@ -57,6 +57,9 @@ def load_library() -> ctypes.CDLL:
             "moe_unpermute_combine": (I, [P, I, I, I, I, P, P, P, P, P]),
             "moe_unpermute_combine_bwd": (I, [P, P, I, I, I, I, P, P, P, P, P]),
             "moe_grouped_swiglu_ffn_bwd": (I, [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P, P]),
+            "moe_grouped_gemm_down_bwd": (I, [P, P, P, I, I, I, I, I, P, P, P]),
+            "moe_grouped_gemm_gate_up_bwd": (I, [P, P, I, I, I, I, I, P, P, P]),
+            "moe_grouped_gemm_wgrad": (I, [P, P, I, I, I, I, I, P, P, I, P]),
             "moe_permute_bwd": (I, [P, I, I, I, I, P, P, P, P]),
             "moe_router_topk_bwd": (I, [P, P, P, P, I, I, I, I, P, P]),
             "moe_router_logits_bwd": (I, [P, P, P, I, I, I, I, P, P, P, P]),
@@ -350,6 +353,52 @@ def moe_grouped_swiglu_ffn_bwd(d_y, x_perm, gu_saved, h, gate_up, down, expert_o
     return d_x_perm, d_gate_up, d_down, d_gu
 
 
+def moe_grouped_gemm_down_bwd(d_y, down, gu_saved, expert_offsets, d_gu=None, stream=None):
+    """d_gu = SwiGLU backward of d_y @ down_e^T for every expert's rows (first product of the FFN backward)."""
+    N, H = d_y.shape
+    E = expert_offsets.shape[0] - 1
+    I = gu_saved.shape[1] // 2
+    _need(down, "down", d_y.dtype, (E * I, H)), _need(gu_saved, "gu_saved", d_y.dtype, (N, 2 * I))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    if d_gu is None:
+        d_gu = torch.empty((N, 2 * I), dtype=d_y.dtype, device=d_y.device)
+    _check(load_library().moe_grouped_gemm_down_bwd(_ptr(d_y), _ptr(down), _ptr(gu_saved), _dt(d_y), N, H, I, E,
+                                                    _ptr(expert_offsets), _ptr(d_gu), _stream(stream)),
+           "moe_grouped_gemm_down_bwd")
+    return d_gu
+
+
+def moe_grouped_gemm_gate_up_bwd(d_gu, gate_up, expert_offsets, d_x_perm=None, stream=None):
+    """d_x_perm = d_gu @ gate_up_e^T for every expert's rows."""
+    N = d_gu.shape[0]
+    I = d_gu.shape[1] // 2
+    E = expert_offsets.shape[0] - 1
+    H = gate_up.shape[0] // E
+    _need(gate_up, "gate_up", d_gu.dtype, (E * H, 2 * I)), _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    if d_x_perm is None:
+        d_x_perm = torch.empty((N, H), dtype=d_gu.dtype, device=d_gu.device)
+    _check(load_library().moe_grouped_gemm_gate_up_bwd(_ptr(d_gu), _ptr(gate_up), _dt(d_gu), N, H, I, E,
+                                                       _ptr(expert_offsets), _ptr(d_x_perm), _stream(stream)),
+           "moe_grouped_gemm_gate_up_bwd")
+    return d_x_perm
+
+
+def moe_grouped_gemm_wgrad(P, Q, expert_offsets, d_w=None, max_workgroups=0, stream=None):
+    """d_w[e*M:(e+1)*M] = P_e^T @ Q_e over the rows of expert e (P [N, M], Q [N, Nq], rows grouped by
+    expert); max_workgroups > 0 caps the CUs the product holds."""
+    N, M = P.shape
+    Nq = Q.shape[1]
+    E = expert_offsets.shape[0] - 1
+    _need(Q, "Q", P.dtype, (N, Nq)), _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    if d_w is None:
+        d_w = torch.empty((E * M, Nq), dtype=P.dtype, device=P.device)
+    _need(d_w, "d_w", P.dtype, (E * M, Nq))
+    _check(load_library().moe_grouped_gemm_wgrad(_ptr(P), _ptr(Q), _dt(P), N, M, Nq, E, _ptr(expert_offsets),
+                                                 _ptr(d_w), int(max_workgroups), _stream(stream)),
+           "moe_grouped_gemm_wgrad")
+    return d_w
+
+
 def moe_permute_bwd(d_x_perm, row_of_slot, T, k, d_x_add=None, d_x=None, stream=None):
     H = d_x_perm.shape[1]
     _need(d_x_perm, "d_x_perm"), _need(row_of_slot, "row_of_slot", torch.int32)
@@ -576,6 +625,72 @@ class LayerGrads:
             self.d_shared_gate_up = torch.empty((H, 2 * I_shared), dtype=dtype, device=device)
             self.d_shared_down = torch.empty((I_shared, H), dtype=dtype, device=device)
             self.d_shared_gu = torch.empty((T, 2 * I_shared), dtype=dtype, device=device)
+
+
+class OverlappedBackward:
+    """moe_layer_backward with its independent products on three streams (default priority):
+
+      main   combine bwd -> dY.down^T + SwiGLU bwd (dGU) -> dGU.gate_up^T (dX) -> join -> permute bwd
+      wgrad  after combine bwd: dW_down = h^T dY; after dGU: dW_gate_up = X^T dGU
+      aux    after combine bwd: shared-expert backward -> top-k bwd -> router-logits bwd
+
+    The weight gradients are bound by writing their E*3*H*I outputs and the data gradients by the
+    matrix cores, so the two share the chip better than they follow each other: the weight-gradient
+    products (persistent, one workgroup per CU) are capped to `wgrad_cus` CUs and the data-gradient
+    tiles run on the others. Every product is the same kernel on the same inputs as in the one-stream
+    backward, so the gradients are bit-identical to moe_layer_backward's."""
+
+    def __init__(self, device=None, wgrad_cus=128):
+        self.wgrad_cus = wgrad_cus
+        self.wgrad = torch.cuda.Stream(device=device)
+        self.aux = torch.cuda.Stream(device=device)
+        self.ev_dy, self.ev_dgu, self.ev_wgrad, self.ev_aux = (torch.cuda.Event() for _ in range(4))
+
+    def __call__(self, d_out, x, gate_up, down, bufs, w_gate=None, logits=None, renorm=True, shared_gate_up=None,
+                 shared_down=None, grads=None, stream=None):
+        main = torch.cuda.current_stream() if stream is None else stream
+        T, H = x.shape
+        E = gate_up.shape[0] // H
+        I = gate_up.shape[1] // 2
+        k = bufs.topk_idx.shape[1]
+        I_sh = 0 if shared_gate_up is None else shared_gate_up.shape[1] // 2
+        if bufs.gu_saved is None:
+            raise ValueError("OverlappedBackward: run the forward with save_for_backward=True")
+        if grads is None:
+            grads = LayerGrads(T, H, I, E, k, x.dtype, x.device, I_shared=I_sh, router=w_gate is not None)
+        g = grads
+        offs = bufs.plan.offsets
+        # the side streams also wait for whatever the caller queued before (inputs, earlier users of grads)
+        self.wgrad.wait_stream(main)
+        self.aux.wait_stream(main)
+        moe_unpermute_combine_bwd(d_out, bufs.y, bufs.plan.row_of_slot, bufs.topk_w, g.d_y, g.d_w, main)
+        self.ev_dy.record(main)
+        self.wgrad.wait_event(self.ev_dy)
+        self.aux.wait_event(self.ev_dy)
+        moe_grouped_gemm_wgrad(bufs.h, g.d_y, offs, g.d_down, self.wgrad_cus, self.wgrad)
+        moe_grouped_gemm_down_bwd(g.d_y, down, bufs.gu_saved, offs, g.d_gu, main)
+        self.ev_dgu.record(main)
+        self.wgrad.wait_event(self.ev_dgu)
+        moe_grouped_gemm_wgrad(bufs.x_perm, g.d_gu, offs, g.d_gate_up, self.wgrad_cus, self.wgrad)
+        moe_grouped_gemm_gate_up_bwd(g.d_gu, gate_up, offs, g.d_x_perm, main)
+        side = None
+        if I_sh:
+            sh = bufs.shared
+            moe_grouped_swiglu_ffn_bwd(d_out, x, sh["gu_saved"], sh["h"], shared_gate_up, shared_down, sh["offsets"],
+                                       g.d_x_side, g.d_shared_gate_up, g.d_shared_down, g.d_shared_gu, self.aux)
+            side = g.d_x_side
+        logits = bufs.logits if logits is None else logits
+        moe_router_topk_bwd(logits, bufs.topk_idx, bufs.topk_w, g.d_w, renorm, g.d_logits, self.aux)
+        if w_gate is not None:
+            dst = g.d_x_side2 if side is not None else g.d_x_side
+            moe_router_logits_bwd(x, w_gate, g.d_logits, g.d_w_gate, d_x_in=side, d_x=dst, stream=self.aux)
+            side = dst
+        self.ev_wgrad.record(self.wgrad)
+        self.ev_aux.record(self.aux)
+        main.wait_event(self.ev_wgrad)
+        main.wait_event(self.ev_aux)
+        moe_permute_bwd(g.d_x_perm, bufs.plan.row_of_slot, T, k, d_x_add=side, d_x=g.d_x, stream=main)
+        return g
 
 
 def moe_layer_backward(d_out, x, gate_up, down, bufs, w_gate=None, logits=None, renorm=True, shared_gate_up=None,

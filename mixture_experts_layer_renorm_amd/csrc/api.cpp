@@ -287,6 +287,59 @@ moe_status moe_grouped_swiglu_ffn_bwd(const void* d_y, const void* x_perm, const
   return hip_status(e, fn);
 }
 
+namespace {
+moe_status check_bwd(const char* fn, moe_dtype dt, int N, int H, int I, int E) {
+  moe_status st = check_ffn(fn, dt, N, H, I, E);
+  if (st != MOE_OK) return st;
+  REQUIRE(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: the backward is implemented for bf16", fn);
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_grouped_gemm_down_bwd(const void* d_y, const void* down, const void* gu_saved, moe_dtype dt, int N,
+                                     int H, int I, int E, const int32_t* expert_offsets, void* d_gu,
+                                     hipStream_t stream) {
+  const char* fn = "moe_grouped_gemm_down_bwd";
+  moe_status st = check_bwd(fn, dt, N, H, I, E);
+  if (st != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE(d_y && down && gu_saved && expert_offsets && d_gu, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(!misaligned16(d_y) && !misaligned16(down) && !misaligned16(gu_saved) && !misaligned16(d_gu),
+          MOE_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  return hip_status(moe::launch_gemm_down_bwd(d_y, down, gu_saved, N, H, I, E, expert_offsets, d_gu, stream), fn);
+}
+
+moe_status moe_grouped_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, moe_dtype dt, int N, int H, int I,
+                                        int E, const int32_t* expert_offsets, void* d_x_perm, hipStream_t stream) {
+  const char* fn = "moe_grouped_gemm_gate_up_bwd";
+  moe_status st = check_bwd(fn, dt, N, H, I, E);
+  if (st != MOE_OK) return st;
+  if (N == 0) return ok();
+  REQUIRE(d_gu && gate_up && expert_offsets && d_x_perm, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(!misaligned16(d_gu) && !misaligned16(gate_up) && !misaligned16(d_x_perm), MOE_ERR_INVALID_ARG,
+          "%s: buffers must be 16-byte aligned", fn);
+  return hip_status(moe::launch_gemm_gate_up_bwd(d_gu, gate_up, N, H, I, E, expert_offsets, d_x_perm, stream), fn);
+}
+
+moe_status moe_grouped_gemm_wgrad(const void* P, const void* Q, moe_dtype dt, int N, int M, int Nq, int E,
+                                  const int32_t* expert_offsets, void* d_w, int max_workgroups, hipStream_t stream) {
+  const char* fn = "moe_grouped_gemm_wgrad";
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  REQUIRE(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: implemented for bf16", fn);
+  REQUIRE(N >= 0 && M >= 1 && Nq >= 1, MOE_ERR_INVALID_ARG, "%s: N=%d M=%d Nq=%d out of range", fn, N, M, Nq);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  REQUIRE(M % 8 == 0 && Nq % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: M and Nq must be multiples of 8 (M=%d Nq=%d)", fn, M,
+          Nq);
+  // rows of one expert and one expert's output block are addressed with 32-bit byte offsets
+  REQUIRE((int64_t)N * (M > Nq ? M : Nq) * 2 < 0x7fffffffLL && (int64_t)M * Nq * 2 < 0x7fffffffLL,
+          MOE_ERR_UNSUPPORTED, "%s: N*max(M, Nq) or M*Nq too large for one call (N=%d M=%d Nq=%d)", fn, N, M, Nq);
+  REQUIRE(expert_offsets && d_w, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (N > 0) REQUIRE(P && Q, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(!misaligned16(P) && !misaligned16(Q) && !misaligned16(d_w), MOE_ERR_INVALID_ARG,
+          "%s: buffers must be 16-byte aligned", fn);
+  return hip_status(moe::launch_gemm_wgrad(P, Q, M, Nq, E, expert_offsets, d_w, stream, max_workgroups), fn);
+}
+
 moe_status moe_permute_bwd(const void* d_x_perm, moe_dtype dt, int T, int H, int k, const int32_t* row_of_slot,
                            const void* d_x_add, void* d_x, hipStream_t stream) {
   const char* fn = "moe_permute_bwd";

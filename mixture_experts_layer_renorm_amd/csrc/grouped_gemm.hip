@@ -1299,7 +1299,7 @@ hipError_t launch_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, int N,
 // are k-row tiles; the result block of expert e is [M, Nq] at dW + e * M * Nq. Every expert gets a
 // block (zeros when it has no rows).
 hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E, const int32_t* offsets, void* d_w,
-                             hipStream_t s) {
+                             hipStream_t s, int max_wg) {
   GemmArgs g{};
   g.A = (const uint16_t*)P;
   g.B = (const uint16_t*)Q;
@@ -1325,8 +1325,10 @@ hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E,
                                                  hipSuccess || cus <= 0)
       cus = 256;
   }
-  const int64_t grid_res = std::min<int64_t>(round_up8((int64_t)E * g.ntiles_m), (int64_t)round_up8(cus));
-  const int64_t grid = std::min<int64_t>(round_up8(total), (int64_t)round_up8(cus));
+  // a multiple of 8 (the tile lists are split over the 8 XCDs), at least 8
+  const int64_t cap = max_wg > 0 ? std::max<int64_t>(8, std::min(max_wg, cus) / 8 * 8) : round_up8(cus);
+  const int64_t grid_res = std::min<int64_t>(round_up8((int64_t)E * g.ntiles_m), cap);
+  const int64_t grid = std::min<int64_t>(round_up8(total), cap);
   hipLaunchKernelGGL(grouped_wgrad_res_kernel, dim3((unsigned)grid_res), dim3(kGemmThreads), 0, s, g);
   hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
   return hipGetLastError();

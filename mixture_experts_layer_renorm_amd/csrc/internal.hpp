@@ -39,8 +39,10 @@ hipError_t launch_gemm_down_bwd(const void* d_y, const void* down, const void* g
                                 const int32_t* offsets, void* d_gu, hipStream_t s);
 hipError_t launch_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, int N, int H, int I, int E,
                                    const int32_t* offsets, void* d_x, hipStream_t s);
+// max_wg > 0 caps the workgroups (one per CU) of the persistent weight-gradient kernels, so that
+// another stream's kernels can run on the remaining CUs
 hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E, const int32_t* offsets, void* d_w,
-                             hipStream_t s);
+                             hipStream_t s, int max_wg = 0);
 
 // backward.hip
 hipError_t launch_combine_bwd(const void* d_out, const void* y, int dt, int T, int H, int k, const int32_t* row_of_slot,

@@ -110,7 +110,6 @@ __global__ __launch_bounds__(kPlanThreads) void permute_plan_kernel(
 // One wave per token; 16-byte vectors when rows allow it, 2-byte units otherwise.
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 constexpr int kScatterWaves = 4;
-constexpr int kMaxK = 32;
 
 __global__ __launch_bounds__(kScatterWaves * kWave) void permute_scatter_kernel(
     const uint8_t* __restrict__ x, int T, int64_t row_bytes, int k, const int32_t* __restrict__ row_of_slot,
