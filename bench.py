@@ -95,11 +95,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
-    ap.add_argument("--ffn-groups", type=int, default=0,
+    ap.add_argument("--ffn-groups", type=int, default=1,
                     help="forward only: the routed FFN as this many expert groups on their own streams in the timed "
-                         "step (1 = one stream; 0 = 2 when experts average at most 320 rows, where one launch's "
-                         "tile list is about 3 waves and its tail matters, else 1); per-kernel figures come from a "
-                         "one-stream pass")
+                         "step (1 = one stream); per-kernel figures come from a one-stream pass")
     ap.add_argument("--chunks", type=int, default=1,
                     help="forward only: split the tokens in N chunks and route chunk c+1 on a side stream while "
                          "chunk c's experts run (Domino-style overlap); the step time is the chunked one")
@@ -238,7 +236,7 @@ def main():
     ms_per_step = max(wall * 1e3 / args.steps, total_ev / args.steps)
     one_stream_ms = ms_per_step
     step_us = None
-    ffn_groups = args.ffn_groups if args.ffn_groups > 0 else (2 if N <= 320 * E else 1)
+    ffn_groups = max(1, args.ffn_groups)
     if wl.backward or sh is not None:
         ffn_groups = 1
     st2 = None

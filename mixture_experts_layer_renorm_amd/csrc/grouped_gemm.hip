@@ -53,13 +53,14 @@ constexpr int kDmaPerWave = (kTileA + kTileB) / 1024 / kWaves;  // 1 KB per wave
 constexpr int kDmaA = kTileA / 1024 / kWaves;  // DMA instructions per wave per step, operand A
 constexpr int kDmaB = kTileB / 1024 / kWaves;  // and operand B
 constexpr int kGemmMaxE = 1024;
-// Row-grouped products: a tile holds up to kBMX = 288 rows, the regular 256 plus an extra band of
-// up to 32 rows, so an expert with 257..288 rows (common at E = 128, k = 8, T = 4096, where counts
-// sit around 256 +- 16) is one tile instead of a full tile plus a nearly empty one that streams the
-// same weight panel again. The extra band is spread over the eight waves as one 32-row block each,
-// against a 32-column slice (16 gate + 16 up output columns in the SwiGLU case).
-constexpr int kBMX = kBM + 32;
-constexpr int kTileAX = kBMX * kBK * 2;   // 18 KB: 18 DMA instructions, 2 per wave + 1 for waves 0, 1
+// Row-grouped products: a tile holds up to kBMX = 320 rows, the regular 256 plus an extra band of
+// up to 64 rows, so an expert with 257..320 rows (E = 128, k = 8, T = 4096 gives counts of 256 with
+// a standard deviation near 16) is one tile instead of a full tile plus a nearly empty one that
+// streams the same weight panel again, and the tile count stays a multiple of the CU count. The
+// extra band is one or two 32-row blocks (as many as the tile's rows need), each spread over the
+// eight waves against a 32-column slice per wave (16 gate + 16 up output columns with SwiGLU).
+constexpr int kBMX = kBM + 64;
+constexpr int kTileAX = kBMX * kBK * 2;   // 20 KB: 20 DMA instructions, 2 per wave + 1 for waves 0-3
 
 // LDS swizzles, applied when choosing which global chunk each DMA lane fetches. They keep the
 // fragment reads free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
@@ -162,13 +163,13 @@ __device__ __forceinline__ void store_swiglu_bwd(const GemmArgs& g, uint16_t* cb
   *reinterpret_cast<uint2*>(dr + g.N + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
 }
 
-// Epilogue of the extra band (row-grouped products): lane holds tile row 256 + (lane & 31) and, for
-// accumulator element q, slice column (q / 4) * 8 + (lane / 32) * 4 + q % 4: gate columns 0..15
-// and up columns 16..31 of the SwiGLU slice g0, else columns wn*128 + wm*32 + 0..31.
+// Epilogue of extra-band block xb (row-grouped products): lane holds tile row 256 + 32 xb + (lane & 31)
+// and, for accumulator element q, slice column (q / 4) * 8 + (lane / 32) * 4 + q % 4: gate columns
+// 0..15 and up columns 16..31 of the SwiGLU slice g0, else columns wn*128 + wm*32 + 0..31.
 template <int EPI>
-__device__ __forceinline__ void store_extra(const GemmArgs& g, const f32x16& acc, int m0, int mvalid, int n0, int nt,
-                                            int g0, int wm, int wn, int lane) {
-  const int mloc = kBM + (lane & 31);
+__device__ __forceinline__ void store_extra(const GemmArgs& g, const f32x16& acc, int xb, int m0, int mvalid, int n0,
+                                            int nt, int g0, int wm, int wn, int lane) {
+  const int mloc = kBM + xb * 32 + (lane & 31);
   if (mloc >= mvalid) return;
   const int64_t m = m0 + mloc;
   if constexpr (EPI == kEpiSwiglu) {
@@ -384,8 +385,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
         a_rd[kk][mb][0] = row_rd(wm * 64 + mb * 32 + (lane & 31), kk);
         a_rd[kk][mb][1] = 0;
       } else {
-        a_rd[kk][mb][0] = krow_rd(wm * 64 + mb * 32, kk, 0);
-        a_rd[kk][mb][1] = krow_rd(wm * 64 + mb * 32, kk, 1);
+        a_rd[kk][mb][0] = krow_rd(wm * 64 + mb * 32, 0, 0);  // + kk * 8192 at the read
+        a_rd[kk][mb][1] = 0;
       }
     }
 #pragma unroll
@@ -394,16 +395,17 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
         b_rd[kk][nb][0] = row_rd(bcol[nb] + (lane & 31), kk);
         b_rd[kk][nb][1] = 0;
       } else {
-        b_rd[kk][nb][0] = krow_rd(bcol[nb], kk, 0);
-        b_rd[kk][nb][1] = krow_rd(bcol[nb], kk, 1);
+        b_rd[kk][nb][0] = krow_rd(bcol[nb], 0, 0);  // + kk * 8192 at the read
+        b_rd[kk][nb][1] = 0;
       }
     }
   }
 
-  // Extra band (row-grouped products): A block = tile rows 256..287; B block = this wave's
+  // Extra band (row-grouped products): A blocks = tile rows 256..287 and 288..319; B block = this wave's
   // 32-column slice: columns wn*128 + wm*32 of its half, or for SwiGLU the 16 gate columns
   // g0 .. g0+15 (lanes with column index < 16) and the matching 16 up columns, g0 = (wn*4+wm)*16.
   const int g0 = (wn * 4 + wm) * 16;
+  // (the second band block's addresses are the first's + 32 rows: the row swizzle repeats every 16 rows)
   int xa_rd[2], xb_rd[2][2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -414,13 +416,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     } else if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
       for (int ri = 0; ri < 2; ++ri) {
-        const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
+        const int kr = (q >> 1) * 8 + (sl >> 2);  // k-row of kk = 0, ri = 0 (+ kk * 8192 at the read)
         const int col = (q & 1) * 128 + g0 + 4 * (sl & 3);
-        xb_rd[kk][ri] = kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+        xb_rd[kk][ri] = ri ? 0 : kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
       }
     } else {
-      xb_rd[kk][0] = krow_rd(wn * 128 + wm * 32, kk, 0);
-      xb_rd[kk][1] = krow_rd(wn * 128 + wm * 32, kk, 1);
+      xb_rd[kk][0] = krow_rd(wn * 128 + wm * 32, 0, 0);
+      xb_rd[kk][1] = 0;
     }
   }
 
@@ -433,46 +435,66 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
 
   struct Frags {
-    bf16x8 a[2], b[4], xa, xb;
+    bf16x8 a[2], b[4], xa[2], xb;
   };
-  auto frag = [&](const uint8_t* base, const int* rd, bool rows) -> bf16x8 {
+  // k-row tiles: the swizzle depends on the k-row mod 4 only, so the lane's address for k-rows +4
+  // (second half of its 8 k) is +2048 bytes and for sub-step kk = 1 (+16 k-rows) +8192: one base
+  // register per 32-column block, the rest in the instructions' offset fields
+  auto frag = [&](const uint8_t* base, const int* rd, bool rows, int kk) -> bf16x8 {
     if (rows) return *reinterpret_cast<const bf16x8*>(base + rd[0]);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[0]));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + rd[1]));
+    const uint8_t* p = base + rd[0] + kk * 8192;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2048));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // NMB = number of this wave's 32-row blocks that hold rows (0..2, wave-uniform). Waves of one
-  // tile may run different NMB variants: every variant issues the same DMAs and barriers.
-  auto read_frags = [&](auto nmb_c, auto x_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
+  // NMB = number of this wave's 32-row blocks that hold rows (0..2, wave-uniform); NX = number of
+  // extra-band blocks of the tile (0..2). Waves of one tile may run different NMB variants: every
+  // variant issues the same DMAs and barriers.
+  auto read_frags = [&](auto nmb_c, auto nx_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
     constexpr int NMB = decltype(nmb_c)::value;
+    constexpr int NX = decltype(nx_c)::value;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag(sb, b_rd[kk][nb], B_ROWS);
+    for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag(sb, b_rd[kk][nb], B_ROWS, kk);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = frag(sa, a_rd[kk][mb], A_ROWS);
-    if constexpr (decltype(x_c)::value) {
-      f.xa = frag(sa, &xa_rd[kk], true);
-      f.xb = frag(sb, xb_rd[kk], B_ROWS);
+    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = frag(sa, a_rd[kk][mb], A_ROWS, kk);
+    if constexpr (NX > 0) {
+#pragma unroll
+      for (int xb = 0; xb < NX; ++xb) f.xa[xb] = frag(sa + xb * 32 * 64, &xa_rd[kk], true, kk);
+      f.xb = frag(sb, xb_rd[kk], B_ROWS, kk);
     }
   };
-  auto mfmas = [&](auto nmb_c, auto x_c, const Frags& f, f32x16& acc_x) {
+  auto mfmas = [&](auto nmb_c, auto nx_c, const Frags& f, f32x16* acc_x) {
     constexpr int NMB = decltype(nmb_c)::value;
+    constexpr int NX = decltype(nx_c)::value;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
-    if constexpr (decltype(x_c)::value) acc_x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb, f.xa, acc_x, 0, 0, 0);
+#pragma unroll
+    for (int xb = 0; xb < NX; ++xb)
+      acc_x[xb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb, f.xa[xb], acc_x[xb], 0, 0, 0);
   };
   // One step: prefetch step kt+3 into the slot freed by step kt-1, compute step kt, then wait for
   // this wave's DMA of step kt+1 (the two later steps stay in flight) and meet at the barrier.
   // The scheduler is told to interleave: the first sub-step's fragment reads, then MFMAs with the
   // DMA issues and the second sub-step's fragment reads threaded between them.
-  auto step = [&](auto nmb_c, auto x_c, f32x16& acc_x, int kt, const uint8_t* sa, const uint8_t* sb, uint8_t* pa,
+  auto step = [&](auto nmb_c, auto x_c, f32x16* acc_x, int kt, const uint8_t* sa, const uint8_t* sb, uint8_t* pa,
                   uint8_t* pb) {
     constexpr int NMB = decltype(nmb_c)::value;
-    constexpr int X = decltype(x_c)::value ? 1 : 0;
+    constexpr int NX = decltype(x_c)::value;
+    constexpr int X = NX > 0 ? 1 : 0;
     if constexpr (NMB == 0) {
       dma(kt + 3, pa, pb);
+    } else if constexpr (NX == 2) {
+      // two band blocks: the sub-steps one after the other, so that one set of fragments is live
+      // (both sets with the band's accumulators would not fit in the register budget)
+      Frags f;
+      read_frags(nmb_c, x_c, sa, sb, 0, f);
+      dma(kt + 3, pa, pb);
+      mfmas(nmb_c, x_c, f, acc_x);
+      read_frags(nmb_c, x_c, sa, sb, 1, f);
+      mfmas(nmb_c, x_c, f, acc_x);
     } else {
       Frags f0, f1;
       read_frags(nmb_c, x_c, sa, sb, 0, f0);
@@ -480,8 +502,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       dma(kt + 3, pa, pb);
       mfmas(nmb_c, x_c, f0, acc_x);
       mfmas(nmb_c, x_c, f1, acc_x);
-      constexpr int R = (B_ROWS ? 4 : 8) + (A_ROWS ? 1 : 2) * NMB + X * (1 + (B_ROWS ? 1 : 2));  // LDS reads per sub-step
-      constexpr int M = 4 * NMB + X;                                                          // MFMAs per sub-step
+      constexpr int R = (B_ROWS ? 4 : 8) + (A_ROWS ? 1 : 2) * NMB + NX + X * (B_ROWS ? 1 : 2);  // LDS reads per sub-step
+      constexpr int M = 4 * NMB + NX;                                                          // MFMAs per sub-step
       __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
       for (int i = 0; i < DPW; ++i) {
@@ -499,9 +521,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     // count is padded to a multiple of the ring depth and the loop body has no memory branches.
     const int KT = (K + kBK - 1) / kBK;
     const int KT4 = (KT + kStages - 1) / kStages * kStages;
-    f32x16 acc_x;
+    f32x16 acc_x[2];
 #pragma unroll
-    for (int qq = 0; qq < 16; ++qq) acc_x[qq] = 0.0f;
+    for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+      for (int qq = 0; qq < 16; ++qq) acc_x[xb][qq] = 0.0f;
     dma(0, sA0, sB0);
     dma(1, sA1, sB1);
     dma(2, sA2, sB2);
@@ -513,13 +537,20 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       step(nmb_c, x_c, acc_x, kt + 3, sA3, sB3, sA2, sB2);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (decltype(x_c)::value) store_extra<EPI>(g, acc_x, m0, mvalid, n0, nt, g0, wm, wn, lane);
+#pragma unroll
+    for (int xb = 0; xb < decltype(x_c)::value; ++xb)
+      store_extra<EPI>(g, acc_x[xb], xb, m0, mvalid, n0, nt, g0, wm, wn, lane);
   };
   const int wrows = mvalid - wm * 64;
   const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(2, (wrows + 31) / 32));
-  using F = std::false_type;
+  using F = std::integral_constant<int, 0>;
   if (ROWS && mvalid > kBM) {  // the extra band holds rows: every regular band is full
-    if constexpr (ROWS) main_loop(std::integral_constant<int, 2>{}, std::true_type{});
+    if constexpr (ROWS) {
+      if (mvalid > kBM + 32)
+        main_loop(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+      else
+        main_loop(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+    }
   } else {
     switch (nmb) {
       case 2: main_loop(std::integral_constant<int, 2>{}, F{}); break;

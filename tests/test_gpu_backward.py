@@ -90,7 +90,8 @@ def test_router_logits_bwd(T, H, E, dtype, add):
     ([3, 0, 0, 517, 31, 64, 0, 1], 512, 128),
     ([0, 0, 0], 64, 32),
     ([600, 5], 7168, 256),
-    ([288, 289, 270, 0, 257], 136, 40),                # tiles with an extra band of up to 32 rows
+    ([288, 289, 270, 0, 257], 136, 40),                # tiles with an extra band of one or two blocks
+    ([320, 321, 300, 0, 641], 136, 40),                # two-block bands and 320-row tiles
 ])
 def test_grouped_swiglu_ffn_bwd(counts, H, I):
     E = len(counts)

@@ -105,8 +105,10 @@ def test_permute_bit_exact(T, H, E, k, dtype, skew):
     ([3, 0, 0, 517, 31, 64, 0, 1], 512, 128, "bf16"),
     ([16, 16, 16, 16, 16, 16, 16, 16], 64, 32, "f32"),
     ([0, 5, 0, 40], 48, 16, "f32"),
-    ([288, 289, 270, 0, 256, 577], 136, 40, "bf16"),   # tiles with an extra band of up to 32 rows
+    ([288, 289, 270, 0, 256, 577], 136, 40, "bf16"),   # tiles with an extra band of one 32-row block
     ([260, 300], 256, 384, "bf16"),
+    ([320, 321, 319, 0, 640, 641, 33, 290], 136, 40, "bf16"),   # two-block bands, 320-row tiles, splits
+    ([300, 310, 256, 290, 333], 512, 256, "bf16"),
 ])
 def test_grouped_swiglu_ffn(counts, H, I, dtype):
     E = len(counts)
