@@ -564,6 +564,104 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
 
   // ---- epilogue: lane holds output row (lane & 31) of each 32-row block and, per 32-column
   // block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
+  if constexpr (EPI == kEpiStore && SCHED == kSchedRows) {
+    // Staged: after the K loop every ring slot is free, so the tile's 256 regular rows go to LDS as
+    // bf16 (32-row block j in slot j of sA0..sA3, sB0..sB3, 16 KB each; 16-byte chunk c of row r at
+    // chunk c ^ r) and out as whole 512-byte rows, two rows per 1 KB store. Straight from the
+    // accumulators each 8-byte-per-lane store touches 32 rows, and with every CU reaching its
+    // epilogue at about the same time that was a quarter of the down product's tile time.
+    auto blk = [&](int j) -> uint8_t* {
+      return j == 0 ? sA0 : j == 1 ? sA1 : j == 2 ? sA2 : j == 3 ? sA3 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
+    };
+    asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
+    const int lr = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      uint8_t* st = blk(wm * 2 + mb) + lr * 512 + (lane >> 5) * 8;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int chunk = (wn * 16 + nb * 4 + gq) ^ lr;
+          *reinterpret_cast<uint2*>(st + (chunk << 4)) =
+              make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                         pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint8_t* src = blk(wave);
+    const int c = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 2 * i + (lane >> 5);
+      const int mloc = wave * 32 + r, col = n0 + c * 8;
+      if (mloc < mvalid && col < g.N) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + r * 512 + ((c ^ r) << 4));
+        {
+          typedef __attribute__((ext_vector_type(4))) unsigned int v4u;
+          __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(g.C + (int64_t)(m0 + mloc) * g.ldc + col));
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (EPI == kEpiSwiglu && SCHED == kSchedRows) {
+    // Staged as above: h of the 256 regular rows (128 columns, 256-byte rows) goes to LDS (32-row
+    // block j in the first 8 KB of slot j; 16-byte chunk c of row r at chunk c ^ (r & 15)) and out as
+    // whole rows, four per 1 KB store; the saved g | u (training only) are stored straight
+    auto blk = [&](int j) -> uint8_t* {
+      return j == 0 ? sA0 : j == 1 ? sA1 : j == 2 ? sA2 : j == 3 ? sA3 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
+    };
+    asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
+    const int lr = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      uint8_t* st = blk(wm * 2 + mb) + lr * 256 + (lane >> 5) * 8;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float hv[4];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[mb][nb][gq * 4 + qq]) * acc[mb][nb + 2][gq * 4 + qq];
+          const int chunk = (wn * 8 + nb * 4 + gq) ^ (lr & 15);
+          *reinterpret_cast<uint2*>(st + (chunk << 4)) = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+        }
+      if (g.gu_out) {
+        const int mloc = wm * 64 + mb * 32 + lr;
+        if (mloc < mvalid) {
+          uint16_t* gs = g.gu_out + (int64_t)(m0 + mloc) * 2 * g.N;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = nt * 128 + wn * 64 + nb * 32 + gq * 8 + (lane >> 5) * 4;
+              if (col >= g.N) continue;
+              *reinterpret_cast<uint2*>(gs + col) =
+                  make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                             pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
+              *reinterpret_cast<uint2*>(gs + g.N + col) =
+                  make_uint2(pack_bf16x2(acc[mb][nb + 2][gq * 4 + 0], acc[mb][nb + 2][gq * 4 + 1]),
+                             pack_bf16x2(acc[mb][nb + 2][gq * 4 + 2], acc[mb][nb + 2][gq * 4 + 3]));
+            }
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint8_t* src = blk(wave);
+    const int c = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int mloc = wave * 32 + r, col = nt * 128 + c * 8;
+      if (mloc < mvalid && col < g.N) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + r * 256 + ((c ^ (r & 15)) << 4));
+        typedef __attribute__((ext_vector_type(4))) unsigned int v4u;
+        __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(g.C + (int64_t)(m0 + mloc) * g.ldc + col));
+      }
+    }
+    return;
+  }
   uint16_t* cbase = SCHED == kSchedRows ? g.C : g.C + (int64_t)e * g.c_expert;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
