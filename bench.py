@@ -10,9 +10,10 @@ each stage a call into libmoe_rocm.so on the current stream:
             top-k bwd -> router-logits bwd -> permute-bwd.
 
 Prints ONE JSON line. `value` is tokens/s of the layer. The timed region is bracketed by
-torch.cuda.synchronize(); HIP events recorded on the launch stream between the calls give each
-stage's duration, from which the roofline of the dominant kernel (the gate_up grouped GEMM) is
-computed. The CPU baseline is the oracle (C, fp64, OpenMP) timed on a bounded sample of the same
+torch.cuda.synchronize(). An eager pass with HIP events recorded on the launch stream between the
+calls gives each stage's duration, from which the roofline of the dominant kernel (the gate_up
+grouped GEMM) is computed; the timed step is then the same one-stream sequence captured once in a
+HIP graph and replayed (--no-graph: the eager pass is the timed step). The CPU baseline is the oracle (C, fp64, OpenMP) timed on a bounded sample of the same
 tokens. --copy-calibration runs one 512 MiB device-to-device copy first, the known-size kernel
 that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters into HBM bytes.
 """
@@ -105,6 +106,10 @@ def main():
                     help="backward workloads: time the step with the backward on three streams and the weight "
                          "gradients capped to this many CUs (0 = one stream); per-kernel figures come from a "
                          "one-stream pass")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="time the step as eager launches; by default the one-stream step is captured once in a HIP "
+                         "graph and the timed steps are its replays (the same kernels on the same buffers, without "
+                         "per-launch host overhead); the per-kernel figures always come from the eager pass")
     ap.add_argument("--no-gather", action="store_true",
                     help="forward: copy the rows to x_perm in the permute instead of gathering them in GEMM-1")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -285,6 +290,31 @@ def main():
         seg2 /= args.steps
         ms_per_step = max(wall * 1e3 / args.steps, tot2 / args.steps)
         step_us = {n: round(seg2[i] * 1e3, 2) for i, (n, _) in enumerate(st2)}
+    graph_ms = None
+    use_graph = args.graph and st2 is None and args.chunks == 1   # multi-stream schedules run eagerly
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()          # default priority
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        graph_ms = max(wall * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps)
+        ms_per_step = graph_ms
     unchunked_ms = ms_per_step
     if args.chunks > 1:
         # the timed step is the chunked, two-stream forward; the per-kernel figures above (and the
@@ -352,6 +382,8 @@ def main():
     if step_us is not None:
         perf["timed_step_us"] = step_us
         perf["one_stream_ms_per_step"] = round(one_stream_ms, 4)
+    if graph_ms is not None:
+        perf["eager_ms_per_step"] = round(one_stream_ms, 4)
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -362,7 +394,8 @@ def main():
                    "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward",
                    "gemm1_rows": "gathered from x" if gather else "x_perm", "chunks": args.chunks,
                    "ffn_expert_groups": ffn_groups if args.chunks == 1 else 1,
-                   "backward_wgrad_cus": args.bwd_wgrad_cus if wl.backward else None},
+                   "backward_wgrad_cus": args.bwd_wgrad_cus if wl.backward else None,
+                   "hip_graph": use_graph},
         "roofline": roof, "perf": perf,
     }
     if args.cpu_seconds > 0:
