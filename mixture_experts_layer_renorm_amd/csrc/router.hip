@@ -13,15 +13,16 @@ namespace moe {
 // ---------------------------------------------------------------------------------------------
 // logits[t, e] = fp32 chain over h = 0..H-1 of fma(x[t,h], w_gate[h,e], acc).
 //
-// Lanes are tokens: a workgroup of 4 waves owns 64 tokens (one per lane) and 4 * EQ experts
-// (EQ per wave), so a lane runs EQ independent chains, all consuming h = 0, 1, ..., H-1 in order.
+// Lanes are tokens: a workgroup of 8 waves owns 64 tokens (one per lane) and 8 * EQ experts
+// (EQ per wave), so a lane runs EQ independent chains, all consuming h = 0, 1, ..., H-1 in order;
+// the eight waves share each x tile the workgroup stages (one workgroup per CU, two waves per SIMD).
 // The hidden dimension is walked in chunks of HB. Each chunk's x tile [64 x HB] and W_g tile
-// [HB x 4*EQ] are loaded into registers DEPTH chunks ahead (the loads of x come from HBM, so
+// [HB x 8*EQ] are loaded into registers DEPTH chunks ahead (the loads of x come from HBM, so
 // their latency has to be covered by more than one chunk of arithmetic), widened to fp32 once and
 // stored to a double-buffered LDS tile. A lane then reads four h of its own token with one 16-byte
-// read (row pitch padded by 4 floats, so 16 consecutive rows cover all banks) and the wave's EQ
-// weights of each h with 16-byte broadcast reads.
-constexpr int kLogitWaves = 4;
+// read (row pitch padded by 4 floats, so 16 consecutive rows cover all banks); the wave's weights
+// reach every lane through DPP row broadcasts (fmac4 below).
+constexpr int kLogitWaves = 8;
 constexpr int kLogitTok = kWave;  // tokens per workgroup
 
 template <typename TIn>
@@ -136,9 +137,9 @@ __device__ __forceinline__ void fmac4<8>(float* acc, const float* w, const float
 template <typename TIn, int EQ>
 struct LogitTile {
   static constexpr int EB = kLogitWaves * EQ;                     // experts per workgroup
-  static constexpr int HB = EQ >= 8 ? 64 : 32;                    // hidden chunk (64 measured faster for EQ = 8)
+  static constexpr int HB = 128;                                  // hidden chunk (the largest that fits LDS at EQ = 8)
   static constexpr int PITCH = HB + 4;                            // LDS row pitch of the x tile
-  static constexpr int DEPTH = 6;                                 // chunks in flight
+  static constexpr int DEPTH = 3;                                 // chunks in flight
   static constexpr int G = 32 / EQ;                               // h per software-pipelined group
   static constexpr int VEC = 16 / sizeof(TIn);                    // elements per 16-byte load
   static constexpr int XCH = kLogitTok * HB / VEC;                // 16-byte chunks of the x tile
@@ -516,12 +517,12 @@ static void launch_logits_t(const void* x, const void* w_gate, int T, int H, int
                      (const TIn*)w_gate, T, H, E, logits, (int)vec_x, (int)vec_w);
 }
 
-// Eight chains per lane when that still gives two workgroups per CU, else four (twice the
-// workgroups, twice the broadcast weight reads per multiply-add).
+// Eight chains per lane when that still gives a workgroup per CU, else four (twice the
+// workgroups, twice the weight broadcasts per multiply-add).
 template <typename TIn>
 static void launch_logits_dt(const void* x, const void* w_gate, int T, int H, int E, float* logits, hipStream_t s) {
-  const int64_t blocks8 = (int64_t)((T + kLogitTok - 1) / kLogitTok) * ((E + 31) / 32);
-  if (blocks8 >= 512)
+  const int64_t blocks8 = (int64_t)((T + kLogitTok - 1) / kLogitTok) * ((E + 8 * kLogitWaves - 1) / (8 * kLogitWaves));
+  if (blocks8 >= 256)
     launch_logits_t<TIn, 8>(x, w_gate, T, H, E, logits, s);
   else
     launch_logits_t<TIn, 4>(x, w_gate, T, H, E, logits, s);
