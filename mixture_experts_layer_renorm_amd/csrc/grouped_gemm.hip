@@ -92,9 +92,16 @@ __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offset
                                               int* s_pref, int* s_wtot, int* s_e, TileInfo& ti) {
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  for (int e = tid; e < E; e += NT) {
-    const int n = offsets[e + 1] - offsets[e];
-    s_pref[e] = n > 0 ? (n + bm - 1) / bm : 0;
+  // each thread keeps the offsets it loaded; the one whose expert owns the tile hands them over
+  // through LDS (reloading them from global memory would add a dependent round trip per tile)
+  constexpr int PER = (kGemmMaxE + NT - 1) / NT;
+  int my_o0[PER], my_n[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + i * NT;
+    my_o0[i] = e < E ? offsets[e] : 0;
+    my_n[i] = e < E ? offsets[e + 1] - my_o0[i] : 0;
+    if (e < E) s_pref[e] = my_n[i] > 0 ? (my_n[i] + bm - 1) / bm : 0;
   }
   __syncthreads();
   block_exclusive_scan<NT>(s_pref, E, s_wtot);
@@ -108,13 +115,20 @@ __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offset
   if ((b >> 3) >= Q || L >= total) return false;
   const int mt_g = L / ntiles_n;
   ti.nt = L - mt_g * ntiles_n;
-  for (int e = tid; e < E; e += NT)
-    if (s_pref[e] <= mt_g && mt_g < s_pref[e + 1]) *s_e = e;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + i * NT;
+    if (e < E && s_pref[e] <= mt_g && mt_g < s_pref[e + 1]) {
+      s_e[0] = e;
+      s_e[1] = my_o0[i];
+      s_e[2] = my_n[i];
+    }
+  }
   __syncthreads();
-  ti.e = __builtin_amdgcn_readfirstlane(*s_e);
+  ti.e = __builtin_amdgcn_readfirstlane(s_e[0]);
   const int p0 = __builtin_amdgcn_readfirstlane(s_pref[ti.e]), p1 = __builtin_amdgcn_readfirstlane(s_pref[ti.e + 1]);
   const int j = mt_g - p0, nte = p1 - p0;
-  const int o0 = offsets[ti.e], c = offsets[ti.e + 1] - o0;
+  const int o0 = __builtin_amdgcn_readfirstlane(s_e[1]), c = __builtin_amdgcn_readfirstlane(s_e[2]);
   ti.row0 = __builtin_amdgcn_readfirstlane(o0 + (int)((int64_t)j * c / nte));
   ti.row_end = __builtin_amdgcn_readfirstlane(o0 + (int)((int64_t)(j + 1) * c / nte));
   return true;
@@ -222,7 +236,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   __shared__ __attribute__((aligned(1024))) uint8_t sSpare[ROWS ? 1024 : 16];
   __shared__ int s_pref[kGemmMaxE + 1];
   __shared__ int s_wtot[kGemmThreads / kWave];
-  __shared__ int s_e;
+  __shared__ int s_e[3];  // the tile's expert, its first row and its row count
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   int a_records, b_records;
   if constexpr (SCHED == kSchedRows) {
     TileInfo ti;
-    if (!tile_of_block<kGemmThreads>(g.offsets, g.E, kBMX, g.ntiles_n, s_pref, s_wtot, &s_e, ti)) return;
+    if (!tile_of_block<kGemmThreads>(g.offsets, g.E, kBMX, g.ntiles_n, s_pref, s_wtot, s_e, ti)) return;
     e = ti.e;
     m0 = ti.row0;
     mvalid = ti.row_end - ti.row0;
