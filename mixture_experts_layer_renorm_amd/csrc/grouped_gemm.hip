@@ -6,14 +6,16 @@
 // optimisation doc (section 2.1) groups the experts into one call to avoid per-expert launches.
 // Gate columns are [0, I) and up columns [I, 2I) of an expert's block; h = silu(gate) * up.
 //
-// One kernel serves every grouped product of the layer, for each expert e with rows
-// [offsets[e], offsets[e+1]) of the expert-grouped buffers:
+// The grouped products of the layer, for each expert e with rows [offsets[e], offsets[e+1]) of the
+// expert-grouped buffers:
 //   forward   h  = silu(X_e Wg_e) * (X_e Wu_e)            (SwiGLU epilogue, optional saved g|u)
 //             y  = h_e D_e
 //   backward  dGU = SwiGLU'(dY_e D_e^T, g, u)              (SwiGLU-backward epilogue)
 //             dX  = dGU_e GU_e^T
-//             dD_e  = h_e^T dY_e,   dGU_e = X_e^T dGU_e   (weight gradients; K = rows of expert e,
-//                                                          experts without rows get zeros)
+// run as one row-grouped kernel template (grouped_gemm_bf16_kernel); the weight gradients
+//             dD_e  = h_e^T dY_e,   dGU_e = X_e^T dGU_e   (K = rows of expert e, experts without
+//                                                          rows get zeros)
+// have persistent kernels of their own (grouped_wgrad_res_kernel, grouped_wgrad_kernel).
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16, fp32 accumulation. A workgroup of 8 waves (2 per SIMD)
 // computes a 256 x 256 tile; each wave 64 x 128. Both operand tiles go global -> LDS by 16-byte
@@ -22,7 +24,8 @@
 // operand whose M or N dimension is contiguous is staged in its natural layout as a "k-row tile"
 // ([32 k][256 cols], 512-byte rows) and read with the LDS transpose read ds_read_b64_tr_b16, so no
 // operand is ever repacked. The MFMA takes the B fragment first, so a lane ends up holding four
-// consecutive output columns of one row, which become one 8-byte store.
+// consecutive output columns of one row; the forward epilogues stage the tile through the (then
+// free) LDS ring and store whole rows.
 #include <algorithm>
 #include <type_traits>
 
@@ -136,12 +139,11 @@ __device__ __forceinline__ bool tile_of_block(const int32_t* __restrict__ offset
 
 
 enum { kEpiSwiglu = 0, kEpiStore = 1, kEpiSwigluBwd = 2 };
-enum { kSchedRows = 0, kSchedWgrad = 1 };
 
 // Arguments of one grouped product C = A B (per expert). Sizes in elements.
 struct GemmArgs {
-  const uint16_t* A;   // rows-grouped operand (SchedRows) or activations whose rows are K (SchedWgrad)
-  const uint16_t* B;   // weights (SchedRows) or the second activation (SchedWgrad)
+  const uint16_t* A;   // row-grouped operand (row-grouped products) or P, whose rows are K (weight gradients)
+  const uint16_t* B;   // weights (row-grouped products) or Q (weight gradients)
   uint16_t* C;
   const uint16_t* gu;  // saved g|u [rows, 2*N] read by the SwiGLU-backward epilogue
   uint16_t* gu_out;    // optional g|u written by the SwiGLU epilogue [rows, 2*N]
@@ -149,11 +151,11 @@ struct GemmArgs {
   const int32_t* a_slot;  // optional (row-grouped A): A row r is row a_slot[r] / a_div of A, i.e. the
   int a_div;              // grouped rows are gathered from the token matrix through the slot map
   int E;
-  int M, N, K;         // SchedRows: N output columns, K; SchedWgrad: M, N per expert (K from offsets)
+  int M, N, K;         // row-grouped: N output columns, K (M = tokens when gathering); weight gradients: M, N per expert
   int lda, ldb, ldc;
-  int64_t b_expert;    // SchedRows: elements between two experts' weight blocks
-  int64_t c_expert;    // SchedWgrad: elements between two experts' output blocks
-  int b_rows;          // SchedRows: rows of one expert's weight block (K for a k-row B, N for a row B)
+  int64_t b_expert;    // row-grouped: elements between two experts' weight blocks
+  int64_t c_expert;    // weight gradients: elements between two experts' output blocks
+  int b_rows;          // row-grouped: rows of one expert's weight block (K for a k-row B, N for a row B)
   int ntiles_m, ntiles_n;
 };
 
@@ -225,15 +227,14 @@ __device__ __forceinline__ void store_extra(const GemmArgs& g, const f32x16& acc
 
 // A_ROWS: A is a row tile (K contiguous) - else a k-row tile (M contiguous).
 // B_ROWS: B is a row tile (K contiguous) - else a k-row tile (N contiguous).
-template <bool A_ROWS, bool B_ROWS, int EPI, int SCHED>
+template <bool A_ROWS, bool B_ROWS, int EPI>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const GemmArgs g) {
-  constexpr bool ROWS = SCHED == kSchedRows;
-  constexpr int TA = ROWS ? kTileAX : kTileA;
-  constexpr int DPW = ROWS ? kDmaPerWave + 1 : kDmaPerWave;  // DMA instructions per wave per step
+  constexpr int TA = kTileAX;
+  constexpr int DPW = kDmaPerWave + 1;  // DMA instructions per wave per step (+1: the extra band)
   // one LDS object per ring slot, so that the compiler can tell a DMA into one slot from reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TA], sA1[TA], sA2[TA], sA3[TA];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sSpare[ROWS ? 1024 : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sSpare[1024];
   __shared__ int s_pref[kGemmMaxE + 1];
   __shared__ int s_wtot[kGemmThreads / kWave];
   __shared__ int s_e[3];  // the tile's expert, its first row and its row count
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   const uint16_t* abase;
   const uint16_t* bbase;
   int a_records, b_records;
-  if constexpr (SCHED == kSchedRows) {
+  {
     TileInfo ti;
     if (!tile_of_block<kGemmThreads>(g.offsets, g.E, kBMX, g.ntiles_n, s_pref, s_wtot, s_e, ti)) return;
     e = ti.e;
@@ -266,25 +267,6 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     }
     bbase = g.B + (int64_t)e * g.b_expert;   // expert e's weight block
     b_records = g.b_rows * g.ldb * 2;
-  } else {
-    const int G = gridDim.x;
-    const int b = blockIdx.x;
-    const int L = (b & 7) * (G >> 3) + (b >> 3);
-    const int per_e = g.ntiles_m * g.ntiles_n;
-    e = L / per_e;
-    if (e >= g.E) return;
-    const int rem = L - e * per_e;
-    const int mt = rem / g.ntiles_n;
-    nt = rem - mt * g.ntiles_n;
-    m0 = mt * kBM;
-    n0 = nt * kBN;
-    mvalid = min(kBM, g.M - m0);
-    const int r0 = g.offsets[e];
-    K = __builtin_amdgcn_readfirstlane(max(0, (int)g.offsets[e + 1] - r0));  // rows of expert e
-    abase = g.A + (int64_t)r0 * g.lda;       // expert e's rows; k-row tiles over them
-    bbase = g.B + (int64_t)r0 * g.ldb;
-    a_records = K * g.lda * 2;
-    b_records = K * g.ldb * 2;
   }
   const __amdgpu_buffer_rsrc_t rsA =
       __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, a_records, kBufferWord3);
@@ -347,11 +329,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   const int x_c = (lane & 3) ^ swz_a(x_r);
   const int x_kc = x_c * 8;
   const bool x_ok = x_real && x_r < mvalid;
-  const int x_src = (ROWS && g.a_slot) ? (x_ok ? g.a_slot[m0 + x_r] / g.a_div : 0) : x_r;
+  const int x_src = g.a_slot ? (x_ok ? g.a_slot[m0 + x_r] / g.a_div : 0) : x_r;
   const int x_off = (x_src * g.lda + x_c * 8) * 2;
   auto dma = [&](int kt, uint8_t* sa, uint8_t* sb) {
     const int k0 = kt * kBK;
-    if constexpr (ROWS) {
+    {
       const int off = (x_ok && k0 + x_kc < K) ? x_off + k0 * 2 : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(x_real ? sa + (kBM / 16 + wave) * 1024 : sSpare), 16,
                                                off, 0, 0, 0);
@@ -561,13 +543,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   const int wrows = mvalid - wm * 64;
   const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(2, (wrows + 31) / 32));
   using F = std::integral_constant<int, 0>;
-  if (ROWS && mvalid > kBM) {  // the extra band holds rows: every regular band is full
-    if constexpr (ROWS) {
-      if (mvalid > kBM + 32)
-        main_loop(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
-      else
-        main_loop(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
-    }
+  if (mvalid > kBM) {  // the extra band holds rows: every regular band is full
+    if (mvalid > kBM + 32)
+      main_loop(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    else
+      main_loop(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
   } else {
     switch (nmb) {
       case 2: main_loop(std::integral_constant<int, 2>{}, F{}); break;
@@ -578,7 +558,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
 
   // ---- epilogue: lane holds output row (lane & 31) of each 32-row block and, per 32-column
   // block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
-  if constexpr (EPI == kEpiStore && SCHED == kSchedRows) {
+  if constexpr (EPI == kEpiStore) {
     // Staged: after the K loop every ring slot is free, so the tile's 256 regular rows go to LDS as
     // bf16 (32-row block j in slot j of sA0..sA3, sB0..sB3, 16 KB each; 16-byte chunk c of row r at
     // chunk c ^ r) and out as whole 512-byte rows, two rows per 1 KB store. Straight from the
@@ -618,7 +598,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     }
     return;
   }
-  if constexpr (EPI == kEpiSwiglu && SCHED == kSchedRows) {
+  if constexpr (EPI == kEpiSwiglu) {
     // Staged as above: h of the 256 regular rows (128 columns, 256-byte rows) goes to LDS (32-row
     // block j in the first 8 KB of slot j; 16-byte chunk c of row r at chunk c ^ (r & 15)) and out as
     // whole rows, four per 1 KB store; the saved g | u (training only) are stored straight
@@ -675,36 +655,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     }
     return;
   }
-  uint16_t* cbase = SCHED == kSchedRows ? g.C : g.C + (int64_t)e * g.c_expert;
+  // SwiGLU backward: dG | dU from the accumulators and the saved g, u (8-byte pieces, read and written)
+  if constexpr (EPI == kEpiSwigluBwd) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int mloc = wm * 64 + mb * 32 + (lane & 31);
-    if (mloc >= mvalid) continue;
-    const int64_t m = m0 + mloc;
-    if constexpr (EPI == kEpiSwiglu) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int col = nt * 128 + wn * 64 + nb * 32 + gq * 8 + (lane >> 5) * 4;
-          if (col >= g.N) continue;
-          float hv[4];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[mb][nb][gq * 4 + qq]) * acc[mb][nb + 2][gq * 4 + qq];
-          *reinterpret_cast<uint2*>(cbase + m * g.ldc + col) =
-              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-          if (g.gu_out) {
-            uint16_t* gs = g.gu_out + m * 2 * g.N;
-            *reinterpret_cast<uint2*>(gs + col) =
-                make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
-                           pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
-            *reinterpret_cast<uint2*>(gs + g.N + col) =
-                make_uint2(pack_bf16x2(acc[mb][nb + 2][gq * 4 + 0], acc[mb][nb + 2][gq * 4 + 1]),
-                           pack_bf16x2(acc[mb][nb + 2][gq * 4 + 2], acc[mb][nb + 2][gq * 4 + 3]));
-          }
-        }
-      }
-    } else {
+    for (int mb = 0; mb < 2; ++mb) {
+      const int mloc = wm * 64 + mb * 32 + (lane & 31);
+      if (mloc >= mvalid) continue;
+      const int64_t m = m0 + mloc;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
@@ -714,12 +671,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
           float v[4];
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mb][nb][gq * 4 + qq];
-          if constexpr (EPI == kEpiSwigluBwd) {
-            store_swiglu_bwd(g, cbase, m, col, v);
-          } else {
-            *reinterpret_cast<uint2*>(cbase + m * g.ldc + col) =
-                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          }
+          store_swiglu_bwd(g, g.C, m, col, v);
         }
       }
     }
@@ -1326,10 +1278,10 @@ __global__ __launch_bounds__(256) void grouped_ffn2_f32_kernel(const float* __re
 // ---------------------------------------------------------------------------------------------
 static inline int round_up8(int64_t v) { return (int)((v + 7) / 8 * 8); }
 
-template <bool A_ROWS, bool B_ROWS, int EPI, int SCHED>
+template <bool A_ROWS, bool B_ROWS, int EPI>
 static void launch_generic(GemmArgs g, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<A_ROWS, B_ROWS, EPI, SCHED>), dim3(round_up8(grid)), dim3(kGemmThreads),
-                     0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<A_ROWS, B_ROWS, EPI>), dim3(round_up8(grid)), dim3(kGemmThreads), 0, s,
+                     g);
 }
 
 // worst-case row tiles over any distribution of N rows among E experts
@@ -1359,7 +1311,7 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
     g.b_expert = (int64_t)H * 2 * I;
     g.b_rows = H;
     g.ntiles_n = (I + 127) / 128;
-    launch_generic<true, false, kEpiSwiglu, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+    launch_generic<true, false, kEpiSwiglu>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
     const int64_t n1 = (int64_t)N * I;
     hipLaunchKernelGGL(grouped_ffn1_f32_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s,
@@ -1386,7 +1338,7 @@ hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int 
     g.b_expert = (int64_t)I * H;
     g.b_rows = I;
     g.ntiles_n = (H + kBN - 1) / kBN;
-    launch_generic<true, false, kEpiStore, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+    launch_generic<true, false, kEpiStore>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
     const int64_t n2 = (int64_t)N * H;
     hipLaunchKernelGGL(grouped_ffn2_f32_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, (const float*)h,
@@ -1415,7 +1367,7 @@ hipError_t launch_gemm_down_bwd(const void* d_y, const void* down, const void* g
   g.b_expert = (int64_t)I * H;
   g.b_rows = I;
   g.ntiles_n = (I + kBN - 1) / kBN;
-  launch_generic<true, true, kEpiSwigluBwd, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+  launch_generic<true, true, kEpiSwigluBwd>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   return hipGetLastError();
 }
 
@@ -1436,7 +1388,7 @@ hipError_t launch_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, int N,
   g.b_expert = (int64_t)H * 2 * I;
   g.b_rows = H;
   g.ntiles_n = (H + kBN - 1) / kBN;
-  launch_generic<true, true, kEpiStore, kSchedRows>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+  launch_generic<true, true, kEpiStore>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   return hipGetLastError();
 }
 
