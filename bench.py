@@ -202,14 +202,15 @@ def main():
                 g.d_shared_down, g.d_shared_gu)))
         stages.append(("router_topk_bwd", lambda: moe.moe_router_topk_bwd(logits, bufs.topk_idx, bufs.topk_w, g.d_w, True,
                                                                           g.d_logits)))
+        # (the buffers are bound when each stage is defined: `side` changes below)
         side = g.d_x_side if sh is not None else None
         if w_gate is not None:
             dst = g.d_x_side2 if sh is not None else g.d_x_side
-            stages.append(("router_logits_bwd", lambda: moe.moe_router_logits_bwd(x, w_gate, g.d_logits, g.d_w_gate,
-                                                                                  d_x_in=side, d_x=dst)))
+            stages.append(("router_logits_bwd", lambda d_in=side, d_out_=dst: moe.moe_router_logits_bwd(
+                x, w_gate, g.d_logits, g.d_w_gate, d_x_in=d_in, d_x=d_out_)))
             side = dst
-        stages.append(("permute_bwd", lambda: moe.moe_permute_bwd(g.d_x_perm, bufs.plan.row_of_slot, T, k,
-                                                                  d_x_add=side, d_x=g.d_x)))
+        stages.append(("permute_bwd", lambda d_add=side: moe.moe_permute_bwd(g.d_x_perm, bufs.plan.row_of_slot, T, k,
+                                                                             d_x_add=d_add, d_x=g.d_x)))
     names = [n for n, _ in stages]
     ns = len(stages)
 
@@ -293,23 +294,23 @@ def main():
     graph_ms = None
     use_graph = args.graph and st2 is None and args.chunks == 1   # multi-stream schedules run eagerly
     if use_graph:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()          # default priority
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        cap_side = torch.cuda.Stream()      # default priority
+        cap_side.wait_stream(stream)
+        with torch.cuda.stream(cap_side):
             step()
-        stream.wait_stream(side)
+        stream.wait_stream(cap_side)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(graph):
             step()
         for _ in range(args.warmup):
-            g.replay()
+            graph.replay()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ev0.record(stream)
         for _ in range(args.steps):
-            g.replay()
+            graph.replay()
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0

@@ -274,6 +274,111 @@ static void launch_small_gemm(const SmallGemm<TA, TB, TC>& p, hipStream_t s) {
   hipLaunchKernelGGL((small_gemm_kernel<TA, TB, TC>), grid, dim3(256), 0, s, p);
 }
 
+// The same products on the matrix cores (used for dW_g, whose K = T is long): v_mfma_f32_32x32x2_f32
+// takes fp32 operands (bf16 inputs widen exactly) and accumulates in fp32. A 64 x 64 tile per workgroup, four waves of 32 x 32; K is
+// staged 32 at a time in a double-buffered LDS tile ([k][m] and [k][n], rows padded to 96 floats so
+// that the two half-waves of a read, one k-row apart, fall on different banks), and the next chunk
+// is loaded into registers while the current one is multiplied.
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+constexpr int kMmK = 32, kMmPitch = 96;
+
+template <typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA, TB, TC> p) {
+  __shared__ float as[2][kMmK][kMmPitch];
+  __shared__ float bs[2][kMmK][kMmPitch];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int nch = (p.K + kMmK - 1) / kMmK;
+  // chunk c -> register set (consecutive threads walk whichever index is contiguous in memory);
+  // two sets, so that a chunk's loads are issued two chunks of multiply-adds before their use
+  float ra[2][8], rb[2][8];
+  auto load = [&](int c, float* pa, float* pb) {
+    const int k0 = c * kMmK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = tid + 256 * j;
+      const int kk = p.a_k == 1 ? i % kMmK : i / 64, mm = p.a_k == 1 ? i / kMmK : i % 64;
+      const int m = m0 + mm, k = k0 + kk;
+      pa[j] = (m < p.M && k < p.K) ? Elem<TA>::load(p.a, (int64_t)m * p.a_m + (int64_t)k * p.a_k) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = tid + 256 * j;
+      const int kk = p.b_k == 1 ? i % kMmK : i / 64, nn = p.b_k == 1 ? i / kMmK : i % 64;
+      const int n = n0 + nn, k = k0 + kk;
+      pb[j] = (n < p.N && k < p.K) ? Elem<TB>::load(p.b, (int64_t)k * p.b_k + (int64_t)n * p.b_n) : 0.0f;
+    }
+  };
+  auto put = [&](int buf, const float* pa, const float* pb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = tid + 256 * j;
+      const int kk = p.a_k == 1 ? i % kMmK : i / 64, mm = p.a_k == 1 ? i / kMmK : i % 64;
+      as[buf][kk][mm] = pa[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = tid + 256 * j;
+      const int kk = p.b_k == 1 ? i % kMmK : i / 64, nn = p.b_k == 1 ? i / kMmK : i % 64;
+      bs[buf][kk][nn] = pb[j];
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+  // lane l supplies A(m = l % 32, k = l / 32) and B(k = l / 32, n = l % 32) of each 2-deep MFMA
+  const int lm = wm * 32 + (lane & 31), ln = wn * 32 + (lane & 31), lk = lane >> 5;
+  // all of the chunk's operands are read before its MFMAs (read one by one ahead of each MFMA, every
+  // multiply waited for the LDS)
+  auto mul = [&](int buf) {
+    float av[kMmK / 2], bv[kMmK / 2];
+#pragma unroll
+    for (int k = 0; k < kMmK; k += 2) {
+      av[k / 2] = as[buf][k + lk][lm];
+      bv[k / 2] = bs[buf][k + lk][ln];
+    }
+#pragma unroll
+    for (int k = 0; k < kMmK / 2; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[k], bv[k], acc, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kMmK, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMmK / 2, 0);
+  };
+  // chunk c sits in LDS buffer c % 2; when it is multiplied, chunk c + 1 waits in register set
+  // (c + 1) % 2 and chunk c + 2 is being loaded into set c % 2 (which held chunk c)
+  load(0, ra[0], rb[0]);
+  if (nch > 1) load(1, ra[1], rb[1]);
+  put(0, ra[0], rb[0]);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 2 < nch) load(c + 2, ra[0], rb[0]);
+    mul(0);
+    if (c + 1 < nch) put(1, ra[1], rb[1]);
+    __syncthreads();
+    if (c + 1 >= nch) break;
+    if (c + 3 < nch) load(c + 3, ra[1], rb[1]);
+    mul(1);
+    if (c + 2 < nch) put(0, ra[0], rb[0]);
+    __syncthreads();
+  }
+  // lane l holds column n = l % 32 and rows (q / 4) * 8 + (l / 32) * 4 + q % 4 of the wave's block
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int m = m0 + wm * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3), n = n0 + ln;
+    if (m < p.M && n < p.N) {
+      const int64_t o = (int64_t)m * p.N + n;
+      const float add = p.c_add ? Elem<TC>::load(p.c_add, o) : 0.0f;
+      Elem<TC>::store(p.c, o, acc[q] + add);
+    }
+  }
+}
+
+template <typename TA, typename TB, typename TC>
+static void launch_small_gemm_mfma(const SmallGemm<TA, TB, TC>& p, hipStream_t s) {
+  dim3 grid((p.N + 63) / 64, (p.M + 63) / 64);
+  hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC>), grid, dim3(256), 0, s, p);
+}
+
 // ---------------------------------------------------------------------------------------------
 template <typename TE>
 static void combine_bwd_t(const void* d_out, const void* y, int T, int H, int k, const int32_t* ros, const float* w,
@@ -351,7 +456,7 @@ static void router_logits_bwd_t(const void* x, const void* w_gate, const float* 
     p.M = H;
     p.N = E;
     p.K = T;
-    launch_small_gemm(p, s);
+    launch_small_gemm_mfma(p, s);
   }
   if (d_x) {
     SmallGemm<float, TE, TE> p{};
@@ -366,7 +471,7 @@ static void router_logits_bwd_t(const void* x, const void* w_gate, const float* 
     p.M = T;
     p.N = H;
     p.K = E;
-    launch_small_gemm(p, s);
+    launch_small_gemm(p, s);  // K = E is short: the vector-ALU tiles measured faster here
   }
 }
 
