@@ -230,7 +230,7 @@ __device__ __forceinline__ void store_extra(const GemmArgs& g, const f32x16& acc
 template <bool A_ROWS, bool B_ROWS, int EPI>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const GemmArgs g) {
   constexpr int TA = kTileAX;
-  constexpr int DPW = kDmaPerWave + 1;  // DMA instructions per wave per step (+1: the extra band)
+  // DMA instructions per wave per step: kDmaPerWave, + 1 in tiles with an extra band (NX > 0)
   // one LDS object per ring slot, so that the compiler can tell a DMA into one slot from reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[TA], sA1[TA], sA2[TA], sA3[TA];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
@@ -331,9 +331,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   const bool x_ok = x_real && x_r < mvalid;
   const int x_src = g.a_slot ? (x_ok ? g.a_slot[m0 + x_r] / g.a_div : 0) : x_r;
   const int x_off = (x_src * g.lda + x_c * 8) * 2;
-  auto dma = [&](int kt, uint8_t* sa, uint8_t* sb) {
+  auto dma = [&](auto x_c, int kt, uint8_t* sa, uint8_t* sb) {
     const int k0 = kt * kBK;
-    {
+    if constexpr (decltype(x_c)::value > 0) {  // band rows (a tile without a band skips the DMA)
       const int off = (x_ok && k0 + x_kc < K) ? x_off + k0 * 2 : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(x_real ? sa + (kBM / 16 + wave) * 1024 : sSpare), 16,
                                                off, 0, 0, 0);
@@ -483,14 +483,15 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     constexpr int NMB = decltype(nmb_c)::value;
     constexpr int NX = decltype(x_c)::value;
     constexpr int X = NX > 0 ? 1 : 0;
+    constexpr int DPW = kDmaPerWave + X;
     if constexpr (NMB == 0) {
-      dma(kt + 3, pa, pb);
+      dma(x_c, kt + 3, pa, pb);
     } else if constexpr (NX == 2) {
       // two band blocks: the sub-steps one after the other, so that one set of fragments is live
       // (both sets with the band's accumulators would not fit in the register budget)
       Frags f;
       read_frags(nmb_c, x_c, sa, sb, 0, f);
-      dma(kt + 3, pa, pb);
+      dma(x_c, kt + 3, pa, pb);
       mfmas(nmb_c, x_c, f, acc_x);
       read_frags(nmb_c, x_c, sa, sb, 1, f);
       mfmas(nmb_c, x_c, f, acc_x);
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       Frags f0, f1;
       read_frags(nmb_c, x_c, sa, sb, 0, f0);
       read_frags(nmb_c, x_c, sa, sb, 1, f1);
-      dma(kt + 3, pa, pb);
+      dma(x_c, kt + 3, pa, pb);
       mfmas(nmb_c, x_c, f0, acc_x);
       mfmas(nmb_c, x_c, f1, acc_x);
       constexpr int R = (B_ROWS ? 4 : 8) + (A_ROWS ? 1 : 2) * NMB + NX + X * (B_ROWS ? 1 : 2);  // LDS reads per sub-step
@@ -525,9 +526,10 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     for (int xb = 0; xb < 2; ++xb)
 #pragma unroll
       for (int qq = 0; qq < 16; ++qq) acc_x[xb][qq] = 0.0f;
-    dma(0, sA0, sB0);
-    dma(1, sA1, sB1);
-    dma(2, sA2, sB2);
+    constexpr int DPW = kDmaPerWave + (decltype(x_c)::value > 0 ? 1 : 0);
+    dma(x_c, 0, sA0, sB0);
+    dma(x_c, 1, sA1, sB1);
+    dma(x_c, 2, sA2, sB2);
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * DPW) : "memory");
     for (int kt = 0; kt < KT4; kt += kStages) {
       step(nmb_c, x_c, acc_x, kt + 0, sA0, sB0, sA3, sB3);
