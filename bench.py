@@ -361,7 +361,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gu_flops / t_gu / 1e12, 1), "peak": peak_tf, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = load_traffic(wl.name, "gathered" if gather else "x_perm")
-    roof["kernel"] = "grouped_gemm_bf16_kernel<true, false, 0, 0> (gate_up + SwiGLU)"
+    roof["kernel"] = "grouped_gemm_bf16_kernel<true, false, 0> (gate_up + SwiGLU)"
     roof["algorithmic_bytes"] = gu_bytes
     roof["algorithmic_flops"] = gu_flops
     roof["avg_launch_us"] = round(t_gu * 1e6, 2)
