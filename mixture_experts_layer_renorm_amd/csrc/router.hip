@@ -20,9 +20,16 @@ namespace moe {
 // [HB x 8*EQ] are loaded into registers DEPTH chunks ahead (the loads of x come from HBM, so
 // their latency has to be covered by more than one chunk of arithmetic), widened to fp32 once and
 // stored to a double-buffered LDS tile. A lane then reads four h of its own token with one 16-byte
-// read (row pitch padded by 4 floats, so 16 consecutive rows cover all banks); the wave's weights
-// reach every lane through DPP row broadcasts (fmac4 below).
+// read (row pitch padded by 4 floats, so 16 consecutive rows cover all banks).
+//
+// Waves 0-3 run their chains on the vector ALUs: the wave's weights reach every lane through DPP
+// row broadcasts (fmac4 below). Waves 4-7 run theirs on the matrix cores: one
+// v_mfma_f32_4x4x1_16b_f32 per h takes x[token][h] from each lane and W_g[h][e] for the four experts
+// of a quad, and adds to each of its 16 blocks of 4 tokens x 4 experts the products, one fused
+// multiply-add per element onto the accumulator (the operation fmaf performs, measured bit-identical
+// to it, subnormals included). The matrix and vector pipelines of a SIMD run at the same time.
 constexpr int kLogitWaves = 8;
+constexpr int kRd = 3;  // groups of four h whose LDS reads run ahead of the arithmetic
 constexpr int kLogitTok = kWave;  // tokens per workgroup
 
 template <typename TIn>
@@ -133,6 +140,8 @@ __device__ __forceinline__ void fmac4<8>(float* acc, const float* w, const float
                : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3]), [a4] "+v"(acc[4]), [a5] "+v"(acc[5]), [a6] "+v"(acc[6]), [a7] "+v"(acc[7])
                : [w0] "v"(w[0]), [w1] "v"(w[1]), [x0] "v"(x.x), [x1] "v"(x.y), [x2] "v"(x.z), [x3] "v"(x.w));
 }
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename TIn, int EQ>
 struct LogitTile {
@@ -249,23 +258,69 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
     if (nh == HB) {
       // four h at a time: the lane's x for them (one 16-byte read) and the wave's weights for them
       // (16 values per register, replicated over the four 16-lane rows), consumed by fmac with a
-      // row_newbcast operand; the reads of the next four h are issued before this group's fmacs
-      float4 xv[2];
-      float wv[2][EQ / 4];
+      // row_newbcast operand; the reads run kRd groups of four h ahead of the fmacs
+      float4 xv[kRd + 1];
+      float wv[kRd + 1][EQ / 4];
       auto rd = [&](int h4, int slot) {
         xv[slot] = *reinterpret_cast<const float4*>(xl + h4);
 #pragma unroll
         for (int r = 0; r < EQ / 4; ++r) wv[slot][r] = ws[buf][h4 + r * (16 / EQ) + wrow][wave * EQ + wcol];
       };
-      rd(0, 0);
+#pragma unroll
+      for (int i = 0; i < kRd; ++i) rd(4 * i, i);
 #pragma unroll
       for (int h4 = 0; h4 < HB; h4 += 4) {
-        const int cs = (h4 / 4) & 1;
-        if (h4 + 4 < HB) rd(h4 + 4, cs ^ 1);
+        const int cs = (h4 / 4) % (kRd + 1);
+        if (h4 + 4 * kRd < HB) rd(h4 + 4 * kRd, (cs + kRd) % (kRd + 1));
         fmac4<EQ>(acc, wv[cs], xv[cs]);
       }
     } else {
       for (int hh = 0; hh < nh; ++hh) fma_h(buf, hh, xl[hh]);
+    }
+  };
+
+  // matrix-core waves: quad q of the wave's experts accumulates in macc[q]; lane l holds, in element
+  // m, the logit of token 4 * (l / 4) + m and expert 4 q + l % 4 of the wave
+  const bool mx = wave >= kLogitWaves / 2;
+  f32x4_t macc[EQ / 4];
+#pragma unroll
+  for (int q = 0; q < EQ / 4; ++q) macc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int wc = wave * EQ + (lane & 3);
+  auto compute_mx = [&](int c) {
+    const int buf = c & 1;
+    const int nh = min(HB, H - c * HB);
+    const float* xl = &xs[buf][lane][0];
+    if (nh == HB) {
+      // four h at a time, read kRd groups ahead
+      float4 xv[kRd + 1];
+      float wv[kRd + 1][4][EQ / 4];
+      auto rd = [&](int h4, int slot) {
+        xv[slot] = *reinterpret_cast<const float4*>(xl + h4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < EQ / 4; ++q) wv[slot][i][q] = ws[buf][h4 + i][wc + 4 * q];
+      };
+#pragma unroll
+      for (int i = 0; i < kRd; ++i) rd(4 * i, i);
+#pragma unroll
+      for (int h4 = 0; h4 < HB; h4 += 4) {
+        const int cs = (h4 / 4) % (kRd + 1);
+        if (h4 + 4 * kRd < HB) rd(h4 + 4 * kRd, (cs + kRd) % (kRd + 1));
+        const float xa[4] = {xv[cs].x, xv[cs].y, xv[cs].z, xv[cs].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < EQ / 4; ++q)
+            macc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[i], wv[cs][i][q], macc[q], 0, 0, 0);
+      }
+    } else {
+      for (int hh = 0; hh < nh; ++hh) {
+        const float xa = xl[hh];
+#pragma unroll
+        for (int q = 0; q < EQ / 4; ++q)
+          macc[q] = __builtin_amdgcn_mfma_f32_4x4x1f32(xa, ws[buf][hh][wc + 4 * q], macc[q], 0, 0, 0);
+      }
     }
   };
 
@@ -282,11 +337,24 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
         store(c & 1, rx[r], rw[r]);
         __syncthreads();
         if (c + DEPTH < nch) load(c + DEPTH, rx[r], rw[r]);
-        compute(c);
+        if (mx)
+          compute_mx(c);
+        else
+          compute(c);
       }
     }
   }
 
+  if (mx) {
+#pragma unroll
+    for (int q = 0; q < EQ / 4; ++q)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int t = t0 + (lane & ~3) + m, e = e0 + wave * EQ + 4 * q + (lane & 3);
+        if (t < T && e < E) logits[(int64_t)t * E + e] = macc[q][m];
+      }
+    return;
+  }
   const int t = t0 + lane;
   if (t < T) {
     float* out = logits + (int64_t)t * E + e0 + wave * EQ;

@@ -43,6 +43,26 @@ def test_router_logits_bit_exact(T, H, E, dtype):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("T,H,E,dtype", [(4096, 72, 256, "bf16"), (16384, 40, 64, "f32")])
+def test_router_logits_eight_chains_per_lane(T, H, E, dtype):
+    # shapes with at least 256 workgroups of 64 experts: the launch that gives each lane eight chains
+    x = normal((T, H), 1.0, (953, T, H), dtype)
+    w = normal((H, E), 0.02, (954, H, E), dtype)
+    got = host(moe.moe_router_logits(dev(x), dev(w)))
+    assert np.array_equal(got.view(np.uint32), oracle.router_logits(x, w).view(np.uint32))
+
+
+def test_router_logits_subnormal_products():
+    # |x w| ~ 1e-40: every product and most partial sums are subnormal, on both kinds of waves
+    T, H, E = 130, 200, 40
+    x = normal((T, H), 1e-20, (955, T, H), "f32")
+    w = normal((H, E), 1e-20, (956, H, E), "f32")
+    want = oracle.router_logits(x, w)
+    assert np.count_nonzero((want != 0) & (np.abs(want) < np.finfo(np.float32).tiny)) > T * E // 2
+    got = host(moe.moe_router_logits(dev(x), dev(w)))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
 @pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1000, 128, 8), (77, 256, 8), (50, 1024, 32), (10, 5, 5),
                                    (33, 64, 1), (20, 3, 3), (129, 100, 7)])
 @pytest.mark.parametrize("renorm", [True, False])
