@@ -23,7 +23,7 @@ namespace moe {
 // read (row pitch padded by 4 floats, so 16 consecutive rows cover all banks).
 //
 // Waves 0-3 run their chains on the vector ALUs: the wave's weights reach every lane through DPP
-// row broadcasts (fmac4 below). Waves 4-7 run theirs on the matrix cores: one
+// row broadcasts (fmac4 below). With four chains per lane, waves 4-7 run theirs on the matrix cores: one
 // v_mfma_f32_4x4x1_16b_f32 per h takes x[token][h] from each lane and W_g[h][e] for the four experts
 // of a quad, and adds to each of its 16 blocks of 4 tokens x 4 experts the products, one fused
 // multiply-add per element onto the accumulator (the operation fmaf performs, measured bit-identical
@@ -281,7 +281,9 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
 
   // matrix-core waves: quad q of the wave's experts accumulates in macc[q]; lane l holds, in element
   // m, the logit of token 4 * (l / 4) + m and expert 4 q + l % 4 of the wave
-  const bool mx = wave >= kLogitWaves / 2;
+  // (with eight chains per lane the matrix-core waves would read twice the weights per h and the
+  // kernel becomes bound by LDS reads: measured slower, so that launch keeps every wave on the vector ALUs)
+  const bool mx = EQ == 4 && wave >= kLogitWaves / 2;
   f32x4_t macc[EQ / 4];
 #pragma unroll
   for (int q = 0; q < EQ / 4; ++q) macc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
