@@ -19,11 +19,12 @@
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16, fp32 accumulation. A workgroup of 8 waves (2 per SIMD)
 // computes a 256 x 256 tile; each wave 64 x 128. Both operand tiles go global -> LDS by 16-byte
-// buffer DMA into a 4-stage ring of 32-deep K steps. An operand whose K dimension is contiguous in
-// memory is staged as a "row tile" ([256 rows][32 k], 64-byte rows) and read with ds_read_b128; an
-// operand whose M or N dimension is contiguous is staged in its natural layout as a "k-row tile"
-// ([32 k][256 cols], 512-byte rows) and read with the LDS transpose read ds_read_b64_tr_b16, so no
-// operand is ever repacked. The MFMA takes the B fragment first, so a lane ends up holding four
+// buffer DMA in 32-deep K steps. An operand whose K dimension is contiguous in memory is staged as
+// a "row tile" ([rows][k], read with ds_read_b128); an operand whose M or N dimension is contiguous
+// is staged in its natural layout as a "k-row tile" ([32 k][256 cols], 512-byte rows) and read with
+// the LDS transpose read ds_read_b64_tr_b16, so no operand is ever repacked. In the row-grouped
+// products the grouped operand A is loaded two K steps at a time (128-byte row pieces) into two
+// alternating stages and the weights B one step at a time into a 4-slot ring. The MFMA takes the B fragment first, so a lane ends up holding four
 // consecutive output columns of one row; the forward epilogues stage the tile through the (then
 // free) LDS ring and store whole rows.
 #include <algorithm>
@@ -52,9 +53,7 @@ constexpr int kGemmThreads = 512;   // 8 waves (2 per SIMD): 4 along M (64 rows 
 constexpr int kTileA = kBM * kBK * 2;  // 16 KB per operand tile, either layout
 constexpr int kTileB = kBK * kBN * 2;
 constexpr int kWaves = kGemmThreads / 64;
-constexpr int kDmaPerWave = (kTileA + kTileB) / 1024 / kWaves;  // 1 KB per wave-wide DMA instruction
-constexpr int kDmaA = kTileA / 1024 / kWaves;  // DMA instructions per wave per step, operand A
-constexpr int kDmaB = kTileB / 1024 / kWaves;  // and operand B
+constexpr int kDmaB = kTileB / 1024 / kWaves;  // DMA instructions (1 KB each) per wave per step, operand B
 constexpr int kGemmMaxE = 1024;
 // Row-grouped products: a tile holds up to kBMX = 320 rows, the regular 256 plus an extra band of
 // up to 64 rows, so an expert with 257..320 rows (E = 128, k = 8, T = 4096 gives counts of 256 with
@@ -63,7 +62,13 @@ constexpr int kGemmMaxE = 1024;
 // extra band is one or two 32-row blocks (as many as the tile's rows need), each spread over the
 // eight waves against a 32-column slice per wave (16 gate + 16 up output columns with SwiGLU).
 constexpr int kBMX = kBM + 64;
-constexpr int kTileAX = kBMX * kBK * 2;   // 20 KB: 20 DMA instructions, 2 per wave + 1 for waves 0-3
+// The row-grouped operand A is staged two K steps at a time: [320 rows][64 k], 128-byte rows, so every
+// DMA lane group fetches whole 128-byte lines of a row (one request per line instead of two 64-byte
+// halves a step apart). Two such stages (40 KB each) alternate; stage s + 1 is loaded while stage s
+// is read, so A arrives two K steps ahead and B, from HBM, keeps its three-step lead in a 4-slot ring.
+constexpr int kBK2 = 2 * kBK;                              // K depth of one A stage
+constexpr int kTileA2 = kBMX * kBK2 * 2;                   // 40 KB per A stage
+constexpr int kDmaA2 = kBM * kBK2 * 2 / 1024 / kWaves;     // 4 DMA instructions per wave per A stage (+1 band)
 
 // LDS swizzles, applied when choosing which global chunk each DMA lane fetches. They keep the
 // fragment reads free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
@@ -76,6 +81,12 @@ constexpr int kTileAX = kBMX * kBK * 2;   // 20 KB: 20 DMA instructions, 2 per w
 //    16-byte pair stays adjacent and the gate / up halves of a forward GEMM-1 row never mix.
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ __forceinline__ int swz_b(int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); }
+// A stage (128-byte rows): chunk c of row r lives at chunk c ^ h(r), h(r) = (r & 7) ^ ((r >> 3) & 1). Eight
+// consecutive rows (one 128-byte LDS cycle) get eight distinct chunks; of sixteen (one 256-byte cycle),
+// the even and the odd rows each get eight distinct chunks, and the two parities sit in opposite halves
+// of the 256 bytes. Chunks 0-3 (the stage's first K step) map to 0-3 or 4-7 as a block per row, so the
+// second step's address is the first's with bit 6 flipped.
+__device__ __forceinline__ int swz_a2(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // sigmoid with the hardware reciprocal (1 ulp) instead of an IEEE division (about ten instructions
 // each): the results are rounded to bf16, and the division sequence was most of the epilogue's time
@@ -229,12 +240,11 @@ __device__ __forceinline__ void store_extra(const GemmArgs& g, const f32x16& acc
 // B_ROWS: B is a row tile (K contiguous) - else a k-row tile (N contiguous).
 template <bool A_ROWS, bool B_ROWS, int EPI>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const GemmArgs g) {
-  constexpr int TA = kTileAX;
-  // DMA instructions per wave per step: kDmaPerWave, + 1 in tiles with an extra band (NX > 0)
-  // one LDS object per ring slot, so that the compiler can tell a DMA into one slot from reads of another
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[TA], sA1[TA], sA2[TA], sA3[TA];
+  static_assert(A_ROWS, "the row-grouped operand is staged as a row tile");
+  // one LDS object per A stage and per B ring slot, so that the compiler can tell a DMA into one
+  // buffer from reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA2], sA1[kTileA2];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sSpare[1024];
   __shared__ int s_pref[kGemmMaxE + 1];
   __shared__ int s_wtot[kGemmThreads / kWave];
   __shared__ int s_e[3];  // the tile's expert, its first row and its row count
@@ -274,28 +284,25 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, b_records, kBufferWord3);
 
   // ---- DMA lanes (offsets in bytes from the descriptor base, for k0 = 0)
-  // Row tile: instruction i fills rows (kDma w + i) * 16 .. +16, four lanes (16-byte chunks) per row.
-  // k-row tile: instruction i fills k-rows (kDma w + i) * 2 .. +2, 32 lanes per row.
-  int a_off[kDmaA], b_off[kDmaB];
-  bool a_ok[kDmaA], b_ok[kDmaB];
-  int a_kc[kDmaA], b_kc[kDmaB];  // row tiles: k offset of the lane's chunk (for the K tail)
+  // A stage: instruction i fills rows (kDmaA2 w + i) * 8 .. +8, eight lanes (16-byte chunks) per row.
+  // B row tile: instruction i fills rows (kDmaB w + i) * 16 .. +16, four lanes per row.
+  // B k-row tile: instruction i fills k-rows (kDmaB w + i) * 2 .. +2, 32 lanes per row.
+  // A: a row past the tile gets an offset at or past the descriptor's end, so every stage loads zeros
+  // for it (rows of the grouped operand past the tile are past their descriptor already). The lane's
+  // chunk depends only on the lane and on i % 2 (rows 8 i .. 8 i + 7 share h(r) up to bit 0).
+  int a_off[kDmaA2], b_off[kDmaB];
+  bool b_ok[kDmaB];
+  int b_kc[kDmaB];  // row tiles: k offset of the lane's chunk (for the K tail)
+  const int a_c0 = (lane & 7) ^ swz_a2(lane >> 3);
+  const int a_kc[2] = {a_c0 * 8, (a_c0 ^ 1) * 8};
 #pragma unroll
-  for (int i = 0; i < kDmaA; ++i) {
-    if constexpr (A_ROWS) {
-      const int r = (wave * kDmaA + i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swz_a(r);
-      a_kc[i] = c * 8;
-      a_ok[i] = r < mvalid;
-      const int src = g.a_slot ? (a_ok[i] ? g.a_slot[m0 + r] / g.a_div : 0) : r;
-      a_off[i] = (src * g.lda + c * 8) * 2;
-    } else {
-      const int kr = (wave * kDmaA + i) * 2 + (lane >> 5);
-      const int cb = (lane & 31) ^ swz_b(kr);
-      const int col = m0 + cb * 8;
-      a_kc[i] = 0;
-      a_ok[i] = col < g.M;
-      a_off[i] = (kr * g.lda + (a_ok[i] ? col : 0)) * 2;
-    }
+  for (int i = 0; i < kDmaA2; ++i) {
+    const int r = (wave * kDmaA2 + i) * 8 + (lane >> 3);
+    const int c = a_c0 ^ (i & 1);
+    if (g.a_slot)
+      a_off[i] = r < mvalid ? (g.a_slot[m0 + r] / g.a_div * g.lda + c * 8) * 2 : a_records;
+    else
+      a_off[i] = (r * g.lda + c * 8) * 2;
   }
 #pragma unroll
   for (int i = 0; i < kDmaB; ++i) {
@@ -323,30 +330,30 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
       b_off[i] = (kr * g.ldb + col) * 2;
     }
   }
-  // extra-band rows 256 + 16 w .. + 15 for waves 0, 1 (the other waves aim a spare kilobyte)
-  const bool x_real = wave < (kTileAX - kTileA) / 1024;
-  const int x_r = kBM + wave * 16 + (lane >> 2);
-  const int x_c = (lane & 3) ^ swz_a(x_r);
-  const int x_kc = x_c * 8;
-  const bool x_ok = x_real && x_r < mvalid;
-  const int x_src = g.a_slot ? (x_ok ? g.a_slot[m0 + x_r] / g.a_div : 0) : x_r;
-  const int x_off = (x_src * g.lda + x_c * 8) * 2;
-  auto dma = [&](auto x_c, int kt, uint8_t* sa, uint8_t* sb) {
-    const int k0 = kt * kBK;
-    if constexpr (decltype(x_c)::value > 0) {  // band rows (a tile without a band skips the DMA)
-      const int off = (x_ok && k0 + x_kc < K) ? x_off + k0 * 2 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(x_real ? sa + (kBM / 16 + wave) * 1024 : sSpare), 16,
-                                               off, 0, 0, 0);
+  // extra-band rows 256 + 8 w .. + 7 of an A stage: one DMA instruction per wave
+  const int x_r = kBM + wave * 8 + (lane >> 3);
+  const int xch = (lane & 7) ^ swz_a2(x_r);
+  const int x_kc = xch * 8;
+  const int x_off = !g.a_slot ? (x_r * g.lda + xch * 8) * 2
+                    : x_r < mvalid ? (g.a_slot[m0 + x_r] / g.a_div * g.lda + xch * 8) * 2 : a_records;
+  // A stage st (K 64 st .. 64 st + 63 of the tile's rows) into buffer sa; the band rows only in tiles
+  // that have them
+  auto dma_a = [&](auto x_c, int st, uint8_t* sa) {
+    const int k0 = st * kBK2;
+    if constexpr (decltype(x_c)::value > 0) {
+      const int off = k0 + x_kc < K ? (int)((uint32_t)x_off + (uint32_t)(k0 * 2)) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + kBM * kBK2 * 2 + wave * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < kDmaA; ++i) {
-      int off;
-      if constexpr (A_ROWS)
-        off = (a_ok[i] && k0 + a_kc[i] < K) ? a_off[i] + k0 * 2 : kOutOfRange;
-      else
-        off = a_ok[i] ? a_off[i] + k0 * g.lda * 2 : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + (wave * kDmaA + i) * 1024), 16, off, 0, 0, 0);
+    for (int i = 0; i < kDmaA2; ++i) {
+      // unsigned: a missing gathered row's offset is the descriptor's size, which k0 may push past 2^31
+      const int off = k0 + a_kc[i & 1] < K ? (int)((uint32_t)a_off[i] + (uint32_t)(k0 * 2)) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sa + (wave * kDmaA2 + i) * 1024), 16, off, 0, 0, 0);
     }
+  };
+  // B step kt (K 32 kt .. 32 kt + 31) into ring slot sb
+  auto dma_b = [&](int kt, uint8_t* sb) {
+    const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
       int off;
@@ -358,7 +365,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     }
   };
 
-  // ---- fragment addresses. A block mb: rows (or k-row-tile columns) wm*64 + mb*32 + (lane & 31).
+  // ---- fragment addresses. A block mb: rows wm*64 + mb*32 + (lane & 31), one ds_read_b128 at
+  // k = kk*16 + (lane/32)*8 of the stage's first K step (the second step: address bit 6 flipped).
   // B block nb: 32 tile columns from bcol[nb]. Row tile: one ds_read_b128 at k = kk*16 + (lane/32)*8.
   // k-row tile: two transpose reads at k = kk*16 + (lane/32)*8 + {0..3, 4..7}.
   int bcol[4];
@@ -370,6 +378,10 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     const int c = kk * 2 + (lane >> 5);
     return r * 64 + ((c ^ swz_a(r)) << 4);
   };
+  auto arow_rd = [&](int r, int kk) {
+    const int c = kk * 2 + (lane >> 5);
+    return r * (kBK2 * 2) + ((c ^ swz_a2(r)) << 4);
+  };
   auto krow_rd = [&](int col32, int kk, int ri) {
     const int kr = kk * 16 + (q >> 1) * 8 + ri * 4 + (sl >> 2);
     const int col = col32 + (q & 1) * 16 + 4 * (sl & 3);
@@ -380,13 +392,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      if constexpr (A_ROWS) {
-        a_rd[kk][mb][0] = row_rd(wm * 64 + mb * 32 + (lane & 31), kk);
-        a_rd[kk][mb][1] = 0;
-      } else {
-        a_rd[kk][mb][0] = krow_rd(wm * 64 + mb * 32, 0, 0);  // + kk * 8192 at the read
-        a_rd[kk][mb][1] = 0;
-      }
+      a_rd[kk][mb][0] = arow_rd(wm * 64 + mb * 32 + (lane & 31), kk);
+      a_rd[kk][mb][1] = 0;
     }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   int xa_rd[2], xb_rd[2][2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    xa_rd[kk] = row_rd(kBM + (lane & 31), kk);
+    xa_rd[kk] = arow_rd(kBM + (lane & 31), kk);
     if constexpr (B_ROWS) {
       xb_rd[kk][0] = row_rd(wn * 128 + wm * 32 + (lane & 31), kk);
       xb_rd[kk][1] = 0;
@@ -449,16 +456,18 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   // NMB = number of this wave's 32-row blocks that hold rows (0..2, wave-uniform); NX = number of
   // extra-band blocks of the tile (0..2). Waves of one tile may run different NMB variants: every
   // variant issues the same DMAs and barriers.
-  auto read_frags = [&](auto nmb_c, auto nx_c, const uint8_t* sa, const uint8_t* sb, int kk, Frags& f) {
+  // AX: 0 in the first K step of an A stage, 64 (address bit 6) in the second
+  auto read_frags = [&](auto nmb_c, auto nx_c, const uint8_t* sa, const uint8_t* sb, int kk, int AX, Frags& f) {
     constexpr int NMB = decltype(nmb_c)::value;
     constexpr int NX = decltype(nx_c)::value;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag(sb, b_rd[kk][nb], B_ROWS, kk);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = frag(sa, a_rd[kk][mb], A_ROWS, kk);
+    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(sa + (a_rd[kk][mb][0] ^ AX));
     if constexpr (NX > 0) {
 #pragma unroll
-      for (int xb = 0; xb < NX; ++xb) f.xa[xb] = frag(sa + xb * 32 * 64, &xa_rd[kk], true, kk);
+      for (int xb = 0; xb < NX; ++xb)
+        f.xa[xb] = *reinterpret_cast<const bf16x8*>(sa + xb * 32 * kBK2 * 2 + (xa_rd[kk] ^ AX));
       f.xb = frag(sb, xb_rd[kk], B_ROWS, kk);
     }
   };
@@ -474,32 +483,41 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     for (int xb = 0; xb < NX; ++xb)
       acc_x[xb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb, f.xa[xb], acc_x[xb], 0, 0, 0);
   };
-  // One step: prefetch step kt+3 into the slot freed by step kt-1, compute step kt, then wait for
-  // this wave's DMA of step kt+1 (the two later steps stay in flight) and meet at the barrier.
-  // The scheduler is told to interleave: the first sub-step's fragment reads, then MFMAs with the
-  // DMA issues and the second sub-step's fragment reads threaded between them.
-  auto step = [&](auto nmb_c, auto x_c, f32x16* acc_x, int kt, const uint8_t* sa, const uint8_t* sb, uint8_t* pa,
-                  uint8_t* pb) {
+  // One step kt (P = kt % 2: first or second K step of the A stage in sa): at P = 0 load the next A
+  // stage into pa, the buffer every wave finished with at the last barrier; load B step kt + 3 into
+  // the slot freed by step kt - 1; compute step kt; then wait for this wave's DMAs of step kt + 1
+  // (after P = 1 that includes the A stage issued one step earlier: two steps of lead for A, three
+  // for B) and meet at the barrier. The scheduler is told to interleave: the first sub-step's
+  // fragment reads, then MFMAs with the DMA issues and the second sub-step's reads between them.
+  auto step = [&](auto nmb_c, auto x_c, auto p_c, f32x16* acc_x, int kt, const uint8_t* sa, const uint8_t* sb,
+                  uint8_t* pa, uint8_t* pb) {
     constexpr int NMB = decltype(nmb_c)::value;
     constexpr int NX = decltype(x_c)::value;
+    constexpr int P = decltype(p_c)::value;
     constexpr int X = NX > 0 ? 1 : 0;
-    constexpr int DPW = kDmaPerWave + X;
+    constexpr int DA = kDmaA2 + X;                    // DMAs of an A stage
+    constexpr int DPW = (P == 0 ? DA : 0) + kDmaB;    // DMAs issued in this step
+    constexpr int AX = P * 64;
+    auto issue = [&]() {
+      if constexpr (P == 0) dma_a(x_c, kt / 2 + 1, pa);
+      dma_b(kt + 3, pb);
+    };
     if constexpr (NMB == 0) {
-      dma(x_c, kt + 3, pa, pb);
-    } else if constexpr (NX == 2) {
-      // two band blocks: the sub-steps one after the other, so that one set of fragments is live
-      // (both sets with the band's accumulators would not fit in the register budget)
+      issue();
+    } else if constexpr (NX > 0) {
+      // band blocks: the sub-steps one after the other, so that one set of fragments is live
+      // (both sets with the band's accumulators do not fit in the register budget)
       Frags f;
-      read_frags(nmb_c, x_c, sa, sb, 0, f);
-      dma(x_c, kt + 3, pa, pb);
+      read_frags(nmb_c, x_c, sa, sb, 0, AX, f);
+      issue();
       mfmas(nmb_c, x_c, f, acc_x);
-      read_frags(nmb_c, x_c, sa, sb, 1, f);
+      read_frags(nmb_c, x_c, sa, sb, 1, AX, f);
       mfmas(nmb_c, x_c, f, acc_x);
     } else {
       Frags f0, f1;
-      read_frags(nmb_c, x_c, sa, sb, 0, f0);
-      read_frags(nmb_c, x_c, sa, sb, 1, f1);
-      dma(x_c, kt + 3, pa, pb);
+      read_frags(nmb_c, x_c, sa, sb, 0, AX, f0);
+      read_frags(nmb_c, x_c, sa, sb, 1, AX, f1);
+      issue();
       mfmas(nmb_c, x_c, f0, acc_x);
       mfmas(nmb_c, x_c, f1, acc_x);
       constexpr int R = (B_ROWS ? 4 : 8) + (A_ROWS ? 1 : 2) * NMB + NX + X * (B_ROWS ? 1 : 2);  // LDS reads per sub-step
@@ -512,9 +530,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, R > 2 * DPW ? R - 2 * DPW : 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * M - DPW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * M > DPW ? 2 * M - DPW : 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * DPW) : "memory");
+    // ops issued after the B DMA of step kt + 1: P = 0: B kt + 2, then this step's A stage and B kt + 3;
+    // P = 1: B kt + 2 and B kt + 3 (the A stage of step kt + 1 went out just before B kt + 2)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(P == 0 ? 2 * kDmaB + DA : 2 * kDmaB) : "memory");
   };
   auto main_loop = [&](auto nmb_c, auto x_c) {
     // Steps past the last real one load zeros (out-of-range offsets) and add nothing, so the step
@@ -526,16 +546,18 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     for (int xb = 0; xb < 2; ++xb)
 #pragma unroll
       for (int qq = 0; qq < 16; ++qq) acc_x[xb][qq] = 0.0f;
-    constexpr int DPW = kDmaPerWave + (decltype(x_c)::value > 0 ? 1 : 0);
-    dma(x_c, 0, sA0, sB0);
-    dma(x_c, 1, sA1, sB1);
-    dma(x_c, 2, sA2, sB2);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * DPW) : "memory");
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    dma_a(x_c, 0, sA0);
+    dma_b(0, sB0);
+    dma_b(1, sB1);
+    dma_b(2, sB2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaB) : "memory");  // A stage 0 and B step 0
     for (int kt = 0; kt < KT4; kt += kStages) {
-      step(nmb_c, x_c, acc_x, kt + 0, sA0, sB0, sA3, sB3);
-      step(nmb_c, x_c, acc_x, kt + 1, sA1, sB1, sA0, sB0);
-      step(nmb_c, x_c, acc_x, kt + 2, sA2, sB2, sA1, sB1);
-      step(nmb_c, x_c, acc_x, kt + 3, sA3, sB3, sA2, sB2);
+      step(nmb_c, x_c, P0{}, acc_x, kt + 0, sA0, sB0, sA1, sB3);
+      step(nmb_c, x_c, P1{}, acc_x, kt + 1, sA0, sB1, nullptr, sB0);
+      step(nmb_c, x_c, P0{}, acc_x, kt + 2, sA1, sB2, sA0, sB1);
+      step(nmb_c, x_c, P1{}, acc_x, kt + 3, sA1, sB3, nullptr, sB2);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
@@ -562,14 +584,14 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   // block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
   if constexpr (EPI == kEpiStore) {
     // Staged: after the K loop every ring slot is free, so the tile's 256 regular rows go to LDS as
-    // bf16 (32-row block j in slot j of sA0..sA3, sB0..sB3, 16 KB each; 16-byte chunk c of row r at
+    // bf16 (32-row block j in 16 KB block j: the halves of sA0 and sA1, then sB0..sB3; 16-byte chunk c of row r at
     // chunk c ^ r) and out as whole 512-byte rows, two rows per 1 KB store. Straight from the
     // accumulators each 8-byte-per-lane store touches 32 rows, and with every CU reaching its
     // epilogue at about the same time that was a quarter of the down product's tile time. The
     // stores are plain: the combine reads y right after, partly from the last-level cache (with
     // non-temporal stores the down product was 5 us faster and the combine 9 us slower).
     auto blk = [&](int j) -> uint8_t* {
-      return j == 0 ? sA0 : j == 1 ? sA1 : j == 2 ? sA2 : j == 3 ? sA3 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
+      return j == 0 ? sA0 : j == 1 ? sA0 + 16384 : j == 2 ? sA1 : j == 3 ? sA1 + 16384 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
     };
     asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
     const int lr = lane & 31;
@@ -605,7 +627,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     // block j in the first 8 KB of slot j; 16-byte chunk c of row r at chunk c ^ (r & 15)) and out as
     // whole rows, four per 1 KB store; the saved g | u (training only) are stored straight
     auto blk = [&](int j) -> uint8_t* {
-      return j == 0 ? sA0 : j == 1 ? sA1 : j == 2 ? sA2 : j == 3 ? sA3 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
+      return j == 0 ? sA0 : j == 1 ? sA0 + 16384 : j == 2 ? sA1 : j == 3 ? sA1 + 16384 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
     };
     asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
     const int lr = lane & 31;
