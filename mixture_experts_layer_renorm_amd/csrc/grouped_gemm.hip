@@ -24,9 +24,9 @@
 // is staged in its natural layout as a "k-row tile" ([32 k][256 cols], 512-byte rows) and read with
 // the LDS transpose read ds_read_b64_tr_b16, so no operand is ever repacked. In the row-grouped
 // products the grouped operand A is loaded two K steps at a time (128-byte row pieces) into two
-// alternating stages and the weights B one step at a time into a 4-slot ring. The MFMA takes the B fragment first, so a lane ends up holding four
-// consecutive output columns of one row; the forward epilogues stage the tile through the (then
-// free) LDS ring and store whole rows.
+// alternating stages and the weights B one step at a time into a 4-slot ring. The MFMA takes the
+// B fragment first, so a lane ends up holding four consecutive output columns of one row; the
+// forward epilogues stage the tile through the (then free) operand buffers and store whole rows.
 #include <algorithm>
 #include <type_traits>
 
@@ -583,9 +583,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   // ---- epilogue: lane holds output row (lane & 31) of each 32-row block and, per 32-column
   // block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for accumulator element q
   if constexpr (EPI == kEpiStore) {
-    // Staged: after the K loop every ring slot is free, so the tile's 256 regular rows go to LDS as
-    // bf16 (32-row block j in 16 KB block j: the halves of sA0 and sA1, then sB0..sB3; 16-byte chunk c of row r at
-    // chunk c ^ r) and out as whole 512-byte rows, two rows per 1 KB store. Straight from the
+    // Staged: after the K loop every operand buffer is free, so the tile's 256 regular rows go to LDS
+    // as bf16 (32-row block j in 16 KB block j: the halves of sA0 and sA1, then sB0..sB3; 16-byte
+    // chunk c of row r at chunk c ^ r) and out as whole 512-byte rows, two rows per 1 KB store. Straight from the
     // accumulators each 8-byte-per-lane store touches 32 rows, and with every CU reaching its
     // epilogue at about the same time that was a quarter of the down product's tile time. The
     // stores are plain: the combine reads y right after, partly from the last-level cache (with
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     auto blk = [&](int j) -> uint8_t* {
       return j == 0 ? sA0 : j == 1 ? sA0 + 16384 : j == 2 ? sA1 : j == 3 ? sA1 + 16384 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
     };
-    asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
+    asm volatile("s_barrier" ::: "memory");  // every wave is done with the operand buffers
     const int lr = lane & 31;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -624,12 +624,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
   }
   if constexpr (EPI == kEpiSwiglu) {
     // Staged as above: h of the 256 regular rows (128 columns, 256-byte rows) goes to LDS (32-row
-    // block j in the first 8 KB of slot j; 16-byte chunk c of row r at chunk c ^ (r & 15)) and out as
+    // block j in the first 8 KB of 16 KB block j; 16-byte chunk c of row r at chunk c ^ (r & 15)) and out as
     // whole rows, four per 1 KB store; the saved g | u (training only) are stored straight
     auto blk = [&](int j) -> uint8_t* {
       return j == 0 ? sA0 : j == 1 ? sA0 + 16384 : j == 2 ? sA1 : j == 3 ? sA1 + 16384 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
     };
-    asm volatile("s_barrier" ::: "memory");  // every wave is done with the ring
+    asm volatile("s_barrier" ::: "memory");  // every wave is done with the operand buffers
     const int lr = lane & 31;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
