@@ -31,6 +31,8 @@ CASES = [
     (1100, 256, 64, 4, 1, "bf16", [1, 1, 0.1, 0]),  # > 288 rows: two row tiles per expert
     (513, 2048, 768, 128, 8, "bf16", None),
     (77, 48, 16, 5, 3, "f32", [1, 0, 1, 1, 1]),
+    (600, 120, 72, 4, 2, "bf16", None),          # K = 120 / 72: ragged 64-deep row-operand stages, band tiles
+    (700, 200, 56, 4, 2, "bf16", [1, 1, 1, 0.2]),
 ]
 
 

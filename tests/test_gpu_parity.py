@@ -129,6 +129,10 @@ def test_permute_bit_exact(T, H, E, k, dtype, skew):
     ([260, 300], 256, 384, "bf16"),
     ([320, 321, 319, 0, 640, 641, 33, 290], 136, 40, "bf16"),   # two-block bands, 320-row tiles, splits
     ([300, 310, 256, 290, 333], 512, 256, "bf16"),
+    # K just below, just above and three rows-of-64 past a multiple of the 64-deep row-operand stage
+    ([290, 0, 300, 17, 320], 56, 72, "bf16"),
+    ([301, 64, 0, 289], 120, 200, "bf16"),
+    ([257, 33, 1], 200, 56, "bf16"),
 ])
 def test_grouped_swiglu_ffn(counts, H, I, dtype):
     E = len(counts)
