@@ -32,8 +32,15 @@
  *     failed check enqueues nothing. moe_last_error() gives the calling thread's last message.
  *     A launch failure reports MOE_ERR_HIP. Nothing aborts and nothing falls back silently.
  *     Device-side values are not checked on the host: expert indices outside [0, E) are dropped by the
- *     permute, and negative row maps are skipped; expert_offsets must be non-decreasing with
- *     offsets[E] <= the buffer's rows, and row maps must index existing rows.
+ *     permute (no row, not counted), a token may name one expert in several slots (one row per slot),
+ *     and negative row maps are skipped; expert_offsets must be non-decreasing with offsets[E] <= the
+ *     buffer's rows, and row maps must index existing rows.
+ *   - Sizing: the permute's layout handle is four caller-owned int32 arrays (counts [E], offsets [E+1],
+ *     row_of_slot [T*k], slot_of_row [T*k]) rather than one packed plan buffer, because the FFN and the
+ *     combine take them one by one and a caller that already holds grouped rows (one expert-parallel
+ *     rank after its exchange) passes its own offsets and row maps; the permute's scratch is sized by
+ *     moe_permute_workspace_bytes. The FFN backward's only intermediate, d_gu [N, 2I], is also one of
+ *     its outputs, so the caller allocates it like the other outputs instead of sizing a workspace.
  */
 #ifndef MOE_ROCM_H
 #define MOE_ROCM_H
@@ -96,10 +103,12 @@ moe_status moe_router_stats(const float* logits, const int32_t* topk_idx, int T,
 
 /* ---- (3) permute ----------------------------------------------------------------------------------
  * [DS VeOmni] group the N = T*k rows by expert: counts[e] = #slots choosing e, offsets = exclusive
- * scan (offsets[E] = number of valid slots), rows ordered by (expert, token) ascending:
+ * scan (offsets[E] = number of valid slots), rows ordered by (expert, token, slot) ascending:
  *   row_of_slot[t*k + j] = row of slot j of token t,  slot_of_row[row] = t*k + j,
  *   x_perm[row, :] = x[t, :]  (bit copy).
- * Slots whose index is outside [0, E) get no row: row_of_slot = -1, they are not counted.
+ * Slots whose index is outside [0, E) get no row: row_of_slot = -1, they are not counted, and
+ * slot_of_row past offsets[E] is left untouched. A token that names one expert in several slots
+ * gets one row per slot.
  *   x [T, H] dt; topk_idx [T, k] int32; x_perm [T*k, H] dt (out); counts [E], offsets [E+1],
  *   row_of_slot [T*k], slot_of_row [T*k] int32 (out); workspace: device scratch of at least
  *   moe_permute_workspace_bytes(T, k, E) bytes (contents need no initialisation).
@@ -110,6 +119,15 @@ size_t moe_permute_workspace_bytes(int T, int k, int E);
 moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t* topk_idx, int k, int E,
                        void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                        int32_t* slot_of_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* (2)+(3) in one call: the selection and weights of moe_router_topk, then the layout handle (and
+ * x_perm unless NULL) of moe_permute, with the same results bit for bit. For E <= 256 the top-k
+ * kernel also counts each 64-token chunk's expert choices, so the permute skips its counting pass.
+ * Arguments as in (2) and (3); workspace: moe_permute_workspace_bytes(T, k, E) bytes.           */
+moe_status moe_router_topk_permute(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                                   float* topk_w, const void* x, moe_dtype dt, int H, void* x_perm, int32_t* counts,
+                                   int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* ---- (4) grouped SwiGLU expert FFN -----------------------------------------------------------------
  * [MM 2, 8.3; opt. 2.1] for each expert e with rows [offsets[e], offsets[e+1]) of x_perm:
@@ -165,6 +183,9 @@ moe_status moe_unpermute_combine(const void* y, moe_dtype dt, int T, int H, int 
  * accumulated. */
 
 /* ---- (6) combine backward ------------------------------------------------------------------------
+ * [DS Automodel/DeepEP] the combine is the dispatch's backward: the gradient of the gate-weighted sum
+ * goes back along the layout handle of the forward's dispatch to each slot's row, and the gradient of
+ * the fp32 top-k weights is the row's dot product with the upstream gradient.
  *   d_y[row_of_slot[t*k+j]] = topk_w[t,j] * d_out[t]        (dt; rows without a slot are untouched)
  *   d_w[t,j] = <d_out[t], y[row_of_slot[t*k+j]]>            (fp32)
  *   d_out [T,H] dt; y [N,H] dt; row_of_slot [T*k]; topk_w [T,k] fp32; d_y [N,H] dt; d_w [T,k] fp32.  */
@@ -173,7 +194,9 @@ moe_status moe_unpermute_combine_bwd(const void* d_out, const void* y, moe_dtype
                                      hipStream_t stream);
 
 /* ---- (7) grouped SwiGLU FFN backward (bf16) --------------------------------------------------------
- * For each expert e and its rows r (g, u = the forward pre-activations saved in gu_saved, s = sigmoid(g)):
+ * [MM 2, 8.3] the transposed products of the experts' permute -> grouped_matmul -> SwiGLU ->
+ * grouped_matmul path over the same fused weights; [FT 3] experts without rows get zero weight
+ * gradients. For each expert e and its rows r (g, u = the forward pre-activations saved in gu_saved, s = sigmoid(g)):
  *   dh[r] = d_y[r] @ down_e^T;  dg = dh * u * s * (1 + g (1 - s));  du = dh * g * s;   d_gu[r] = dg | du
  *   d_x_perm[r] = d_gu[r] @ gate_up_e^T
  *   d_down_e    = h_e^T @ d_y_e        [I, H]   (zeros for an expert without rows)
@@ -206,13 +229,16 @@ moe_status moe_grouped_gemm_wgrad(const void* P, const void* Q, moe_dtype dt, in
                                   const int32_t* expert_offsets, void* d_w, int max_workgroups, hipStream_t stream);
 
 /* ---- (8) permute backward (gather-sum of a token's k rows) ----------------------------------------
+ * [DS Automodel/DeepEP] the dispatch's backward is a combine: each token's k row gradients are
+ * gathered through the same layout handle and summed (unweighted).
  *   d_x[t] = d_x_add[t] + sum_{j<k} d_x_perm[row_of_slot[t*k+j]]   (fp32, rounded once; d_x_add may
  *   be NULL; slots with row_of_slot < 0 are skipped).  d_x_perm [N,H], d_x_add, d_x [T,H] dt.         */
 moe_status moe_permute_bwd(const void* d_x_perm, moe_dtype dt, int T, int H, int k, const int32_t* row_of_slot,
                            const void* d_x_add, void* d_x, hipStream_t stream);
 
 /* ---- (9) top-k / renormalisation backward ----------------------------------------------------------
- * Selection has no gradient. With w the forward weights and s = sum_j w_j d_w_j:
+ * [MM 8.2/8.3] gradient of the FP32 softmax -> top-k -> weight normalisation of (2) with respect to
+ * the logits. Selection has no gradient. With w the forward weights and s = sum_j w_j d_w_j:
  *   renorm = 1:  d_logits[t, S_j] = w_j (d_w_j - s), 0 for experts outside the selection;
  *   renorm = 0:  d_logits[t, e] = p_e (1[e selected] d_w_e - s), p = softmax(logits[t]) recomputed
  *                (logits may be NULL when renorm = 1).   d_logits [T,E] fp32, every entry written.     */
@@ -220,9 +246,10 @@ moe_status moe_router_topk_bwd(const float* logits, const int32_t* topk_idx, con
                                int T, int E, int k, int renorm, float* d_logits, hipStream_t stream);
 
 /* ---- (10) router logits backward -------------------------------------------------------------------
- *   d_w_gate = x^T @ d_logits   [H,E] fp32   (skipped when NULL)
+ * [MM 8.2/8.3] gradient of the gate logits = x @ w_gate of (1):
+ *   d_w_gate = x^T @ d_logits   [H,E] fp32   (skipped when NULL; zeros when T = 0)
  *   d_x      = d_x_in + d_logits @ w_gate^T   [T,H] dt   (skipped when NULL; d_x_in may be NULL)
- * fp32 accumulation on the vector ALU.                                                                */
+ * fp32 accumulation: d_w_gate on the matrix cores (fp32 MFMA), d_x on the vector ALU.                 */
 moe_status moe_router_logits_bwd(const void* x, const void* w_gate, const float* d_logits, moe_dtype dt, int T,
                                  int H, int E, float* d_w_gate, const void* d_x_in, void* d_x, hipStream_t stream);
 

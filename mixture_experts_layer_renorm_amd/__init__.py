@@ -49,6 +49,7 @@ def load_library() -> ctypes.CDLL:
             "moe_router_stats": (I, [P, P, I, I, I, P, P, P, P, Z, P]),
             "moe_permute_workspace_bytes": (Z, [I, I, I]),
             "moe_permute": (I, [P, I, I, I, P, I, I, P, P, P, P, P, P, Z, P]),
+            "moe_router_topk_permute": (I, [P, I, I, I, I, P, P, P, I, I, P, P, P, P, P, P, Z, P]),
             "moe_grouped_swiglu_ffn": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P]),
             "moe_grouped_gemm_swiglu": (I, [P, P, I, I, I, I, I, P, P, P, P]),
             "moe_grouped_gemm_down": (I, [P, P, I, I, I, I, I, P, P, P]),
@@ -200,6 +201,41 @@ def moe_permute(x, topk_idx, E, x_perm=None, plan=None, workspace=None, stream=N
                                       _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "moe_permute")
     return x_perm, plan
+
+
+def moe_router_topk_permute(logits, k, x, E=None, renorm=True, topk_idx=None, topk_w=None, x_perm=None, plan=None,
+                            workspace=None, stream=None, rows=True):
+    """moe_router_topk then moe_permute in one call (same results bit for bit); rows=False computes
+    the plan only. Returns (topk_idx, topk_w, x_perm or None, plan)."""
+    T, E = logits.shape
+    H = x.shape[1]
+    _need(logits, "logits", torch.float32), _need(x, "x")
+    if x.shape[0] != T:
+        raise ValueError("x must have the logits' T rows")
+    dev = logits.device
+    N = T * k
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k)), _need(topk_w, "topk_w", torch.float32, (T, k))
+    if not rows:
+        x_perm = None
+    elif x_perm is None:
+        x_perm = torch.empty((N, H), dtype=x.dtype, device=dev)
+    if plan is None:
+        plan = Plan(torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+                    torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev))
+    ws_bytes = moe_permute_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(load_library().moe_router_topk_permute(_ptr(logits), T, E, k, int(bool(renorm)), _ptr(topk_idx),
+                                                  _ptr(topk_w), _ptr(x), _dt(x), H, _ptr(x_perm) if rows else None,
+                                                  _ptr(plan.counts), _ptr(plan.offsets), _ptr(plan.row_of_slot),
+                                                  _ptr(plan.slot_of_row), _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_router_topk_permute")
+    return topk_idx, topk_w, x_perm, plan
 
 
 def moe_grouped_swiglu_ffn(x_perm, gate_up, down, expert_offsets, h=None, y=None, gu_saved=None, stream=None):
@@ -493,11 +529,8 @@ def moe_layer_forward(x, gate_up, down, k, w_gate=None, logits=None, renorm=True
                             I_shared=I_sh, x_perm=not gather)
     if logits is None:
         logits = moe_router_logits(x, w_gate, bufs.logits, stream)
-    moe_router_topk(logits, k, renorm, bufs.topk_idx, bufs.topk_w, stream)
-    if gather:
-        moe_permute(x, bufs.topk_idx, E, None, bufs.plan, bufs.workspace, stream, rows=False)
-    else:
-        moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace, stream)
+    moe_router_topk_permute(logits, k, x, E, renorm, bufs.topk_idx, bufs.topk_w, bufs.x_perm, bufs.plan,
+                            bufs.workspace, stream, rows=not gather)
     if ffn_groups is not None:
         ffn_groups(gate_up, down, bufs.plan.offsets, bufs.h, bufs.y, x_perm=bufs.x_perm, x=x if gather else None,
                    slot_of_row=bufs.plan.slot_of_row, k=k, gu_saved=bufs.gu_saved, stream=stream)
@@ -590,8 +623,8 @@ class ChunkedForward:
             t0, t1 = self.bounds[c], self.bounds[c + 1]
             xc = x[t0:t1]
             lg = logits[t0:t1] if logits is not None else moe_router_logits(xc, w_gate, b.logits, side)
-            moe_router_topk(lg, k, renorm, b.topk_idx, b.topk_w, side)
-            moe_permute(xc, b.topk_idx, E, b.x_perm, b.plan, b.workspace, side, rows=not self.gather)
+            moe_router_topk_permute(lg, k, xc, E, renorm, b.topk_idx, b.topk_w, b.x_perm, b.plan, b.workspace, side,
+                                    rows=not self.gather)
             if overlap:
                 self.routed[c].record(side)
                 main.wait_event(self.routed[c])

@@ -126,6 +126,40 @@ moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t*
                     "moe_permute");
 }
 
+moe_status moe_router_topk_permute(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                                   float* topk_w, const void* x, moe_dtype dt, int H, void* x_perm, int32_t* counts,
+                                   int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_router_topk_permute";
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_ARG, "%s: T=%d H=%d must be >= 0", fn, T, H);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  REQUIRE(k >= 1 && k <= E && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, min(E=%d, %d)]", fn, k, E,
+          kMaxK);
+  REQUIRE(renorm == 0 || renorm == 1, MOE_ERR_INVALID_ARG, "%s: renorm=%d must be 0 or 1", fn, renorm);
+  REQUIRE((int64_t)T * k <= 0x7fffffffLL, MOE_ERR_INVALID_ARG, "%s: T*k overflows int32", fn);
+  REQUIRE(counts && offsets, MOE_ERR_INVALID_ARG, "%s: null counts/offsets", fn);
+  if (T == 0) {
+    hipError_t e = moe::launch_fill_i32(counts, E, 0, stream);
+    if (e == hipSuccess) e = moe::launch_fill_i32(offsets, E + 1, 0, stream);
+    return hip_status(e, fn);
+  }
+  REQUIRE(logits && topk_idx && topk_w && row_of_slot && slot_of_row, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(!x_perm || x, MOE_ERR_INVALID_ARG, "%s: x is NULL but x_perm is not", fn);
+  const size_t need = moe::permute_workspace_bytes(T, E);
+  REQUIRE(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+          workspace ? workspace_bytes : (size_t)0, need);
+  int32_t* chunk_counts = (int32_t*)workspace;
+  bool counted = false;
+  hipError_t e = moe::launch_router_topk(logits, T, E, k, renorm, topk_idx, topk_w, stream, chunk_counts, &counted);
+  if (e == hipSuccess)
+    e = counted ? moe::launch_permute_counted(x, (int)dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot,
+                                              slot_of_row, chunk_counts, stream)
+                : moe::launch_permute(x, (int)dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot,
+                                      slot_of_row, chunk_counts, stream);
+  return hip_status(e, fn);
+}
+
 namespace {
 moe_status check_ffn(const char* fn, moe_dtype dt, int N, int H, int I, int E) {
   REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
@@ -370,8 +404,13 @@ moe_status moe_router_logits_bwd(const void* x, const void* w_gate, const float*
   REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   REQUIRE(T >= 0 && H >= 1, MOE_ERR_INVALID_ARG, "%s: T=%d H=%d out of range", fn, T, H);
   REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
-  REQUIRE(x && w_gate && d_logits, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
   REQUIRE(d_w_gate || d_x, MOE_ERR_INVALID_ARG, "%s: nothing to compute (d_w_gate and d_x are both NULL)", fn);
+  if (T == 0) {  // no tokens: x^T dl over an empty K is zero (a fill kernel); d_x has no rows
+    const int64_t n = (int64_t)H * E;
+    REQUIRE(n <= 0x7fffffffLL, MOE_ERR_INVALID_ARG, "%s: H*E too large", fn);
+    return hip_status(d_w_gate ? moe::launch_fill_i32((int32_t*)d_w_gate, (int)n, 0, stream) : hipSuccess, fn);
+  }
+  REQUIRE(x && w_gate && d_logits, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
   return hip_status(
       moe::launch_router_logits_bwd(x, w_gate, d_logits, (int)dt, T, H, E, d_w_gate, d_x_in, d_x, stream), fn);
 }

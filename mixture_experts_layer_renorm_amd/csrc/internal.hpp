@@ -17,8 +17,10 @@ hipError_t launch_router_logits(const void* x, const void* w_gate, int dt, int T
 size_t router_stats_workspace_bytes(int T, int E);
 hipError_t launch_router_stats(const float* logits, const int32_t* topk_idx, int T, int E, int k, float* probs,
                                float* mean_prob, int32_t* load, void* workspace, hipStream_t s);
+// chunk_counts (may be NULL): the expert histogram of every kPermuteChunk tokens, [nchunks, E], as
+// permute_count_kernel writes it; returns false in *counted when this E takes the separate count
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w,
-                              hipStream_t s);
+                              hipStream_t s, int32_t* chunk_counts = nullptr, bool* counted = nullptr);
 
 // permute.hip
 constexpr int kPermuteChunk = 64;   // tokens per plan chunk (64 measured faster than 128 or 256)
@@ -28,6 +30,10 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,
                           int32_t* chunk_counts, hipStream_t s);
+// the same from chunk counts already computed (by the top-k kernel)
+hipError_t launch_permute_counted(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E,
+                                  void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                                  int32_t* slot_of_row, const int32_t* chunk_counts, hipStream_t s);
 
 // grouped_gemm.hip
 hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, int N, int H, int I, int E,

@@ -8,7 +8,10 @@
 //  1. count : per chunk of kPermuteChunk tokens, an LDS histogram of the chunk's expert choices.
 //  2. plan  : per chunk, global bases = exclusive scan over experts of the totals + the counts of
 //             earlier chunks; in-chunk ranks from per-expert token bitmaps (popcount of the
-//             tokens before this one). Writes counts, offsets, row_of_slot, slot_of_row.
+//             tokens before this one). Writes counts, offsets, row_of_slot, slot_of_row. A chunk
+//             in which a token names one expert in two slots ranks by counting earlier slots
+//             instead, so every slot gets its own row in (expert, token, slot) order.
+//     (The router's top-k kernel can produce the counts of step 1 itself: launch_permute_counted.)
 //  3. scatter: one wave per token copies x[t] (read once) to its k rows of x_perm.
 // Slots whose expert index is outside [0, E) get no row (row_of_slot = -1).
 #include "common.hpp"
@@ -19,6 +22,7 @@ namespace moe {
 constexpr int kPlanThreads = 256;
 constexpr int kMaxE = 1024;
 constexpr int kMaskWords = kPermuteChunk / 32;
+constexpr int kMaxChunkSlots = kPermuteChunk * 32;  // k <= 32
 
 __global__ __launch_bounds__(kPlanThreads) void permute_count_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                                      int E, int32_t* __restrict__ chunk_counts) {
@@ -43,61 +47,95 @@ __global__ __launch_bounds__(kPlanThreads) void permute_plan_kernel(
   __shared__ int scan[kMaxE + 1];
   __shared__ int base[kMaxE];
   __shared__ uint32_t mask[kMaxE * kMaskWords];
+  __shared__ int s_idx[kMaxChunkSlots];      // the chunk's expert choices, slot order
+  __shared__ int p_tot[kPlanThreads], p_bef[kPlanThreads];
   __shared__ int wave_tot[kPlanThreads / kWave];
+  __shared__ int s_dup;
   const int c = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
-    // the chunk counts of expert e, sixteen independent loads at a time (one at a time, the loop
-    // is a chain of L2 round trips)
-    int tot = 0, before = 0;
-    int cc = 0;
-    for (; cc + 16 <= nchunks; cc += 16) {
+  const int tid = threadIdx.x;
+  // per expert: its total over all chunks and over the chunks before this one. With E < 256 the
+  // chunks of an expert are split over G = 256 / E threads, each issuing its loads as one batch
+  // (the loads are independent; one chain of them per expert would be a chain of L2 round trips).
+  auto sum_chunks = [&](int e, int g, int G, int& tot, int& before) {
+    tot = 0;
+    before = 0;
+    int cc = g;
+    for (; cc + 15 * G < nchunks; cc += 16 * G) {
       int v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = chunk_counts[(int64_t)(cc + u) * E + e];
+      for (int u = 0; u < 16; ++u) v[u] = chunk_counts[(int64_t)(cc + u * G) * E + e];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         tot += v[u];
-        if (cc + u < c) before += v[u];
+        if (cc + u * G < c) before += v[u];
       }
     }
-    for (; cc < nchunks; ++cc) {
+    for (; cc < nchunks; cc += G) {
       const int v = chunk_counts[(int64_t)cc * E + e];
       tot += v;
       if (cc < c) before += v;
     }
-    scan[e] = tot;
-    base[e] = before;
+  };
+  if (E >= kPlanThreads) {
+    for (int e = tid; e < E; e += kPlanThreads) sum_chunks(e, 0, 1, scan[e], base[e]);
+  } else {
+    const int G = kPlanThreads / E;
+    int tot = 0, before = 0;
+    if (tid < G * E) sum_chunks(tid % E, tid / E, G, tot, before);
+    p_tot[tid] = tot;
+    p_bef[tid] = before;
+    __syncthreads();
+    if (tid < E) {
+      int a = 0, b = 0;
+      for (int g = 0; g < G; ++g) {
+        a += p_tot[g * E + tid];
+        b += p_bef[g * E + tid];
+      }
+      scan[tid] = a;
+      base[tid] = b;
+    }
   }
-  for (int i = threadIdx.x; i < E * kMaskWords; i += kPlanThreads) mask[i] = 0u;
+  for (int i = tid; i < E * kMaskWords; i += kPlanThreads) mask[i] = 0u;
+  const int t0 = c * kPermuteChunk;
+  const int64_t s0 = (int64_t)t0 * k;
+  const int ns = (int)((int64_t)min(T, t0 + kPermuteChunk) * k - s0);
+  for (int i = tid; i < ns; i += kPlanThreads) s_idx[i] = idx[s0 + i];
+  if (tid == 0) s_dup = 0;
   __syncthreads();
   if (c == 0)
-    for (int e = threadIdx.x; e < E; e += kPlanThreads) counts[e] = scan[e];
+    for (int e = tid; e < E; e += kPlanThreads) counts[e] = scan[e];
   block_exclusive_scan<kPlanThreads>(scan, E, wave_tot);
-  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
+  for (int e = tid; e < E; e += kPlanThreads) {
     base[e] += scan[e];
     if (c == 0) offsets[e] = scan[e];
   }
-  if (c == 0 && threadIdx.x == 0) offsets[E] = scan[E];
+  if (c == 0 && tid == 0) offsets[E] = scan[E];
 
-  const int t0 = c * kPermuteChunk;
-  const int64_t s0 = (int64_t)t0 * k;
-  const int64_t s1 = (int64_t)min(T, t0 + kPermuteChunk) * k;
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += kPlanThreads) {
-    const int e = idx[s];
+  // per-expert bitmaps of the chunk's tokens; a bit found already set means that a token names one
+  // expert in two of its slots (the router never does that; routing supplied by a caller may)
+  for (int i = tid; i < ns; i += kPlanThreads) {
+    const int e = s_idx[i];
     if (e >= 0 && e < E) {
-      const int tl = (int)(s / k) - t0;
-      atomicOr(&mask[e * kMaskWords + (tl >> 5)], 1u << (tl & 31));
+      const int tl = i / k;
+      const uint32_t bit = 1u << (tl & 31);
+      if (atomicOr(&mask[e * kMaskWords + (tl >> 5)], bit) & bit) s_dup = 1;
     }
   }
   __syncthreads();
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += kPlanThreads) {
-    const int e = idx[s];
+  const bool dup = s_dup != 0;
+  for (int i = tid; i < ns; i += kPlanThreads) {
+    const int e = s_idx[i];
+    const int64_t s = s0 + i;
     if (e >= 0 && e < E) {
-      const int tl = (int)(s / k) - t0;
-      const uint32_t* m = mask + e * kMaskWords;
       int rank = 0;
-      for (int w = 0; w < (tl >> 5); ++w) rank += __popc(m[w]);
-      rank += __popc(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
+      if (!dup) {  // rank = earlier tokens of the chunk that chose e
+        const int tl = i / k;
+        const uint32_t* m = mask + e * kMaskWords;
+        for (int w = 0; w < (tl >> 5); ++w) rank += __popc(m[w]);
+        rank += __popc(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
+      } else {     // rank = earlier slots of the chunk that chose e: (token, slot) order
+        for (int i2 = 0; i2 < i; ++i2) rank += s_idx[i2] == e;
+      }
       const int row = base[e] + rank;
       row_of_slot[s] = row;
       slot_of_row[row] = (int32_t)s;
@@ -165,13 +203,13 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
-                          int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,
-                          int32_t* chunk_counts, hipStream_t s) {
+// plan + row copy from chunk counts already in chunk_counts
+static hipError_t plan_and_scatter(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E,
+                                   void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                                   int32_t* slot_of_row, const int32_t* chunk_counts, hipStream_t s) {
   const int nchunks = permute_nchunks(T);
   const int64_t row_bytes = (int64_t)H * (int64_t)dtype_bytes(dt);
   const int vec16 = (row_bytes % 16 == 0) && (((uintptr_t)x | (uintptr_t)x_perm) % 16 == 0);
-  hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(kPlanThreads), 0, s, topk_idx, T, k, E, chunk_counts);
   hipLaunchKernelGGL(permute_plan_kernel, dim3(nchunks), dim3(kPlanThreads), 0, s, topk_idx, T, k, E, chunk_counts,
                      nchunks, counts, offsets, row_of_slot, slot_of_row);
   if (x_perm)  // else the plan only: a gathering GEMM reads the rows from x itself
@@ -179,6 +217,22 @@ hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* to
                        dim3(kScatterWaves * kWave), 0, s, (const uint8_t*)x, T, row_bytes, k, row_of_slot,
                        (uint8_t*)x_perm, vec16);
   return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
+                          int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,
+                          int32_t* chunk_counts, hipStream_t s) {
+  hipLaunchKernelGGL(permute_count_kernel, dim3(permute_nchunks(T)), dim3(kPlanThreads), 0, s, topk_idx, T, k, E,
+                     chunk_counts);
+  return plan_and_scatter(x, dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot, slot_of_row,
+                          chunk_counts, s);
+}
+
+hipError_t launch_permute_counted(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E,
+                                  void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                                  int32_t* slot_of_row, const int32_t* chunk_counts, hipStream_t s) {
+  return plan_and_scatter(x, dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot, slot_of_row,
+                          chunk_counts, s);
 }
 
 }  // namespace moe

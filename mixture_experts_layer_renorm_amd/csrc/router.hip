@@ -446,6 +446,137 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// The same selection and weights with L = 8 or 16 lanes per token (E <= 256): lane `sub` of a
+// token's group holds experts e = q * L + sub, q = 0..VPL-1 (ascending e per lane), so a round's
+// argmax is a local scan plus log2(L) exchanges inside a 16-lane row (DPP quad permutes and the
+// row mirrors, a few cycles each, against the 64-lane shuffles above). Slot j is kept by lane
+// j % L. A workgroup holds kPermuteChunk tokens (L waves of 64 / L tokens), so it can also write
+// the chunk's expert histogram that the permute's plan takes (permute_count_kernel's output).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+constexpr int kNoExpert = 0x7fffffff;
+// (value, index) order: larger value first, ties to the lower index; kNoExpert = no candidate
+__device__ __forceinline__ void take_better(float& bv, int& be, float ov, int oe) {
+  const bool take = (oe != kNoExpert) && (be == kNoExpert || ov > bv || (ov == bv && oe < be));
+  bv = take ? ov : bv;
+  be = take ? oe : be;
+}
+template <int CTRL>
+__device__ __forceinline__ void xchg_better(float& bv, int& be) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oe = dpp_i<CTRL>(be);
+  take_better(bv, be, ov, oe);
+}
+// all-reduce over groups of L lanes: quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror
+template <int L>
+__device__ __forceinline__ void group_best(float& bv, int& be) {
+  xchg_better<0xB1>(bv, be);
+  xchg_better<0x4E>(bv, be);
+  xchg_better<0x141>(bv, be);
+  if constexpr (L == 16) xchg_better<0x140>(bv, be);
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  if constexpr (L == 16) v += dpp_f<0x140>(v);
+  return v;
+}
+
+template <int L, int VPL>
+__global__ __launch_bounds__(L * kWave) void router_topk_group_kernel(const float* __restrict__ logits, int T, int E,
+                                                                      int k, int renorm, int32_t* __restrict__ topk_idx,
+                                                                      float* __restrict__ topk_w,
+                                                                      int32_t* __restrict__ chunk_counts) {
+  static_assert(L == 8 || L == 16, "a token's lanes stay inside one 16-lane row");
+  constexpr int TPW = kWave / L;  // tokens per wave
+  constexpr int KR = 32 / L;      // slots kept per lane (k <= 32)
+  __shared__ int cnt[L * VPL];
+  const int lane = lane_id(), sub = lane & (L - 1);
+  const int t = blockIdx.x * kPermuteChunk + (int)(threadIdx.x / kWave) * TPW + lane / L;
+  const bool live = t < T;
+  if (chunk_counts) {
+    for (int e = threadIdx.x; e < E; e += L * kWave) cnt[e] = 0;
+    __syncthreads();
+  }
+  const float* l = logits + (int64_t)t * E;
+  float v[VPL];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int q = 0; q < VPL; ++q) {
+    const int e = q * L + sub;
+    const bool ok = live && e < E;
+    v[q] = ok ? l[e] : 0.0f;
+    avail |= ok ? 1u << q : 0u;
+  }
+  const uint32_t valid = avail;
+  float sv[KR];
+  int se[KR];
+#pragma unroll
+  for (int r = 0; r < KR; ++r) {
+    sv[r] = 0.0f;
+    se[r] = -1;
+  }
+  float m = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.0f;
+    int be = kNoExpert;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {  // ascending e: strict > keeps the lower index on ties
+      const bool take = ((avail >> q) & 1u) && (be == kNoExpert || v[q] > bv);
+      bv = take ? v[q] : bv;
+      be = take ? q * L + sub : be;
+    }
+    group_best<L>(bv, be);
+    if (j == 0) m = bv;
+    if (be != kNoExpert && (be & (L - 1)) == sub) avail &= ~(1u << (be / L));
+#pragma unroll
+    for (int r = 0; r < KR; ++r)
+      if (j == r * L + sub) {
+        sv[r] = bv;
+        se[r] = be;
+      }
+  }
+  float part = 0.0f;
+  if (renorm) {
+#pragma unroll
+    for (int r = 0; r < KR; ++r)
+      if (r * L + sub < k) part += expf(sv[r] - m);
+  } else {
+#pragma unroll
+    for (int q = 0; q < VPL; ++q)
+      if ((valid >> q) & 1u) part += expf(v[q] - m);
+  }
+  const float den = group_sum<L>(part);
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < KR; ++r) {
+      const int j = r * L + sub;
+      if (j < k) {
+        topk_idx[(int64_t)t * k + j] = se[r];
+        topk_w[(int64_t)t * k + j] = expf(sv[r] - m) / den;
+      }
+    }
+  }
+  if (chunk_counts) {
+    if (live) {
+#pragma unroll
+      for (int r = 0; r < KR; ++r)
+        if (r * L + sub < k) atomicAdd(&cnt[se[r]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += L * kWave) chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Router statistics for an auxiliary load-balance loss: the full softmax per token (probs), its
 // sum over tokens, and the expert load (how many (token, slot) pairs chose each expert).
 // Stage 1: a workgroup of 4 waves owns kStatsTok tokens, a wave a contiguous run of them in
@@ -608,7 +739,29 @@ hipError_t launch_router_logits(const void* x, const void* w_gate, int dt, int T
 }
 
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w,
-                              hipStream_t s) {
+                              hipStream_t s, int32_t* chunk_counts, bool* counted) {
+  if (E <= 256) {
+    const dim3 grid(permute_nchunks(T));
+#define MOE_TOPK_GROUP(L, V) \
+  hipLaunchKernelGGL((router_topk_group_kernel<L, V>), grid, dim3(L * kWave), 0, s, logits, T, E, k, renorm, idx, w, \
+                     chunk_counts)
+    if (E <= 8)
+      MOE_TOPK_GROUP(8, 1);
+    else if (E <= 16)
+      MOE_TOPK_GROUP(8, 2);
+    else if (E <= 32)
+      MOE_TOPK_GROUP(8, 4);
+    else if (E <= 64)
+      MOE_TOPK_GROUP(8, 8);
+    else if (E <= 128)
+      MOE_TOPK_GROUP(8, 16);
+    else
+      MOE_TOPK_GROUP(16, 16);
+#undef MOE_TOPK_GROUP
+    if (counted) *counted = chunk_counts != nullptr;
+    return hipGetLastError();
+  }
+  if (counted) *counted = false;
   dim3 grid((T + kTopkWaves - 1) / kTopkWaves), block(kTopkWaves * kWave);
   const int vpl = (E + kWave - 1) / kWave;
 #define MOE_TOPK_CASE(V)                                                                                  \

@@ -135,12 +135,19 @@ int orc_permute_plan(const int32_t* topk_idx, int64_t T, int64_t k, int64_t E, i
     if (!topk_idx || !counts || !offsets || !row_of_slot || !slot_of_row || T < 0 || k < 1 || E < 1)
         return -1;
     const int64_t N = T * k;
-    for (int64_t s = 0; s < N; ++s)
-        if (topk_idx[s] < 0 || topk_idx[s] >= E) return -2;
+    /* a slot whose index lies outside [0, E) names no expert: it is sent nowhere, so it is not
+     * counted and gets no row (row_of_slot = -1); the rows of the valid slots follow in order */
     for (int64_t e = 0; e < E; ++e) counts[e] = 0;
-    for (int64_t s = 0; s < N; ++s) counts[topk_idx[s]] += 1;
+    for (int64_t s = 0; s < N; ++s)
+        if (topk_idx[s] >= 0 && topk_idx[s] < E) counts[topk_idx[s]] += 1;
     offsets[0] = 0;
     for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t s = 0; s < N; ++s) {
+        row_of_slot[s] = -1;
+        slot_of_row[s] = -1;
+    }
+    /* rows expert by expert; inside an expert, tokens ascending and, should a token name the same
+     * expert in several slots, those slots in ascending order */
     int64_t row = 0;
     for (int64_t e = 0; e < E; ++e)
         for (int64_t t = 0; t < T; ++t)
@@ -157,6 +164,8 @@ int orc_permute_rows(const void* x, int64_t elem_bytes, int64_t H, const int32_t
                      int64_t k, int64_t N, void* x_perm) {
     if (!x || !slot_of_row || !x_perm || elem_bytes < 1 || H < 0 || k < 1 || N < 0) return -1;
     const size_t rb = (size_t)(elem_bytes * H);
+    for (int64_t r = 0; r < N; ++r)
+        if (slot_of_row[r] < 0) return -2; /* only rows that exist (below offsets[E]) are copied */
     for (int64_t r = 0; r < N; ++r) {
         int64_t t = slot_of_row[r] / k;
         memcpy((char*)x_perm + (size_t)r * rb, (const char*)x + (size_t)t * rb, rb);

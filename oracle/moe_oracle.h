@@ -49,8 +49,9 @@ int orc_router_stats(const float* logits, const int32_t* topk_idx, int64_t T, in
 int orc_router_topk(const float* logits, int64_t T, int64_t E, int64_t k, int renorm,
                     int32_t* topk_idx, double* topk_w);
 
-/* counts[e], exclusive offsets[0..E], rows ordered by (expert, token) ascending.
- * row_of_slot[t*k+j] = row, slot_of_row[row] = t*k+j. */
+/* counts[e], exclusive offsets[0..E], rows ordered by (expert, token, slot) ascending.
+ * row_of_slot[t*k+j] = row, slot_of_row[row] = t*k+j. A slot whose index is outside [0, E) is
+ * dropped (not counted, row_of_slot = -1); slot_of_row entries past offsets[E] are -1. */
 int orc_permute_plan(const int32_t* topk_idx, int64_t T, int64_t k, int64_t E, int32_t* counts,
                      int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row);
 

@@ -17,11 +17,15 @@ pytestmark = [pytest.mark.gpu,
 
 
 @pytest.mark.parametrize("T,H,k,dtype", [(64, 64, 2, "f32"), (500, 2048, 8, "bf16"), (77, 136, 3, "bf16"),
-                                         (5, 40, 1, "bf16"), (33, 7168, 8, "bf16"), (31, 20, 4, "f32")])
+                                         (5, 40, 1, "bf16"), (33, 7168, 8, "bf16"), (31, 20, 4, "f32"),
+                                         (100, 2048, 9, "bf16"), (40, 136, 16, "bf16"), (21, 256, 32, "bf16"),
+                                         (9, 24, 32, "f32")])
 def test_combine_bwd(T, H, k, dtype):
     N = T * k + 3                                  # three rows no slot points at: left untouched
     g = generator((970, T, H, k))
     ros = g.permutation(N)[:T * k].astype(np.int32)
+    if k > 8:
+        ros[5::13] = -1                            # dropped slots: zero d_w, no row written
     y = normal((N, H), 1.0, (971, N, H), dtype)
     w = g.random((T, k), dtype=np.float32)
     d_out = normal((T, H), 1.0, (972, T, H), dtype)
@@ -30,15 +34,20 @@ def test_combine_bwd(T, H, k, dtype):
     d_y, d_w = moe.moe_unpermute_combine_bwd(dev(d_out), dev(y), dev(ros), dev(w), d_y=d_y)
     ref_dy, ref_dw = oracle.combine_bwd(d_out, y, ros, w)
     gy = host(d_y)
-    assert rel_err(gy[ros].reshape(T, k, H), ref_dy) <= TOL[dtype]
+    valid = (ros >= 0).reshape(T, k)
+    got_dy = gy[np.where(ros >= 0, ros, 0)].reshape(T, k, H)
+    assert rel_err(got_dy[valid], ref_dy[valid]) <= TOL[dtype]
     assert rel_err(host(d_w), ref_dw) <= TOL["f32"]
-    untouched = np.setdiff1d(np.arange(N), ros)
+    assert np.all(host(d_w)[~valid] == 0.0)
+    untouched = np.setdiff1d(np.arange(N), ros[ros >= 0])
     assert np.all(as64(gy[untouched]) == 7.0)
 
 
 @pytest.mark.parametrize("T,H,k,dtype,add", [(64, 64, 2, "f32", False), (500, 2048, 8, "bf16", True),
                                              (77, 136, 3, "bf16", False), (5, 40, 1, "bf16", True),
-                                             (33, 7168, 8, "bf16", True), (31, 20, 4, "f32", True)])
+                                             (33, 7168, 8, "bf16", True), (31, 20, 4, "f32", True),
+                                             (100, 2048, 9, "bf16", True), (40, 136, 16, "bf16", False),
+                                             (21, 256, 32, "bf16", True), (9, 24, 32, "f32", False)])
 def test_permute_bwd(T, H, k, dtype, add):
     N = T * k
     g = generator((973, T, H, k))
@@ -81,6 +90,17 @@ def test_router_logits_bwd(T, H, E, dtype, add):
         ref_dx = ref_dx + as64(dxa)
     assert rel_err(host(dwg), ref_dwg) <= TOL["f32"]
     assert rel_err(host(dx), ref_dx) <= TOL[dtype]
+
+
+def test_router_logits_bwd_no_tokens():
+    """T = 0: d_w_gate = x^T dl over no tokens is zero; nothing else is written."""
+    H, E = 64, 16
+    dwg = torch.full((H, E), 5.0, device="cuda")
+    x = torch.zeros((0, H), dtype=torch.bfloat16, device="cuda")
+    dwg, dx = moe.moe_router_logits_bwd(x, torch.zeros((H, E), dtype=torch.bfloat16, device="cuda"),
+                                        torch.zeros((0, E), device="cuda"), d_w_gate=dwg)
+    torch.cuda.synchronize()
+    assert torch.all(dwg == 0) and dx.shape == (0, H)
 
 
 @pytest.mark.parametrize("counts,H,I", [

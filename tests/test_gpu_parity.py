@@ -64,7 +64,8 @@ def test_router_logits_subnormal_products():
 
 
 @pytest.mark.parametrize("T,E,k", [(64, 8, 2), (1000, 128, 8), (77, 256, 8), (50, 1024, 32), (10, 5, 5),
-                                   (33, 64, 1), (20, 3, 3), (129, 100, 7)])
+                                   (33, 64, 1), (20, 3, 3), (129, 100, 7), (200, 16, 16), (70, 32, 32),
+                                   (65, 250, 32), (4097, 128, 8), (100, 257, 9), (3, 200, 17)])
 @pytest.mark.parametrize("renorm", [True, False])
 def test_router_topk(T, E, k, renorm):
     g = generator((952, T, E, k))
@@ -117,6 +118,75 @@ def test_permute_bit_exact(T, H, E, k, dtype, skew):
     assert np.array_equal(host(x_perm), want)
 
 
+def routing_repeats_drops(T, E, k, key, drop):
+    """Caller-supplied routing that the router never produces: a token may name one expert in
+    several slots, and with drop=True some indices lie outside [0, E) (-1, E, large)."""
+    g = generator(key)
+    idx = g.integers(0, E, (T, k)).astype(np.int32)
+    if drop:
+        knock = g.random((T, k)) < 0.2
+        idx = np.where(knock, g.choice(np.array([-1, E, -5, 1 << 24]), (T, k)), idx).astype(np.int32)
+    return idx
+
+
+@pytest.mark.parametrize("T,H,E,k,drop", [(300, 40, 8, 4, False), (257, 64, 16, 8, True), (64, 16, 1, 3, False),
+                                          (1000, 24, 128, 8, True), (129, 8, 4, 32, True), (70, 48, 1024, 5, True),
+                                          (2, 16, 3, 2, True)])
+def test_permute_repeats_and_drops(T, H, E, k, drop):
+    """Reading r19 through moe_permute: out-of-range indices get no row and are not counted; repeated
+    experts get one row per slot in (expert, token, slot) order. Rows past offsets[E] are untouched."""
+    x = normal((T, H), 1.0, (964, T, H), "bf16")
+    idx = routing_repeats_drops(T, E, k, (965, T, E, k), drop)
+    N = T * k
+    x_perm = torch.full((N, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    plan = moe.Plan(torch.empty(E, dtype=torch.int32, device="cuda"),
+                    torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                    torch.empty(N, dtype=torch.int32, device="cuda"),
+                    torch.full((N,), -9, dtype=torch.int32, device="cuda"))
+    x_perm, plan = moe.moe_permute(dev(x), dev(idx), E, x_perm=x_perm, plan=plan)
+    counts, offsets, ros, sor = oracle.permute_plan(idx, E)
+    n = int(offsets[E])
+    assert np.array_equal(host(plan.counts), counts)
+    assert np.array_equal(host(plan.offsets), offsets)
+    assert np.array_equal(host(plan.row_of_slot), ros)
+    gs = host(plan.slot_of_row)
+    assert np.array_equal(gs[:n], sor[:n]) and np.all(gs[n:] == -9)
+    gx = host(x_perm)
+    assert np.array_equal(gx[:n], oracle.permute_rows(x, sor[:n], k))
+    assert np.all(as64(gx[n:]) == 3.0)
+    if drop:
+        assert n < N
+
+
+@pytest.mark.parametrize("T,H,E,k,rows", [(1000, 64, 128, 8, True), (77, 40, 256, 8, True), (50, 24, 1024, 32, True),
+                                          (64, 16, 8, 2, False), (130, 8, 200, 16, True), (4097, 16, 128, 8, False),
+                                          (1, 8, 1, 1, True), (129, 32, 64, 32, True)])
+@pytest.mark.parametrize("renorm", [True, False])
+def test_router_topk_permute(T, H, E, k, rows, renorm):
+    """The fused call: the same bits as moe_router_topk then moe_permute, and the oracle's plan."""
+    g = generator((966, T, E, k))
+    logits = (np.round(g.standard_normal((T, E)) * 4) / 4).astype(np.float32)   # frequent ties
+    x = normal((T, H), 1.0, (967, T, H), "bf16")
+    idx, w, xp, plan = moe.moe_router_topk_permute(dev(logits), k, dev(x), renorm=renorm, rows=rows)
+    idx2, w2 = moe.moe_router_topk(dev(logits), k, renorm)
+    xp2, plan2 = moe.moe_permute(dev(x), idx2, E, rows=rows)
+    assert np.array_equal(host(idx), host(idx2))
+    assert np.array_equal(host(w).view(np.uint32), host(w2).view(np.uint32))
+    for a, b in [(plan.counts, plan2.counts), (plan.offsets, plan2.offsets), (plan.row_of_slot, plan2.row_of_slot),
+                 (plan.slot_of_row, plan2.slot_of_row)]:
+        assert np.array_equal(host(a), host(b))
+    ridx, rw = oracle.router_topk(logits, k, renorm)
+    assert np.array_equal(host(idx), ridx)
+    assert rel_err(host(w), rw) <= TOL["f32"]
+    counts, offsets, ros, sor = oracle.permute_plan(ridx, E)
+    assert np.array_equal(host(plan.counts), counts) and np.array_equal(host(plan.offsets), offsets)
+    assert np.array_equal(host(plan.row_of_slot), ros) and np.array_equal(host(plan.slot_of_row), sor)
+    if rows:
+        assert np.array_equal(host(xp), oracle.permute_rows(x, sor, k))
+    else:
+        assert xp is None
+
+
 # ---- grouped FFN ------------------------------------------------------------------------------
 @pytest.mark.parametrize("counts,H,I,dtype", [
     ([0, 300, 1, 0, 257, 142], 136, 40, "bf16"),
@@ -157,11 +227,15 @@ def test_grouped_swiglu_ffn(counts, H, I, dtype):
 # ---- combine ----------------------------------------------------------------------------------
 @pytest.mark.parametrize("T,H,k,dtype,res", [(64, 64, 2, "f32", False), (1000, 2048, 8, "bf16", True),
                                              (77, 136, 3, "bf16", False), (5, 40, 1, "bf16", True),
-                                             (300, 7168, 8, "bf16", False), (31, 20, 4, "f32", True)])
+                                             (300, 7168, 8, "bf16", False), (31, 20, 4, "f32", True),
+                                             (200, 2048, 9, "bf16", True), (65, 136, 16, "bf16", False),
+                                             (33, 256, 32, "bf16", True), (17, 40, 32, "f32", False)])
 def test_unpermute_combine(T, H, k, dtype, res):
     N = T * k
     g = generator((958, T, H, k))
     ros = g.permutation(N).astype(np.int32)
+    if k > 8:
+        ros[::11] = -1                             # dropped slots, also in the second batch of loads
     y = normal((N, H), 1.0, (959, N, H), dtype)
     w = g.random((T, k), dtype=np.float32)
     r = normal((T, H), 1.0, (960, T, H), dtype) if res else None
@@ -172,7 +246,9 @@ def test_unpermute_combine(T, H, k, dtype, res):
 # ---- whole layer, small shapes -------------------------------------------------------------------
 @pytest.mark.parametrize("T,H,I,E,k,dtype", [(64, 64, 32, 8, 2, "f32"), (300, 136, 40, 16, 4, "bf16"),
                                              (1, 64, 32, 8, 8, "bf16"), (257, 256, 64, 64, 8, "bf16"),
-                                             (100, 48, 16, 1, 1, "bf16"), (50, 32, 16, 4, 4, "f32")])
+                                             (100, 48, 16, 1, 1, "bf16"), (50, 32, 16, 4, 4, "f32"),
+                                             (130, 64, 32, 32, 16, "bf16"), (70, 40, 24, 64, 32, "bf16"),
+                                             (90, 32, 16, 300, 9, "f32")])
 @pytest.mark.parametrize("renorm", [True, False])
 def test_layer_small(T, H, I, E, k, dtype, renorm):
     d = make_layer_inputs(T, H, I, E, k, dtype, (961, T, E), w_std=0.08, wg_std=0.3)

@@ -55,6 +55,47 @@ def test_permute_plan_against_library(T, E, k):
     assert np.array_equal(np.sort(ros), slots)
 
 
+def plan_by_sorting(idx, E):
+    """The plan written with library routines only: keep the slots whose index lies in [0, E),
+    count them per expert, and order them by (expert, slot) with a stable sort."""
+    flat = idx.ravel()
+    slots = np.arange(flat.size)
+    keep = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[keep], minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    order = slots[keep][np.lexsort((slots[keep], flat[keep]))]
+    ros = np.full(flat.size, -1, np.int32)
+    ros[order] = np.arange(order.size)
+    return counts, offsets, ros, order.astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(50, 6, 4, "repeat"), (300, 16, 8, "repeat"), (7, 1, 3, "repeat"),
+                                        (200, 12, 5, "drop"), (64, 4, 2, "drop"), (129, 32, 32, "both")])
+def test_permute_plan_repeats_and_drops(T, E, k, kind):
+    """Reading r19: an index outside [0, E) is dropped (no row, not counted); a token that names one
+    expert in several slots gets one row per slot, in slot order. Both against the sort above."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([912, T, E, k])))
+    lo, hi = (0, E) if kind == "repeat" else (-1, E + 1)
+    if kind == "drop":   # distinct valid experts per token, then a quarter of the slots knocked out
+        idx = random_routing(T, E, min(k, E), (913, T, E, k))
+        knock = g.random(idx.shape) < 0.25
+        idx = np.where(knock, g.choice([-1, E, -7, 1 << 20], idx.shape), idx).astype(np.int32)
+    else:
+        idx = g.integers(lo, hi, (T, k)).astype(np.int32)
+    counts, offsets, ros, sor = oracle.permute_plan(idx, E)
+    w_counts, w_offsets, w_ros, w_sor = plan_by_sorting(idx, E)
+    n = int(offsets[E])
+    assert np.array_equal(counts, w_counts) and np.array_equal(offsets, w_offsets)
+    assert np.array_equal(ros, w_ros)
+    assert np.array_equal(sor[:n], w_sor) and np.all(sor[n:] == -1)
+    valid = (idx.ravel() >= 0) & (idx.ravel() < E)
+    assert n == valid.sum() and np.all(ros[~valid] == -1)
+    # a dropped slot behaves as if the slot were not there: the same rows as the routing with the
+    # token's valid slots only, in the same order
+    if kind == "drop":
+        assert np.array_equal(idx.ravel()[sor[:n]], np.repeat(np.arange(E), counts))
+
+
 def test_permute_rows_round_trip():
     T, H, E, k = 50, 24, 6, 3
     x = normal((T, H), 1.0, (911, 1), "bf16")
@@ -201,7 +242,7 @@ def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.router_topk(np.zeros((2, 3), np.float32), 4)       # k > E
     with pytest.raises(ValueError):
-        oracle.permute_plan(np.array([[0, 7]], np.int32), 4)     # expert index out of range
+        oracle.permute_rows(np.zeros((2, 3), np.float32), np.array([0, -1], np.int32), 1)   # a row with no slot
     with pytest.raises(TypeError):
         oracle.router_logits(np.zeros((2, 2), np.float64), np.zeros((2, 2), np.float64))
 
