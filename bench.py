@@ -67,11 +67,21 @@ def dev(a, torch):
     return torch.from_numpy(a).cuda()
 
 
-def cpu_baseline(wl, d, budget_s: float):
-    """The oracle as it stands on a bounded sample of the workload's tokens: router logits, top-k,
-    then the per-token layer, in chunks until the time budget is used."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(wl, d, budget_s: float):
+    """Tokens/s of the oracle over the first tokens of the workload, in chunks of 32 tokens, until
+    the budget is used: router logits, top-k, then the per-token layer."""
     import oracle
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
     chunk = 32
     done = 0
     t0 = time.perf_counter()
@@ -84,9 +94,80 @@ def cpu_baseline(wl, d, budget_s: float):
                                   d.get("shared_down"))
         done += len(sel)
     el = time.perf_counter() - t0
+    return done, el
+
+
+def _oracle_rate_ep(wl, d, budget_s: float):
+    """Tokens/s of the oracle on one expert-parallel rank's share: each source token's k rows through
+    their experts' FFN, then the weighted combine, 32 source tokens at a time."""
+    import oracle
+    counts = d["counts"]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ntok = wl.ep_rows // wl.k
+    done = 0
+    t0 = time.perf_counter()
+    while done < ntok and time.perf_counter() - t0 < budget_s:
+        toks = np.arange(done, min(ntok, done + 32))
+        rows = d["row_of_slot"][(toks[:, None] * wl.k + np.arange(wl.k)[None, :]).reshape(-1)].astype(np.int64)
+        y = oracle.expert_rows(d["x_perm"], offsets, d["gate_up"], d["down"], rows=rows).astype(np.float32)
+        ros = np.arange(rows.shape[0], dtype=np.int32)
+        oracle.combine(y, ros, d["topk_w"][toks])
+        done += len(toks)
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(wl, d, budget_s: float):
+    """The oracle as it stands, on a bounded sample of the workload: half the budget on all host
+    threads, half on one thread."""
+    import oracle
+    rate = _oracle_rate_ep if wl.ep_rows else _oracle_rate
+    unit_tokens = wl.ep_rows // wl.k if wl.ep_rows else wl.T
+    cores = oracle.max_threads()
+    done, el = rate(wl, d, budget_s / 2)
+    oracle.set_threads(1)
+    try:
+        done1, el1 = rate(wl, d, budget_s / 2)
+    finally:
+        oracle.set_threads(cores)
+    what = ("k expert rows per source token through their SwiGLU experts + combine, fp64" if wl.ep_rows else
+            "router logits + top-k + per-token SwiGLU experts + combine, fp64"
+            f"{', forward only' if wl.backward else ''}")
     return {"value": round(done / el, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {done} of {wl.T} tokens of {wl.name} (router logits + top-k + per-token "
-                      f"SwiGLU experts + combine, fp64{', forward only' if wl.backward else ''}), {el:.1f} s"}
+            "sample": f"first {done} of {unit_tokens} tokens of {wl.name} ({what}), {el:.1f} s on {cores} threads",
+            "one_core": {"value": round(done1 / el1, 2), "unit": "tokens/s", "cores": 1,
+                         "sample": f"first {done1} tokens, {el1:.1f} s on 1 thread"},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def tile_schedule(counts, N_cols, bm=320, bn=256, xcds=8):
+    """The row-grouped GEMMs' tile list as the kernel derives it on the device: an expert with c rows
+    gets ceil(c / bm) row tiles of near-equal height (none when c = 0), each with ceil(N_cols / bn)
+    column tiles; tile L goes to XCD L // Q with Q = ceil(tiles / 8). Returns per-expert tile counts
+    and per-XCD tile counts and row-tile work (rows x columns)."""
+    ntn = (N_cols + bn - 1) // bn
+    rt = [(c + bm - 1) // bm if c > 0 else 0 for c in counts]
+    tiles = []
+    for e, c in enumerate(counts):
+        for j in range(rt[e]):
+            r0, r1 = j * c // rt[e], (j + 1) * c // rt[e]
+            for nt in range(ntn):
+                tiles.append((e, r1 - r0, min(bn, N_cols - nt * bn)))
+    total = len(tiles)
+    Q = (total + xcds - 1) // xcds
+    per_xcd = [0] * xcds
+    work = [0] * xcds
+    for L, (_, rows, cols) in enumerate(tiles):
+        per_xcd[L // Q] += 1
+        work[L // Q] += rows * cols
+    mean_w = sum(work) / xcds if xcds else 0
+    return {"tiles": total, "tiles_per_expert": [r * ntn for r in rt],
+            "empty_experts": int(sum(1 for c in counts if c == 0)),
+            "tiles_of_empty_experts": int(sum(r * ntn for r, c in zip(rt, counts) if c == 0)),
+            "tiles_per_xcd": per_xcd, "xcd_work_max_over_mean": round(max(work) / mean_w, 4) if mean_w else None}
+
+
+def pct(a, q):
+    return round(float(np.percentile(np.asarray(a), q)), 4)
 
 
 def main():
@@ -94,7 +175,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_moe", choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained"])
+    ap.add_argument("--workload", default="qwen3_moe",
+                    choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained", "ep_rank_zipf"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
     ap.add_argument("--ffn-groups", type=int, default=1,
                     help="forward only: the routed FFN as this many expert groups on their own streams in the timed "
@@ -112,6 +194,10 @@ def main():
                          "per-launch host overhead); the per-kernel figures always come from the eager pass")
     ap.add_argument("--no-gather", action="store_true",
                     help="forward: copy the rows to x_perm in the permute instead of gathering them in GEMM-1")
+    ap.add_argument("--separate-routing", action="store_true",
+                    help="forward: moe_router_topk then moe_permute as two calls instead of moe_router_topk_permute")
+    ap.add_argument("--no-mall-cold", dest="mall_cold", action="store_false",
+                    help="skip the per-kernel pass with a 512 MiB write before every call (last-level cache cold)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 512 MiB device copy before the warm-up (counter calibration)")
     args = ap.parse_args()
@@ -130,11 +216,16 @@ def main():
     moe.load_library()
     wl = WORKLOADS[args.workload]
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
-    N = T * k
+    N = wl.N
     t_gen = time.perf_counter()
     d = workload_inputs(wl.name)
     print(f"[bench] {wl.name}: inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
-    x = dev(d["x"], torch)
+    ep = wl.ep_rows > 0
+    if ep:   # one expert-parallel rank's share: the rows arrive grouped; T = source tokens
+        T = wl.ep_rows // k
+        x = dev(d["x_perm"], torch)
+    else:
+        x = dev(d["x"], torch)
     gate_up = dev(d["gate_up"], torch)
     down = dev(d["down"], torch)
     w_gate = dev(d["w_gate"], torch) if "w_gate" in d else None
@@ -146,9 +237,17 @@ def main():
     I_sh = 0 if sh_gu is None else sh_gu.shape[1] // 2
     # forward-only workloads fold the row copy of the permute into the first grouped matmul (it
     # gathers its rows from x); a training step keeps x_perm, which the weight gradients read
-    gather = not wl.backward and not args.no_gather
-    bufs = moe.LayerBuffers(T, H, I, E, k, tdt, x.device, logits=given_logits is None, gu_saved=wl.backward,
-                            I_shared=I_sh, x_perm=not gather)
+    gather = not wl.backward and not args.no_gather and not ep
+    fused_routing = not args.separate_routing
+    bufs = moe.LayerBuffers(T, H, I, E, k, tdt, x.device, logits=given_logits is None and w_gate is not None,
+                            gu_saved=wl.backward, I_shared=I_sh, x_perm=not gather and not ep)
+    if ep:   # the exchange's layout handle, handed straight to the FFN and the combine
+        counts_np = d["counts"].astype(np.int32)
+        bufs.x_perm = x
+        bufs.plan.counts.copy_(torch.from_numpy(counts_np))
+        bufs.plan.offsets.copy_(torch.from_numpy(np.concatenate([[0], np.cumsum(counts_np)]).astype(np.int32)))
+        bufs.plan.row_of_slot.copy_(torch.from_numpy(d["row_of_slot"].astype(np.int32)))
+        bufs.topk_w.copy_(torch.from_numpy(d["topk_w"].astype(np.float32)))
     grads = moe.LayerGrads(T, H, I, E, k, tdt, x.device, I_shared=I_sh, router=w_gate is not None) if wl.backward else None
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
@@ -162,25 +261,25 @@ def main():
     # the stages of one step, in order; HIP events go between them
     sh = bufs.shared
     stages = []
-    if given_logits is None:
+    if given_logits is None and w_gate is not None:
         stages.append(("router_logits", lambda: moe.moe_router_logits(x, w_gate, bufs.logits)))
     logits = bufs.logits if given_logits is None else given_logits
-    stages += [
-        ("router_topk", lambda: moe.moe_router_topk(logits, k, True, bufs.topk_idx, bufs.topk_w)),
-    ]
-    if gather:
-        stages += [
-            ("permute", lambda: moe.moe_permute(x, bufs.topk_idx, E, None, bufs.plan, bufs.workspace, rows=False)),
-            ("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu_gather(x, bufs.plan.slot_of_row, k, gate_up,
-                                                                        bufs.plan.offsets, None, bufs.h,
-                                                                        bufs.gu_saved)),
-        ]
+    if ep:
+        pass
+    elif fused_routing:
+        stages.append(("router_topk_permute", lambda: moe.moe_router_topk_permute(
+            logits, k, x, E, True, bufs.topk_idx, bufs.topk_w, bufs.x_perm, bufs.plan, bufs.workspace,
+            rows=not gather)))
     else:
-        stages += [
-            ("permute", lambda: moe.moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan, bufs.workspace)),
-            ("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu(bufs.x_perm, gate_up, bufs.plan.offsets, bufs.h,
-                                                                 bufs.gu_saved)),
-        ]
+        stages.append(("router_topk", lambda: moe.moe_router_topk(logits, k, True, bufs.topk_idx, bufs.topk_w)))
+        stages.append(("permute", lambda: moe.moe_permute(x, bufs.topk_idx, E, bufs.x_perm, bufs.plan,
+                                                          bufs.workspace, rows=not gather)))
+    if gather:
+        stages.append(("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu_gather(
+            x, bufs.plan.slot_of_row, k, gate_up, bufs.plan.offsets, None, bufs.h, bufs.gu_saved)))
+    else:
+        stages.append(("gemm_gate_up", lambda: moe.moe_grouped_gemm_swiglu(bufs.x_perm, gate_up, bufs.plan.offsets,
+                                                                           bufs.h, bufs.gu_saved)))
     stages.append(("gemm_down", lambda: moe.moe_grouped_gemm_down(bufs.h, down, bufs.plan.offsets, bufs.y)))
     if sh is not None:
         stages.append(("shared_ffn", lambda: moe.moe_grouped_swiglu_ffn(x, sh_gu, sh_dn, sh["offsets"], sh["h"], sh["y"],
@@ -240,6 +339,27 @@ def main():
         total_ev += evs[0].elapsed_time(evs[ns])
     seg /= args.steps
     ms_per_step = max(wall * 1e3 / args.steps, total_ev / args.steps)
+    step_ms = [evs[0].elapsed_time(evs[ns]) for evs in events]
+    seg_med = [float(np.median([evs[i].elapsed_time(evs[i + 1]) for evs in events])) for i in range(ns)]
+    cold_us = None
+    if args.mall_cold:
+        # every call after a 512 MiB write (twice the last-level cache), so its inputs come from HBM;
+        # the same stages in the same order, timed one by one
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=x.device)
+        cold = np.zeros(ns)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ns)] for _ in range(args.steps)]
+        for s_ in range(args.steps):
+            for i, (_, fn) in enumerate(stages):
+                flush.fill_(s_ & 0xff)
+                cev[s_][2 * i].record(stream)
+                fn()
+                cev[s_][2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        for evs in cev:
+            for i in range(ns):
+                cold[i] += evs[2 * i].elapsed_time(evs[2 * i + 1])
+        cold_us = {n: round(cold[i] / args.steps * 1e3, 2) for i, (n, _) in enumerate(stages)}
+        del flush
     one_stream_ms = ms_per_step
     step_us = None
     ffn_groups = max(1, args.ffn_groups)
@@ -306,15 +426,17 @@ def main():
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # an event before every replay and after the last: the per-step distribution
+        rev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            rev[i].record(stream)
             graph.replay()
-        ev1.record(stream)
+        rev[args.steps].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        graph_ms = max(wall * 1e3 / args.steps, ev0.elapsed_time(ev1) / args.steps)
+        step_ms = [rev[i].elapsed_time(rev[i + 1]) for i in range(args.steps)]
+        graph_ms = max(wall * 1e3 / args.steps, rev[0].elapsed_time(rev[args.steps]) / args.steps)
         ms_per_step = graph_ms
     unchunked_ms = ms_per_step
     if args.chunks > 1:
@@ -343,6 +465,7 @@ def main():
 
     counts = bufs.plan.counts.cpu().numpy()
     n_active = int((counts > 0).sum())
+    route_name = "router_topk_permute" if "router_topk_permute" in t_of else ("permute" if "permute" in t_of else None)
     b = 2 if tdt == torch.bfloat16 else 4
     # algorithmic work of each call (what the method must read, write and compute)
     gu_flops = 2.0 * N * H * 2 * I
@@ -351,6 +474,8 @@ def main():
     dn_flops = 2.0 * N * I * H
     dn_bytes = n_active * I * H * b + N * I * b + N * H * b
     perm_bytes = (0 if gather else T * H * b + N * H * b) + T * k * 4 * 3 + E * 4 * 2
+    if route_name == "router_topk_permute":
+        perm_bytes += T * E * 4 + T * k * 8          # the top-k reads the logits, writes indices and weights
     comb_bytes = N * H * b + T * H * b + T * k * 8
     t_gu, t_dn = t_of["gemm_gate_up"], t_of["gemm_down"]
     peak_tf = PEAK_BF16_TFLOPS if tdt == torch.bfloat16 else PEAK_F32_TFLOPS
@@ -374,10 +499,22 @@ def main():
         "gemm_down_tflops": round(dn_flops / t_dn / 1e12, 1),
         "gemm_gate_up_hbm_gbs": round(gu_bytes / t_gu / 1e9, 1),
         "gemm_down_hbm_gbs": round(dn_bytes / t_dn / 1e9, 1),
-        "permute_hbm_gbs": round(perm_bytes / t_of["permute"] / 1e9, 1),
         "combine_hbm_gbs": round(comb_bytes / t_of["combine"] / 1e9, 1),
         "active_experts": n_active,
+        "step_ms_median": pct(step_ms, 50), "step_ms_p10": pct(step_ms, 10), "step_ms_p90": pct(step_ms, 90),
+        "kernel_us_median": {n: round(seg_med[i] * 1e3, 2) for i, n in enumerate(names)},
+        "tile_schedule_gate_up": tile_schedule([int(c) for c in counts], 2 * I),
+        "tile_schedule_down": tile_schedule([int(c) for c in counts], H),
     }
+    if route_name is not None:
+        perf[f"{route_name}_hbm_gbs"] = round(perm_bytes / t_of[route_name] / 1e9, 1)
+    if cold_us is not None:
+        perf["kernel_us_mall_cold"] = cold_us
+        perf["combine_hbm_gbs_mall_cold"] = round(comb_bytes / (cold_us["combine"] * 1e-6) / 1e9, 1)
+        perf["gemm_gate_up_hbm_gbs_mall_cold"] = round(gu_bytes / (cold_us["gemm_gate_up"] * 1e-6) / 1e9, 1)
+        perf["gemm_down_hbm_gbs_mall_cold"] = round(dn_bytes / (cold_us["gemm_down"] * 1e-6) / 1e9, 1)
+        if route_name is not None:
+            perf[f"{route_name}_hbm_gbs_mall_cold"] = round(perm_bytes / (cold_us[route_name] * 1e-6) / 1e9, 1)
     if args.chunks > 1:
         perf["one_shot_ms_per_step"] = round(unchunked_ms, 4)
     if step_us is not None:
@@ -391,9 +528,13 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if tdt == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "I": I, "E": E, "k": k, "renorm": True,
-                   "router": "logits given" if given_logits is not None else "x @ W_g",
+                   "router": ("none: rows arrive grouped by expert" if ep else
+                              "logits given" if given_logits is not None else "x @ W_g"),
+                   "routing_call": (None if ep else "moe_router_topk_permute" if fused_routing else
+                                    "moe_router_topk + moe_permute"),
                    "shared_experts": wl.shared, "pass": "forward+backward" if wl.backward else "forward",
                    "gemm1_rows": "gathered from x" if gather else "x_perm", "chunks": args.chunks,
+                   "rows": N,
                    "ffn_expert_groups": ffn_groups if args.chunks == 1 else 1,
                    "backward_wgrad_cus": args.bwd_wgrad_cus if wl.backward else None,
                    "hip_graph": use_graph},

@@ -66,16 +66,24 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void combine_bwd_kernel(
   for (int j = 0; j < 32; ++j) dot[j] = 0.0f;
   const TE* go = d_out + (int64_t)t * H;
   constexpr int W = VEC ? 8 : 1;
-  for (int c0 = lane * W; c0 < H; c0 += kWave * W) {
+  // every lane runs every iteration (lanes past H only skip their memory accesses), so the
+  // shuffles below always read from active lanes, however few features a lane row covers
+  for (int base = 0; base < H; base += kWave * W) {
+    const int c0 = base + lane * W;
+    const bool act = c0 < H;
     float g[8];
-    if (VEC) load8<TE>(go + c0, g);
-    else g[0] = Elem<TE>::load(go, c0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = 0.0f;
+    if (act) {
+      if (VEC) load8<TE>(go + c0, g);
+      else g[0] = Elem<TE>::load(go, c0);
+    }
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       if (j >= k) break;
       const int r = __shfl(my_row, j, kWave);
       const float w = __shfl(my_w, j, kWave);
-      if (r < 0) continue;
+      if (r < 0 || !act) continue;
       float yv[8], dy[8];
       if (VEC) load8<TE>(y + (int64_t)r * H + c0, yv);
       else yv[0] = Elem<TE>::load(y, (int64_t)r * H + c0);
@@ -106,9 +114,11 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void permute_bwd_kernel(
   if (t >= T) return;
   const int my_row = lane < k ? row_of_slot[(int64_t)t * k + lane] : -1;
   constexpr int W = VEC ? 8 : 1;
-  for (int c0 = lane * W; c0 < H; c0 += kWave * W) {
+  for (int base = 0; base < H; base += kWave * W) {   // uniform trip count: the shuffles read active lanes
+    const int c0 = base + lane * W;
+    const bool act = c0 < H;
     float acc[8];
-    if (d_x_add) {
+    if (d_x_add && act) {
       if (VEC) load8<TE>(d_x_add + (int64_t)t * H + c0, acc);
       else acc[0] = Elem<TE>::load(d_x_add, (int64_t)t * H + c0);
     } else {
@@ -117,13 +127,14 @@ __global__ __launch_bounds__(kBwdWaves * kWave) void permute_bwd_kernel(
     }
     for (int j = 0; j < k; ++j) {
       const int r = __shfl(my_row, j, kWave);
-      if (r < 0) continue;
+      if (r < 0 || !act) continue;
       float v[8];
       if (VEC) load8<TE>(d_x_perm + (int64_t)r * H + c0, v);
       else v[0] = Elem<TE>::load(d_x_perm, (int64_t)r * H + c0);
 #pragma unroll
       for (int i = 0; i < W; ++i) acc[i] += v[i];
     }
+    if (!act) continue;
     if (VEC) store8<TE>(d_x + (int64_t)t * H + c0, acc);
     else Elem<TE>::store(d_x, (int64_t)t * H + c0, acc[0]);
   }

@@ -107,14 +107,16 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_generic_kernel(
   if (t >= T) return;
   const int my_row = lane < k ? row_of_slot[(int64_t)t * k + lane] : -1;
   const float my_w = lane < k ? topk_w[(int64_t)t * k + lane] : 0.0f;
-  for (int c = lane; c < H; c += kWave) {
-    float acc = residual ? Elem<TE>::load(residual, (int64_t)t * H + c) : 0.0f;
+  for (int base = 0; base < H; base += kWave) {   // uniform trip count: the shuffles read active lanes
+    const int c = base + lane;
+    const bool act = c < H;
+    float acc = residual && act ? Elem<TE>::load(residual, (int64_t)t * H + c) : 0.0f;
     for (int j = 0; j < k; ++j) {
       const int r = __shfl(my_row, j, kWave);
       const float w = __shfl(my_w, j, kWave);
-      if (r >= 0) acc = __builtin_fmaf(w, Elem<TE>::load(y, (int64_t)r * H + c), acc);
+      if (r >= 0 && act) acc = __builtin_fmaf(w, Elem<TE>::load(y, (int64_t)r * H + c), acc);
     }
-    Elem<TE>::store(out, (int64_t)t * H + c, acc);
+    if (act) Elem<TE>::store(out, (int64_t)t * H + c, acc);
   }
 }
 

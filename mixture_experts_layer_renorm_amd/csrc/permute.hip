@@ -183,11 +183,13 @@ __global__ __launch_bounds__(kScatterWaves * kWave) void permute_scatter_kernel(
   } else {
     const int64_t n16 = row_bytes >> 1;
     const uint16_t* s2 = reinterpret_cast<const uint16_t*>(src);
-    for (int64_t i = lane; i < n16; i += kWave) {
-      const uint16_t v = s2[i];
+    for (int64_t base = 0; base < n16; base += kWave) {   // uniform trip count: the shuffles read active lanes
+      const int64_t i = base + lane;
+      const bool act = i < n16;
+      const uint16_t v = act ? s2[i] : 0;
       for (int j = 0; j < k; ++j) {
         const int r = __shfl(my_row, j, kWave);
-        if (r >= 0) reinterpret_cast<uint16_t*>(x_perm + (int64_t)r * row_bytes)[i] = v;
+        if (r >= 0 && act) reinterpret_cast<uint16_t*>(x_perm + (int64_t)r * row_bytes)[i] = v;
       }
     }
   }

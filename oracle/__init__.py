@@ -77,6 +77,17 @@ def _call(name, *args):
 I64 = ctypes.c_int64
 
 
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (independent tokens / rows)."""
+    _load().orc_set_threads(ctypes.c_int(int(n)))
+
+
+def max_threads() -> int:
+    f = _load().orc_max_threads
+    f.restype = ctypes.c_int
+    return int(f())
+
+
 def router_logits(x: np.ndarray, w_gate: np.ndarray) -> np.ndarray:
     x, w_gate = _c(x), _c(w_gate)
     T, H = x.shape

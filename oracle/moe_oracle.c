@@ -26,6 +26,17 @@ static inline double eld(const void* p, int dt, int64_t i) { return (double)elf(
 
 static int bad_dt(int dt) { return dt != ORC_F32 && dt != ORC_BF16; }
 
+#ifdef _OPENMP
+#include <omp.h>
+void orc_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+}
+int orc_max_threads(void) { return omp_get_max_threads(); }
+#else
+void orc_set_threads(int n) { (void)n; }
+int orc_max_threads(void) { return 1; }
+#endif
+
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 

@@ -28,6 +28,10 @@
 extern "C" {
 #endif
 
+/* Threads the OpenMP loops below use (n > 0), and the current maximum. */
+void orc_set_threads(int n);
+int orc_max_threads(void);
+
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 
 /* logits[t*E+e] = fp32 chain: acc = 0; for h = 0..H-1: acc = fmaf(x[t,h], w_gate[h,e], acc) */

@@ -19,7 +19,7 @@ pytestmark = [pytest.mark.gpu,
 @pytest.mark.parametrize("T,H,k,dtype", [(64, 64, 2, "f32"), (500, 2048, 8, "bf16"), (77, 136, 3, "bf16"),
                                          (5, 40, 1, "bf16"), (33, 7168, 8, "bf16"), (31, 20, 4, "f32"),
                                          (100, 2048, 9, "bf16"), (40, 136, 16, "bf16"), (21, 256, 32, "bf16"),
-                                         (9, 24, 32, "f32")])
+                                         (9, 24, 32, "f32"), (13, 12, 32, "bf16"), (7, 5, 20, "f32")])
 def test_combine_bwd(T, H, k, dtype):
     N = T * k + 3                                  # three rows no slot points at: left untouched
     g = generator((970, T, H, k))
@@ -47,7 +47,8 @@ def test_combine_bwd(T, H, k, dtype):
                                              (77, 136, 3, "bf16", False), (5, 40, 1, "bf16", True),
                                              (33, 7168, 8, "bf16", True), (31, 20, 4, "f32", True),
                                              (100, 2048, 9, "bf16", True), (40, 136, 16, "bf16", False),
-                                             (21, 256, 32, "bf16", True), (9, 24, 32, "f32", False)])
+                                             (21, 256, 32, "bf16", True), (9, 24, 32, "f32", False),
+                                             (13, 12, 32, "bf16", True), (7, 5, 20, "f32", True)])
 def test_permute_bwd(T, H, k, dtype, add):
     N = T * k
     g = generator((973, T, H, k))

@@ -126,12 +126,13 @@ def routing_repeats_drops(T, E, k, key, drop):
     if drop:
         knock = g.random((T, k)) < 0.2
         idx = np.where(knock, g.choice(np.array([-1, E, -5, 1 << 24]), (T, k)), idx).astype(np.int32)
+        idx[0, 0] = -1
     return idx
 
 
-@pytest.mark.parametrize("T,H,E,k,drop", [(300, 40, 8, 4, False), (257, 64, 16, 8, True), (64, 16, 1, 3, False),
-                                          (1000, 24, 128, 8, True), (129, 8, 4, 32, True), (70, 48, 1024, 5, True),
-                                          (2, 16, 3, 2, True)])
+@pytest.mark.parametrize("T,H,E,k,drop", [(300, 40, 8, 4, False), (257, 64, 16, 8, True), (64, 16, 3, 3, False),
+                                          (1000, 24, 128, 8, True), (129, 8, 32, 32, True), (70, 48, 1024, 5, True),
+                                          (2, 16, 3, 2, True), (50, 3, 40, 32, True)])
 def test_permute_repeats_and_drops(T, H, E, k, drop):
     """Reading r19 through moe_permute: out-of-range indices get no row and are not counted; repeated
     experts get one row per slot in (expert, token, slot) order. Rows past offsets[E] are untouched."""
@@ -229,7 +230,8 @@ def test_grouped_swiglu_ffn(counts, H, I, dtype):
                                              (77, 136, 3, "bf16", False), (5, 40, 1, "bf16", True),
                                              (300, 7168, 8, "bf16", False), (31, 20, 4, "f32", True),
                                              (200, 2048, 9, "bf16", True), (65, 136, 16, "bf16", False),
-                                             (33, 256, 32, "bf16", True), (17, 40, 32, "f32", False)])
+                                             (33, 256, 32, "bf16", True), (17, 40, 32, "f32", False),
+                                             (19, 20, 32, "f32", True), (23, 12, 16, "bf16", False)])
 def test_unpermute_combine(T, H, k, dtype, res):
     N = T * k
     g = generator((958, T, H, k))
