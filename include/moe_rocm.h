@@ -120,6 +120,18 @@ moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t*
                        void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
                        int32_t* slot_of_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* moe_permute without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments and
+ * results as moe_permute; its scratch (the per-chunk expert counts) is a fixed 1 MiB device array
+ * inside the library, one per GPU, held until the process ends. Limit: ceil(T/64) * E <= 262144
+ * (e.g. T <= 131072 at E = 128, T <= 16384 at E = 1024), else MOE_ERR_WORKSPACE. The call allocates
+ * nothing; its first call on a device looks the array's address up. Every call on one GPU shares the
+ * array: calls that overlap on one GPU (concurrent streams, threads) race and must be ordered by the
+ * caller.                                                                                            */
+moe_status moe_permute_noalloc(const void* x, moe_dtype dt, int T, int H, const int32_t* topk_idx, int k, int E,
+                               void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                               int32_t* slot_of_row, hipStream_t stream);
+
 /* (2)+(3) in one call: the selection and weights of moe_router_topk, then the layout handle (and
  * x_perm unless NULL) of moe_permute, with the same results bit for bit. For E <= 256 the top-k
  * kernel also counts each 64-token chunk's expert choices, so the permute skips its counting pass.

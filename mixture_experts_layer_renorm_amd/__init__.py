@@ -49,6 +49,7 @@ def load_library() -> ctypes.CDLL:
             "moe_router_stats": (I, [P, P, I, I, I, P, P, P, P, Z, P]),
             "moe_permute_workspace_bytes": (Z, [I, I, I]),
             "moe_permute": (I, [P, I, I, I, P, I, I, P, P, P, P, P, P, Z, P]),
+            "moe_permute_noalloc": (I, [P, I, I, I, P, I, I, P, P, P, P, P, P]),
             "moe_router_topk_permute": (I, [P, I, I, I, I, P, P, P, I, I, P, P, P, P, P, P, Z, P]),
             "moe_grouped_swiglu_ffn": (I, [P, P, P, I, I, I, I, I, P, P, P, P, P]),
             "moe_grouped_gemm_swiglu": (I, [P, P, I, I, I, I, I, P, P, P, P]),
@@ -201,6 +202,28 @@ def moe_permute(x, topk_idx, E, x_perm=None, plan=None, workspace=None, stream=N
                                       _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "moe_permute")
     return x_perm, plan
+
+
+def moe_permute_noalloc(x, topk_idx, E, x_perm, plan, stream=None, rows=True):
+    """moe_permute with the library's fixed device scratch instead of a workspace: allocates
+    nothing, so every output (x_perm unless rows=False, the four plan arrays) is passed in."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    _need(x, "x"), _need(topk_idx, "topk_idx", torch.int32, (T, k))
+    N = T * k
+    if rows:
+        _need(x_perm, "x_perm", x.dtype)
+        if x_perm.shape[0] < N or x_perm.shape[1] != H:
+            raise ValueError("x_perm must hold [T*k, H] rows")
+    for t, n in [(plan.counts, E), (plan.offsets, E + 1), (plan.row_of_slot, N), (plan.slot_of_row, N)]:
+        _need(t, "plan", torch.int32)
+        if t.numel() < n:
+            raise ValueError("plan arrays too small")
+    _check(load_library().moe_permute_noalloc(_ptr(x), _dt(x), T, H, _ptr(topk_idx), k, E,
+                                              _ptr(x_perm) if rows else None, _ptr(plan.counts), _ptr(plan.offsets),
+                                              _ptr(plan.row_of_slot), _ptr(plan.slot_of_row), _stream(stream)),
+           "moe_permute_noalloc")
+    return x_perm if rows else None, plan
 
 
 def moe_router_topk_permute(logits, k, x, E=None, renorm=True, topk_idx=None, topk_w=None, x_perm=None, plan=None,

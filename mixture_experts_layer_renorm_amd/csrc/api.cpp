@@ -126,6 +126,37 @@ moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t*
                     "moe_permute");
 }
 
+moe_status moe_permute_noalloc(const void* x, moe_dtype dt, int T, int H, const int32_t* topk_idx, int k, int E,
+                               void* x_perm, int32_t* counts, int32_t* offsets, int32_t* row_of_slot,
+                               int32_t* slot_of_row, hipStream_t stream) {
+  const char* fn = "moe_permute_noalloc";
+  REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  REQUIRE(T >= 0 && H >= 0, MOE_ERR_INVALID_ARG, "%s: T=%d H=%d must be >= 0", fn, T, H);
+  REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  REQUIRE(k >= 1 && k <= E && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, min(E=%d, %d)]", fn, k, E,
+          kMaxK);
+  REQUIRE((int64_t)T * k <= 0x7fffffffLL, MOE_ERR_INVALID_ARG, "%s: T*k overflows int32", fn);
+  const int64_t need = (int64_t)moe::permute_nchunks(T) * E;
+  REQUIRE(need <= moe::kPermuteScratchInts, MOE_ERR_WORKSPACE,
+          "%s: ceil(T/64)*E = %lld chunk counts exceed the fixed scratch of %lld (T=%d E=%d); use moe_permute with a "
+          "workspace",
+          fn, (long long)need, (long long)moe::kPermuteScratchInts, T, E);
+  REQUIRE(counts && offsets, MOE_ERR_INVALID_ARG, "%s: null counts/offsets", fn);
+  if (T == 0) {
+    hipError_t e = moe::launch_fill_i32(counts, E, 0, stream);
+    if (e == hipSuccess) e = moe::launch_fill_i32(offsets, E + 1, 0, stream);
+    return hip_status(e, fn);
+  }
+  REQUIRE(topk_idx && row_of_slot && slot_of_row, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  REQUIRE(!x_perm || x, MOE_ERR_INVALID_ARG, "%s: x is NULL but x_perm is not", fn);
+  int32_t* scratch = nullptr;
+  hipError_t e = moe::permute_noalloc_scratch(&scratch);
+  if (e == hipSuccess)
+    e = moe::launch_permute(x, (int)dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot, slot_of_row,
+                            scratch, stream);
+  return hip_status(e, fn);
+}
+
 moe_status moe_router_topk_permute(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
                                    float* topk_w, const void* x, moe_dtype dt, int H, void* x_perm, int32_t* counts,
                                    int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row, void* workspace,

@@ -27,6 +27,10 @@ constexpr int kPermuteChunk = 64;   // tokens per plan chunk (64 measured faster
 inline int permute_nchunks(int T) { return (T + kPermuteChunk - 1) / kPermuteChunk; }
 inline size_t permute_workspace_bytes(int T, int E) { return (size_t)permute_nchunks(T) * (size_t)E * sizeof(int32_t); }
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+// allocation-free permute: its chunk counts in a fixed device array of kPermuteScratchInts int32
+// (1 MiB) per GPU; *out = this device's address of it (looked up once per device)
+constexpr int64_t kPermuteScratchInts = 1 << 18;
+hipError_t permute_noalloc_scratch(int32_t** out);
 hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,
                           int32_t* chunk_counts, hipStream_t s);

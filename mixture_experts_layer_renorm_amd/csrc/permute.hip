@@ -14,6 +14,8 @@
 //     (The router's top-k kernel can produce the counts of step 1 itself: launch_permute_counted.)
 //  3. scatter: one wave per token copies x[t] (read once) to its k rows of x_perm.
 // Slots whose expert index is outside [0, E) get no row (row_of_slot = -1).
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -235,6 +237,34 @@ hipError_t launch_permute_counted(const void* x, int dt, int T, int H, const int
                                   int32_t* slot_of_row, const int32_t* chunk_counts, hipStream_t s) {
   return plan_and_scatter(x, dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot, slot_of_row,
                           chunk_counts, s);
+}
+
+// ---- the allocation-free permute's scratch ---------------------------------------------------
+// The per-chunk expert counts of moe_permute_noalloc live in this file-scope device array instead
+// of a caller workspace: each GPU holds its own copy for the life of the process, and every call on
+// that GPU shares it (the count kernel rewrites every entry the plan reads, so nothing needs
+// clearing; calls that overlap on one GPU race on it). Host code never passes the array's name to
+// a kernel: that is a host-side stand-in, not the device address. The device address is looked up
+// with hipGetSymbolAddress once per device, with that device current, and kept.
+static __device__ __align__(256) int32_t scratch[kPermuteScratchInts];
+
+hipError_t permute_noalloc_scratch(int32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = (int32_t*)p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moe
