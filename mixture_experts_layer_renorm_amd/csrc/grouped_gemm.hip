@@ -1299,8 +1299,568 @@ __global__ __launch_bounds__(256) void grouped_ffn2_f32_kernel(const float* __re
   y[(int64_t)r * H + c] = acc;
 }
 
+// 16 bytes per lane from rsrc + voff into LDS at lds + IMM + 16 * lane; the immediate keeps one
+// scalar register per LDS buffer instead of one per DMA instruction. The add writes SCC, which the
+// clobber list must say: the compiler keeps loop conditions in SCC across code like this.
+template <int IMM>
+__device__ __forceinline__ void dma_16i(const i32x4& rsrc, int voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds),
+               "n"(IMM)
+               : "memory", "m0", "scc");
+}
+
+// ---------------------------------------------------------------------------------------------
+// Forward row-grouped products, persistent: gate_up + SwiGLU (EPI = kEpiSwiglu) and down
+// (EPI = kEpiStore), the rows from the grouped buffer or (GATHER) from the token matrix through
+// the slot map.
+//
+// One workgroup per CU walks a slice of the same tile list as grouped_gemm_bf16_kernel, with the
+// same split over the XCDs (XCD x owns the contiguous range [x Q, (x+1) Q); its workgroups take
+// those tiles in turn). Per tile the K loop is the one above. What changes is the tile boundary,
+// where the one-tile kernel leaves every CU idle at once (set-up, pipeline fill, epilogue):
+//  - the tile list is built once per workgroup (expert offsets and row-tile prefix in LDS);
+//  - the last three K steps issue the next tile's first A stage and B steps 0-2 (where the
+//    one-tile kernel issues zero-filling DMAs past K), so the next tile's data is on its way
+//    during the epilogue;
+//  - the epilogue stages the finished tile through the A stage the last two steps used, one
+//    64-row quarter at a time, and writes whole rows with buffer stores. Every wave issues the
+//    same number of stores (rows past the tile are dropped by the descriptor), and the stores
+//    are issued after the prefetches, so the next tile's first wait leaves exactly them in
+//    flight: they drain while the next tile computes;
+//  - with gathered rows, the slot map of the next tile's rows is brought into LDS by one DMA of
+//    wave 0 in the current tile's first step.
+template <int EPI, bool GATHER>
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const GemmArgs g) {
+  static_assert(EPI == kEpiSwiglu || EPI == kEpiStore, "the forward epilogues");
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA2], sA1[kTileA2];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
+  __shared__ __attribute__((aligned(1024))) int s_slot[512];  // slot map of the next tile's rows (gathered)
+  __shared__ int s_off[kGemmMaxE + 1];
+  __shared__ int s_pref[kGemmMaxE + 1];
+  __shared__ int s_wtot[kGemmThreads / kWave];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = (wave >> 1) & 3, wn = wave & 1;
+
+  // ---- the tile list: expert e owns ceil(c_e / kBMX) row tiles of near-equal height, each with
+  // ntiles_n column tiles; s_pref = exclusive prefix of the row tiles over the experts
+  for (int i = tid; i <= g.E; i += kGemmThreads) s_off[i] = g.offsets[i];
+  __syncthreads();
+  for (int e = tid; e < g.E; e += kGemmThreads) {
+    const int c = s_off[e + 1] - s_off[e];
+    s_pref[e] = c > 0 ? (c + kBMX - 1) / kBMX : 0;
+  }
+  __syncthreads();
+  block_exclusive_scan<kGemmThreads>(s_pref, g.E, s_wtot);
+  const int ntn = g.ntiles_n;
+  const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]) * ntn;
+  const int xcd = blockIdx.x & 7;
+  const int nbx = (int)(gridDim.x >> 3);  // workgroups per XCD (the grid is a multiple of 8)
+  const int Q = (total + 7) >> 3;
+  const int t_end = min((xcd + 1) * Q, total);
+  int L = xcd * Q + (int)(blockIdx.x >> 3);
+  if (L >= t_end) return;
+
+  struct Tile {
+    int e, m0, mvalid, nt;
+  };
+  // (32-bit arithmetic on operands the compiler cannot see through: it would otherwise hoist the
+  // division constants out of the tile loop and keep them in registers through every K loop)
+  auto decode = [&](int LL, Tile& t) {
+    int dn;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(dn) : "s"(ntn));
+    const int mt_g = (int)((uint32_t)LL / (uint32_t)dn);
+    t.nt = __builtin_amdgcn_readfirstlane(LL - mt_g * dn);
+    int lo = 0, hi = g.E;  // the last expert whose row tiles start at or before mt_g
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= mt_g)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int p0 = __builtin_amdgcn_readfirstlane(s_pref[e]);
+    const int nte = __builtin_amdgcn_readfirstlane(s_pref[e + 1]) - p0;
+    const int o0 = __builtin_amdgcn_readfirstlane(s_off[e]);
+    const int c = __builtin_amdgcn_readfirstlane(s_off[e + 1]) - o0;
+    // the expert's c rows in nte contiguous pieces, the first c % nte one row longer
+    const int j = mt_g - p0;
+    const int base = (int)((uint32_t)c / (uint32_t)nte), rem = c - base * nte;
+    t.e = e;
+    t.m0 = __builtin_amdgcn_readfirstlane(o0 + j * base + min(j, rem));
+    t.mvalid = __builtin_amdgcn_readfirstlane(base + (j < rem ? 1 : 0));
+  };
+
+  // ---- operand DMAs (inline assembly, so that only the explicit waits below order them)
+  const int K = g.K;
+  const int a_c0 = (lane & 7) ^ swz_a2(lane >> 3);
+  const int a_kc[2] = {a_c0 * 8, (a_c0 ^ 1) * 8};
+  const int x_r = kBM + wave * 8 + (lane >> 3);       // extra-band row of this DMA lane
+  const int x_kc = ((lane & 7) ^ swz_a2(x_r)) * 8;
+  struct Ops {
+    i32x4 rsA, rsB;
+    int a_off[kDmaA2];   // byte offsets for k = 0 (kOutOfRange: no row)
+    int x_off;
+    int b_off[kDmaB];
+    int band;            // the tile has rows in the extra band: one more DMA per A stage
+  };
+  // slots: the tile's slot map (LDS), for gathered rows
+  auto set_ops = [&](const Tile& t, const int* slots, Ops& o) {
+    int zo;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zo));
+    const int lane = (int)(threadIdx.x & (kWave - 1)) + zo;
+    if constexpr (GATHER) {
+      o.rsA = buffer_rsrc(g.A, g.M * g.lda * 2);
+    } else {
+      o.rsA = buffer_rsrc(g.A + (int64_t)t.m0 * g.lda, t.mvalid * g.lda * 2);
+    }
+    o.rsB = buffer_rsrc(g.B + (int64_t)t.e * g.b_expert, g.b_rows * g.ldb * 2);
+#pragma unroll
+    for (int i = 0; i < kDmaA2; ++i) {
+      const int r = (wave * kDmaA2 + i) * 8 + (lane >> 3);
+      const int c = a_c0 ^ (i & 1);
+      if constexpr (GATHER)
+        o.a_off[i] = r < t.mvalid ? (slots[r] / g.a_div * g.lda + c * 8) * 2 : kOutOfRange;
+      else
+        o.a_off[i] = (r * g.lda + c * 8) * 2;
+    }
+    const int xc = x_kc / 8;
+    if constexpr (GATHER)
+      o.x_off = x_r < t.mvalid ? (slots[x_r] / g.a_div * g.lda + xc * 8) * 2 : kOutOfRange;
+    else
+      o.x_off = (x_r * g.lda + xc * 8) * 2;
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) {
+      const int kr = (wave * kDmaB + i) * 2 + (lane >> 5);
+      const int cb = (lane & 31) ^ swz_b(kr);
+      int col;
+      bool ok;
+      if constexpr (EPI == kEpiSwiglu) {  // 128 gate columns then the matching 128 up columns
+        const int j = t.nt * 128 + (cb & 15) * 8;
+        ok = j < g.N;
+        col = (cb < 16 ? 0 : g.N) + j;
+      } else {
+        col = t.nt * kBN + cb * 8;
+        ok = col < g.N;
+      }
+      o.b_off[i] = ok ? (kr * g.ldb + col) * 2 : kOutOfRange;
+    }
+    o.band = __builtin_amdgcn_readfirstlane(t.mvalid > kBM ? 1 : 0);
+  };
+  // A stage st (K 64 st .. 64 st + 63) into sa; B step kt (K 32 kt .. 32 kt + 31) into sb.
+  // Offsets are unsigned: a missing row's kOutOfRange plus k may pass 2^31 and stays out of range.
+  static_assert(kDmaA2 == 4 && kDmaB == 2, "DMA instruction counts per wave");
+  const uint32_t wa = __builtin_amdgcn_readfirstlane(wave * kDmaA2 * 1024);
+  const uint32_t wx = __builtin_amdgcn_readfirstlane(kBM * kBK2 * 2 + wave * 1024);
+  const uint32_t wb = __builtin_amdgcn_readfirstlane(wave * kDmaB * 1024);
+  auto dma_a = [&](const Ops& o, int st, uint8_t* sa) {
+    const int k0 = st * kBK2;
+    const uint32_t base = lds_addr(sa) + wa;
+    if (o.band) {
+      const int off = k0 + x_kc < K ? (int)((uint32_t)o.x_off + (uint32_t)(k0 * 2)) : kOutOfRange;
+      dma_16i<0>(o.rsA, off, lds_addr(sa) + wx);
+    }
+    int off[kDmaA2];
+#pragma unroll
+    for (int i = 0; i < kDmaA2; ++i)
+      off[i] = k0 + a_kc[i & 1] < K ? (int)((uint32_t)o.a_off[i] + (uint32_t)(k0 * 2)) : kOutOfRange;
+    dma_16i<0>(o.rsA, off[0], base);
+    dma_16i<1024>(o.rsA, off[1], base);
+    dma_16i<2048>(o.rsA, off[2], base);
+    dma_16i<3072>(o.rsA, off[3], base);
+  };
+  auto dma_b = [&](const Ops& o, int kt, uint8_t* sb) {
+    const int kb = kt * kBK * g.ldb * 2;  // k-rows past K are past the expert's block
+    const uint32_t base = lds_addr(sb) + wb;
+    const int off0 = o.b_off[0] == kOutOfRange ? kOutOfRange : o.b_off[0] + kb;
+    const int off1 = o.b_off[1] == kOutOfRange ? kOutOfRange : o.b_off[1] + kb;
+    dma_16i<0>(o.rsB, off0, base);
+    dma_16i<1024>(o.rsB, off1, base);
+  };
+  // wave 0: the slot map of tile t's rows into s_slot (entries past the tile read as zero)
+  auto dma_slots = [&](const Tile& t) {
+    if constexpr (GATHER) {
+      if (wave == 0) {
+        int zs;  // (computed here, not kept from the kernel's start)
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zs));
+        const int lo = (lane + zs) * 16;
+        const i32x4 rs = buffer_rsrc(g.a_slot + t.m0, t.mvalid * 4);
+        dma_16i<0>(rs, lo, lds_addr(s_slot));
+        dma_16i<1024>(rs, lo + 1024, lds_addr(s_slot));
+      }
+    }
+  };
+
+  // ---- fragment addresses (as in grouped_gemm_bf16_kernel)
+  int bcol[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    bcol[nb] = EPI == kEpiSwiglu ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
+  const int q = lane >> 4, sl = lane & 15;
+  auto arow_rd = [&](int r, int kk) {
+    const int c = kk * 2 + (lane >> 5);
+    return r * (kBK2 * 2) + ((c ^ swz_a2(r)) << 4);
+  };
+  auto krow_rd = [&](int col32) {
+    const int kr = (q >> 1) * 8 + (sl >> 2);
+    const int col = col32 + (q & 1) * 16 + 4 * (sl & 3);
+    return kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+  };
+  int a_rd[2][2], b_rd[4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) a_rd[kk][mb] = arow_rd(wm * 64 + mb * 32 + (lane & 31), kk);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) b_rd[nb] = krow_rd(bcol[nb]);
+  const int g0 = (wn * 4 + wm) * 16;
+  int xa_rd[2], xb_rd;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) xa_rd[kk] = arow_rd(kBM + (lane & 31), kk);
+  if constexpr (EPI == kEpiSwiglu) {
+    const int kr = (q >> 1) * 8 + (sl >> 2);
+    const int col = (q & 1) * 128 + g0 + 4 * (sl & 3);
+    xb_rd = kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+  } else {
+    xb_rd = krow_rd(wn * 128 + wm * 32);
+  }
+
+  f32x16 acc[2][4];
+  struct Frags {
+    bf16x8 a[2], b[4], xa[2], xb;
+  };
+  auto frag_b = [&](const uint8_t* base, int rd, int kk) -> bf16x8 {
+    const uint8_t* p = base + rd + kk * 8192;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2048));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto read_frags = [&](auto nmb_c, auto nx_c, const uint8_t* sa, const uint8_t* sb, int kk, int AX, Frags& f) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    constexpr int NX = decltype(nx_c)::value;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) f.b[nb] = frag_b(sb, b_rd[nb], kk);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(sa + (a_rd[kk][mb] ^ AX));
+    if constexpr (NX > 0) {
+#pragma unroll
+      for (int xb = 0; xb < NX; ++xb)
+        f.xa[xb] = *reinterpret_cast<const bf16x8*>(sa + xb * 32 * kBK2 * 2 + (xa_rd[kk] ^ AX));
+      f.xb = frag_b(sb, xb_rd, kk);
+    }
+  };
+  auto mfmas = [&](auto nmb_c, auto nx_c, const Frags& f, f32x16* acc_x) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    constexpr int NX = decltype(nx_c)::value;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+    for (int xb = 0; xb < NX; ++xb)
+      acc_x[xb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb, f.xa[xb], acc_x[xb], 0, 0, 0);
+  };
+  // The waits at the end of a step: the DMAs of step kt + 1 must have landed. Newer than those:
+  // after P = 0: B kt + 2, this step's A stage (kDmaA2 + band) and B kt + 3; after P = 1: B kt + 2
+  // and B kt + 3. (A stage of step kt + 1 went out at step kt - 1 with B kt + 2 after it.)
+  auto wait_p0 = [&](int band) {
+    if (band)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaB + kDmaA2 + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaB + kDmaA2) : "memory");
+  };
+  // One step kt (P = kt % 2) computing from sa / sb; `io` are the operands of the DMAs this step
+  // issues: at P = 0 A stage ast into pa; B step bst into pb. LAST: the tile's last step, whose
+  // end waits for nothing (its successors' DMAs belong to the next tile).
+  auto step = [&](auto nmb_c, auto x_c, auto p_c, f32x16* acc_x, const Ops& io, int ast, int bst, const uint8_t* sa,
+                  const uint8_t* sb, uint8_t* pa, uint8_t* pb, bool last) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    constexpr int NX = decltype(x_c)::value;
+    constexpr int P = decltype(p_c)::value;
+    constexpr int AX = P * 64;
+    auto issue = [&]() {
+      if constexpr (P == 0) dma_a(io, ast, pa);
+      dma_b(io, bst, pb);
+    };
+    if constexpr (NMB == 0) {
+      issue();
+    } else if constexpr (NX > 0) {
+      Frags f;
+      read_frags(nmb_c, x_c, sa, sb, 0, AX, f);
+      issue();
+      mfmas(nmb_c, x_c, f, acc_x);
+      read_frags(nmb_c, x_c, sa, sb, 1, AX, f);
+      mfmas(nmb_c, x_c, f, acc_x);
+    } else {
+      Frags f0, f1;
+      read_frags(nmb_c, x_c, sa, sb, 0, AX, f0);
+      read_frags(nmb_c, x_c, sa, sb, 1, AX, f1);
+      issue();
+      mfmas(nmb_c, x_c, f0, acc_x);
+      mfmas(nmb_c, x_c, f1, acc_x);
+    }
+    if (last)
+      asm volatile("s_barrier" ::: "memory");
+    else if constexpr (P == 0)
+      wait_p0(io.band);
+    else
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaB) : "memory");
+  };
+
+  // ---- the walk
+  Tile cur;
+  decode(L, cur);
+  Ops ops;
+  if constexpr (GATHER) {  // the first tile's slot map straight from global memory
+    int* tmp = s_slot;
+    for (int i = tid; i < kBMX; i += kGemmThreads) tmp[i] = i < cur.mvalid ? g.a_slot[cur.m0 + i] : 0;
+    __syncthreads();
+  }
+  set_ops(cur, s_slot, ops);
+  __syncthreads();  // every wave has read the slot map before it is overwritten
+  dma_a(ops, 0, sA0);
+  dma_b(ops, 0, sB0);
+  dma_b(ops, 1, sB1);
+  dma_b(ops, 2, sB2);
+  int pending_stores = 0;  // stores of the previous tile's epilogue still counted in vmcnt
+  const int KT = (K + kBK - 1) / kBK;
+  const int KT4 = max(kStages, (KT + kStages - 1) / kStages * kStages);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  constexpr int kEpiStores = EPI == kEpiStore ? 16 : 8;  // buffer stores per wave per epilogue
+  while (true) {
+    const int Ln = L + nbx;
+    const bool has_next = Ln < t_end;
+    // A stage 0 and B step 0 of this tile have landed (B 1, B 2 and the previous epilogue's
+    // stores may still be in flight)
+    if (pending_stores)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaB + kEpiStores) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kDmaB) : "memory");
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int qq = 0; qq < 16; ++qq) acc[mb][nb][qq] = 0.0f;
+    f32x16 acc_x[2];
+#pragma unroll
+    for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+      for (int qq = 0; qq < 16; ++qq) acc_x[xb][qq] = 0.0f;
+
+    // K loop of this tile; the last four steps switch the DMA operands to the next tile after
+    // their first step (a tile without a successor keeps its own operands: zero-filling DMAs)
+    auto run = [&](auto nmb_c, auto x_c) {
+      if (GATHER && has_next) {  // older than step 0's DMAs: step 1's wait covers it
+        Tile nx;
+        decode(Ln, nx);
+        dma_slots(nx);
+      }
+      for (int kt = 0; kt < KT4 - kStages; kt += kStages) {
+        step(nmb_c, x_c, P0{}, acc_x, ops, kt / 2 + 1, kt + 3, sA0, sB0, sA1, sB3, false);
+        step(nmb_c, x_c, P1{}, acc_x, ops, 0, kt + 4, sA0, sB1, nullptr, sB0, false);
+        step(nmb_c, x_c, P0{}, acc_x, ops, kt / 2 + 2, kt + 5, sA1, sB2, sA0, sB1, false);
+        step(nmb_c, x_c, P1{}, acc_x, ops, 0, kt + 6, sA1, sB3, nullptr, sB2, false);
+      }
+      const int kt = KT4 - kStages;
+      step(nmb_c, x_c, P0{}, acc_x, ops, kt / 2 + 1, kt + 3, sA0, sB0, sA1, sB3, false);
+      // the slot map DMA is only known to have landed after step 1's wait; with one group of four
+      // steps (K <= 128) wait for it here
+      if (GATHER && has_next && kt == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      Tile nxt = cur;
+      if (has_next) {
+        decode(Ln, nxt);
+        set_ops(nxt, s_slot, ops);
+      }
+      const int o = has_next ? KT4 : 0;  // the next tile's steps 0..2 (or zero fills past K)
+      step(nmb_c, x_c, P1{}, acc_x, ops, 0, kt + 4 - o, sA0, sB1, nullptr, sB0, false);
+      step(nmb_c, x_c, P0{}, acc_x, ops, kt / 2 + 2 - o / 2, kt + 5 - o, sA1, sB2, sA0, sB1, false);
+      step(nmb_c, x_c, P1{}, acc_x, ops, 0, kt + 6 - o, sA1, sB3, nullptr, sB2, true);
+      if constexpr (decltype(x_c)::value > 0) {
+        int zx;  // (an opaque lane id: the band's store addresses are not hoisted out of the tile loop)
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zx));
+#pragma unroll
+        for (int xb = 0; xb < decltype(x_c)::value; ++xb)
+          store_extra<EPI>(g, acc_x[xb], xb, cur.m0, cur.mvalid, cur.nt * kBN, cur.nt, g0, wm, wn, lane + zx);
+      }
+      return nxt;
+    };
+    using F = std::integral_constant<int, 0>;
+    Tile nxt;
+    if (cur.mvalid > kBM) {
+      if (cur.mvalid > kBM + 32)
+        nxt = run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+      else
+        nxt = run(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+    } else {
+      const int wrows = cur.mvalid - wm * 64;
+      const int nmb = __builtin_amdgcn_readfirstlane(wrows <= 0 ? 0 : min(2, (wrows + 31) / 32));
+      switch (nmb) {
+        case 2: nxt = run(std::integral_constant<int, 2>{}, F{}); break;
+        case 1: nxt = run(std::integral_constant<int, 1>{}, F{}); break;
+        default: nxt = run(std::integral_constant<int, 0>{}, F{}); break;
+      }
+    }
+
+    // ---- epilogue: 64-row quarters through sA1 (free after the last step's barrier; the
+    // prefetches went to sA0 and sB0..sB2). Lane holds row (lane & 31) of each 32-row block and,
+    // per 32-column block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for element q. The lane
+    // terms are built from a value the compiler cannot see through, so that they are computed
+    // here rather than hoisted out of the tile loop (where they would stay live through K).
+    int zv;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zv));
+    const int lane_e = lane + zv;
+    const int lr = lane_e & 31;
+    if constexpr (EPI == kEpiStore) {
+      // rounded to bf16 first, so that the quarter loop keeps 64 packed registers live, not the
+      // 128 accumulators; quarter qb = rows 64 qb .. +63 (waves 2 qb, 2 qb + 1), 512-byte rows in
+      // sA1, 16-byte chunk c of row r at chunk c ^ (r & 31); then every wave writes 8 rows, 2 per
+      // 1 KB store
+      uint2 pk[2][4][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            pk[mb][nb][gq] = make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                                        pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
+      const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(g.C + (int64_t)cur.m0 * g.ldc), (short)0, min(cur.mvalid, kBM) * g.ldc * 2, kBufferWord3);
+#pragma unroll 1
+      for (int qb = 0; qb < 4; ++qb) {
+        if (wm == qb) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const int r = mb * 32 + lr;
+            uint8_t* rowp = sA1 + r * 512 + (lane_e >> 5) * 8;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int chunk = (wn * 16 + nb * 4 + gq) ^ (r & 31);
+                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = pk[mb][nb][gq];
+              }
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = wave * 8 + j * 2 + (lane_e >> 5);
+          const int c = lane_e & 31;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sA1 + r * 512 + ((c ^ (r & 31)) << 4));
+          const int col = cur.nt * kBN + c * 8;
+          const int off = col < g.N ? ((qb * 64 + r) * g.ldc + col) * 2 : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    } else {
+      // The saved g | u (training only) go out straight from the accumulators; then h = silu(g) u
+      // is rounded to bf16 (32 packed registers) and staged: quarter qb = rows 64 qb .. +63,
+      // 256-byte rows (128 columns) in sA1, chunk c of row r at chunk c ^ (r & 15); every wave then
+      // writes 8 rows, 4 per 1 KB store.
+      if (g.gu_out) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int mloc = wm * 64 + mb * 32 + lr;
+          if (mloc < cur.mvalid) {
+            uint16_t* gs = g.gu_out + (int64_t)(cur.m0 + mloc) * 2 * g.N;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int col = cur.nt * 128 + wn * 64 + nb * 32 + gq * 8 + (lane_e >> 5) * 4;
+                if (col >= g.N) continue;
+                *reinterpret_cast<uint2*>(gs + col) =
+                    make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
+                               pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
+                *reinterpret_cast<uint2*>(gs + g.N + col) =
+                    make_uint2(pack_bf16x2(acc[mb][nb + 2][gq * 4 + 0], acc[mb][nb + 2][gq * 4 + 1]),
+                               pack_bf16x2(acc[mb][nb + 2][gq * 4 + 2], acc[mb][nb + 2][gq * 4 + 3]));
+              }
+          }
+        }
+      }
+      uint2 hp[2][2][4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            float hv[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[mb][nb][gq * 4 + qq]) * acc[mb][nb + 2][gq * 4 + qq];
+            hp[mb][nb][gq] = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+          }
+      const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(g.C + (int64_t)cur.m0 * g.ldc), (short)0, min(cur.mvalid, kBM) * g.ldc * 2, kBufferWord3);
+#pragma unroll 1
+      for (int qb = 0; qb < 4; ++qb) {
+        if (wm == qb) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const int r = mb * 32 + lr;
+            uint8_t* rowp = sA1 + r * 256 + (lane_e >> 5) * 8;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int chunk = (wn * 8 + nb * 4 + gq) ^ (r & 15);
+                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = hp[mb][nb][gq];
+              }
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = wave * 8 + j * 4 + (lane_e >> 4);
+          const int c = lane_e & 15;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sA1 + r * 256 + ((c ^ (r & 15)) << 4));
+          const int col = cur.nt * 128 + c * 8;
+          const int off = col < g.N ? ((qb * 64 + r) * g.ldc + col) * 2 : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    }
+    if (!has_next) break;
+    cur = nxt;
+    L = Ln;
+    pending_stores = 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last zero-filling DMAs into LDS
+}
+
 // ---------------------------------------------------------------------------------------------
 static inline int round_up8(int64_t v) { return (int)((v + 7) / 8 * 8); }
+
+static int cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+// persistent forward product: one workgroup per CU (at most one per tile), a multiple of 8
+template <int EPI, bool GATHER>
+static void launch_fwd(GemmArgs g, int64_t tiles, hipStream_t s) {
+  const int64_t grid = std::min<int64_t>(round_up8(tiles), std::max(8, cu_count() / 8 * 8));
+  hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EPI, GATHER>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
+}
 
 template <bool A_ROWS, bool B_ROWS, int EPI>
 static void launch_generic(GemmArgs g, int64_t grid, hipStream_t s) {
@@ -1335,7 +1895,10 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
     g.b_expert = (int64_t)H * 2 * I;
     g.b_rows = H;
     g.ntiles_n = (I + 127) / 128;
-    launch_generic<true, false, kEpiSwiglu>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+    if (slot_of_row)
+      launch_fwd<kEpiSwiglu, true>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+    else
+      launch_fwd<kEpiSwiglu, false>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
     const int64_t n1 = (int64_t)N * I;
     hipLaunchKernelGGL(grouped_ffn1_f32_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s,
@@ -1362,7 +1925,7 @@ hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int 
     g.b_expert = (int64_t)I * H;
     g.b_rows = I;
     g.ntiles_n = (H + kBN - 1) / kBN;
-    launch_generic<true, false, kEpiStore>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+    launch_fwd<kEpiStore, false>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
     const int64_t n2 = (int64_t)N * H;
     hipLaunchKernelGGL(grouped_ffn2_f32_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, (const float*)h,

@@ -1,0 +1,94 @@
+"""GPU parity of the forward grouped matmuls with several tiles per workgroup.
+
+The forward products run one workgroup per CU that walks its share of the tile list, loading the
+next tile's first operand steps while it finishes the current one. Small shapes give fewer tiles
+than workgroups, so these cases use many experts (or many rows) to give every workgroup several
+tiles, with every tile height the tiling has (1 row, 256, the 257-320-row band tiles, experts split
+over two or three row tiles, empty experts) and K and column tails. Tolerance as everywhere:
+max|gpu - ref| / max|ref| <= 1e-2 (bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_renorm_amd as moe
+import oracle
+from inputs import normal
+from inputs.generators import generator
+from tests.gpu_util import TOL, as64, dev, host, rel_err
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+HEIGHTS = np.array([0, 1, 3, 40, 255, 256, 257, 288, 289, 320, 321, 640, 700])
+
+
+def counts_mix(E, key, heights=HEIGHTS):
+    return generator(key).choice(heights, size=E).astype(np.int32)
+
+
+def tiles(counts, cols, bn=256, bm=320):
+    return int(sum((c + bm - 1) // bm for c in counts if c > 0)) * ((cols + bn - 1) // bn)
+
+
+@pytest.mark.parametrize("E,H,I,key", [(300, 72, 136, 1), (260, 64, 128, 2), (400, 24, 40, 3)])
+def test_ffn_many_tiles_per_workgroup(E, H, I, key):
+    counts = counts_mix(E, (1100, key))
+    assert tiles(counts, 2 * I) > 256 and tiles(counts, H) > 256
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    pad = 7
+    xp = normal((N + pad, H), 1.0, (1101, key), "bf16")
+    gu = normal((E * H, 2 * I), 0.1, (1102, key), "bf16")
+    dn = normal((E * I, H), 0.1, (1103, key), "bf16")
+    y = torch.full((N + pad, H), 5.0, dtype=torch.bfloat16, device="cuda")
+    h = torch.full((N + pad, I), 5.0, dtype=torch.bfloat16, device="cuda")
+    g = torch.full((N + pad, 2 * I), 5.0, dtype=torch.bfloat16, device="cuda")
+    y, h = moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), dev(offsets), h=h, y=y, gu_saved=g)
+    ry, ra, rgu = oracle.expert_rows(xp[:N], offsets, gu, dn, want_act=True, want_gu=True)
+    gy, gh, gg = host(y), host(h), host(g)
+    assert rel_err(gy[:N], ry) <= TOL["bf16"]
+    assert rel_err(gh[:N], ra) <= TOL["bf16"]
+    assert rel_err(gg[:N], rgu) <= TOL["bf16"]
+    assert np.all(as64(gy[N:]) == 5.0) and np.all(as64(gh[N:]) == 5.0) and np.all(as64(gg[N:]) == 5.0)
+    # run to run: bit-identical
+    y2, h2 = moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), dev(offsets))
+    assert np.array_equal(host(y2)[:N], gy[:N]) and np.array_equal(host(h2)[:N], gh[:N])
+
+
+@pytest.mark.parametrize("E,H,I,k,key", [(300, 72, 136, 4, 4), (200, 136, 136, 8, 5)])
+def test_gathered_ffn_many_tiles_per_workgroup(E, H, I, k, key):
+    counts = counts_mix(E, (1104, key))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    T = (N + k - 1) // k + 3
+    assert tiles(counts, 2 * I) > 256
+    x = normal((T, H), 1.0, (1105, key), "bf16")
+    gu = normal((E * H, 2 * I), 0.1, (1106, key), "bf16")
+    dn = normal((E * I, H), 0.1, (1107, key), "bf16")
+    sor = generator((1108, key)).permutation(T * k)[:N].astype(np.int32)   # every grouped row names a slot
+    xp = x[sor // k]
+    y1, h1 = moe.moe_grouped_swiglu_ffn_gather(dev(x), dev(sor), k, dev(gu), dev(dn), dev(offsets), N=N)
+    y2, h2 = moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), dev(offsets))
+    assert np.array_equal(host(h1), host(h2)) and np.array_equal(host(y1), host(y2))
+    ry, ra = oracle.expert_rows(xp, offsets, gu, dn, want_act=True)
+    assert rel_err(host(y1), ry) <= TOL["bf16"]
+    assert rel_err(host(h1), ra) <= TOL["bf16"]
+
+
+def test_ffn_many_tiles_full_width_sampled():
+    """H = 2048, I = 768 with experts of 2-3 row tiles (over 1000 tiles per product); rows sampled."""
+    E, H, I = 48, 2048, 768
+    counts = generator((1109,)).choice([0, 300, 321, 640, 700, 960], size=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    assert tiles(counts, 2 * I) > 512
+    xp = normal((N, H), 1.0, (1110,), "bf16")
+    gu = normal((E * H, 2 * I), 0.02, (1111,), "bf16")
+    dn = normal((E * I, H), 0.02, (1112,), "bf16")
+    y, h = moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), dev(offsets))
+    nz = counts > 0
+    edges = np.concatenate([offsets[:-1][nz], offsets[1:][nz] - 1])
+    rows = np.unique(np.concatenate([generator((1113,)).choice(N, 96, replace=False), edges])).astype(np.int64)
+    ry, ra = oracle.expert_rows(xp, offsets, gu, dn, rows=rows, want_act=True)
+    assert rel_err(host(h)[rows], ra) <= TOL["bf16"]
+    assert rel_err(host(y)[rows], ry) <= TOL["bf16"]
