@@ -71,9 +71,10 @@ int moe_abi_version(void);
 
 /* ---- (1) router logits -------------------------------------------------------------------------
  * [MM 8.2/8.3] the gate: logits = x @ w_gate, consumed by the FP32 softmax.
- * logits[t, e] = acc after `acc = fmaf(x[t,h], w_gate[h,e], acc)` for h = 0..H-1 from acc = 0 (fp32,
- * IEEE fused multiply-add, hidden dimension ascending) — a fixed order so that the top-k decision is
- * reproducible bit for bit.
+ * logits[t, e] = ((c_0 + c_1) + c_2) + c_3 in fp32, where c_b is acc after `acc = fmaf(x[t,h],
+ * w_gate[h,e], acc)` from acc = 0 over the h of block b = [b*HB, min((b+1)*HB, H)) in ascending order,
+ * HB = 128 * ceil(H / 512) (IEEE fused multiply-add; empty blocks give 0) — a fixed order, so that the
+ * top-k decision is reproducible bit for bit, with four independent chains per logit.
  *   x      [T, H]  dt       w_gate [H, E] dt       logits [T, E] fp32 (output)                       */
 moe_status moe_router_logits(const void* x, const void* w_gate, moe_dtype dt, int T, int H, int E,
                              float* logits, hipStream_t stream);

@@ -1,17 +1,20 @@
 // Router: gate logits, then softmax -> top-k -> renormalised weights.
 //
 // The MoE block of the MindSpeed-MM InternVL3.5 practice doc (issue 625, sections 8.2 and 8.3)
-// routes each token with gate -> FP32 softmax -> top-k -> weight normalisation. The logits are an
-// fp32 fused-multiply-add chain over the hidden dimension in ascending order, so that the top-k
-// decision is reproducible bit for bit by a sequential CPU implementation. Selection works on the
-// logits (softmax is monotone); ties go to the lower expert index.
+// routes each token with gate -> FP32 softmax -> top-k -> weight normalisation. Each logit is four
+// fp32 fused-multiply-add chains, one per fixed block of the hidden dimension, each in ascending h,
+// added in block order: a fixed order, so that the top-k decision is reproducible bit for bit by a
+// sequential CPU implementation. Selection works on the logits (softmax is monotone); ties go to the
+// lower expert index.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------------------------
-// logits[t, e] = fp32 chain over h = 0..H-1 of fma(x[t,h], w_gate[h,e], acc).
+// logits[t, e] = ((c0 + c1) + c2) + c3 in fp32, c_b = the chain fma(x[t,h], w_gate[h,e], acc) from
+// acc = 0 over the h of block b in ascending order; block b = [b*hblk, min((b+1)*hblk, H)) with
+// hblk = logit_block(H) = 128 * ceil(H / 512), a multiple of this kernel's 128-wide chunks (HB).
 //
 // Lanes are tokens: a workgroup of 8 waves owns 64 tokens (one per lane) and 8 * EQ experts
 // (EQ per wave), so a lane runs EQ independent chains, all consuming h = 0, 1, ..., H-1 in order;
@@ -29,6 +32,7 @@ namespace moe {
 // multiply-add per element onto the accumulator (the operation fmaf performs, measured bit-identical
 // to it, subnormals included). The matrix and vector pipelines of a SIMD run at the same time.
 constexpr int kLogitWaves = 8;
+inline int logit_block(int H) { return 128 * ((H + 511) / 512); }
 constexpr int kRd = 3;  // groups of four h whose LDS reads run ahead of the arithmetic
 constexpr int kLogitTok = kWave;  // tokens per workgroup
 
@@ -160,7 +164,7 @@ struct LogitTile {
 template <typename TIn, int EQ>
 __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_logits_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ wg, int T, int H, int E, float* __restrict__ logits, int vec_x,
-    int vec_w) {
+    int vec_w, int hblk) {
   using P = LogitTile<TIn, EQ>;
   constexpr int EB = P::EB, VEC = P::VEC, HB = P::HB, DEPTH = P::DEPTH;
   static_assert(EQ % 4 == 0, "experts per wave come in 16-byte groups");
@@ -326,6 +330,30 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
     }
   };
 
+  // The hidden dimension is four blocks of hblk (a multiple of the chunk) units: at the end of a
+  // block its chains are added to the running totals (the first block's chains are the totals)
+  // and restarted from zero; blocks past H add +0.0.
+  float tot[EQ];
+  f32x4_t mtot[EQ / 4];
+  int nfold = 0;
+  auto fold = [&]() {
+    if (mx) {
+#pragma unroll
+      for (int q = 0; q < EQ / 4; ++q) {
+        mtot[q] = nfold == 0 ? macc[q] : mtot[q] + macc[q];
+        macc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < EQ; ++q) {
+        tot[q] = nfold == 0 ? acc[q] : tot[q] + acc[q];
+        acc[q] = 0.0f;
+      }
+    }
+    ++nfold;
+  };
+  const int cpb = hblk / HB;  // chunks per block
+
   // prologue: chunks 0 .. depth-1 in flight
 #pragma unroll
   for (int r = 0; r < DEPTH; ++r)
@@ -343,9 +371,11 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
           compute_mx(c);
         else
           compute(c);
+        if ((c + 1) % cpb == 0 || c == nch - 1) fold();
       }
     }
   }
+  while (nfold < 4) fold();  // (H = 0 folds four zero blocks)
 
   if (mx) {
 #pragma unroll
@@ -353,7 +383,7 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int t = t0 + (lane & ~3) + m, e = e0 + wave * EQ + 4 * q + (lane & 3);
-        if (t < T && e < E) logits[(int64_t)t * E + e] = macc[q][m];
+        if (t < T && e < E) logits[(int64_t)t * E + e] = mtot[q][m];
       }
     return;
   }
@@ -363,12 +393,218 @@ __global__ __launch_bounds__(kLogitWaves * kWave) __attribute__((amdgpu_waves_pe
     if (e0 + wave * EQ + EQ <= E && (E & 3) == 0) {
 #pragma unroll
       for (int q = 0; q < EQ; q += 4)
-        *reinterpret_cast<float4*>(out + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
+        *reinterpret_cast<float4*>(out + q) = make_float4(tot[q], tot[q + 1], tot[q + 2], tot[q + 3]);
     } else {
 #pragma unroll
       for (int q = 0; q < EQ; ++q)
-        if (e0 + wave * EQ + q < E) out[q] = acc[q];
+        if (e0 + wave * EQ + q < E) out[q] = tot[q];
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same logits on the matrix cores (bf16 inputs, H % 32 == 0, E % 8 == 0, 16-byte aligned):
+// v_mfma_f32_32x32x1f32 adds, to each element of two 32 x 32 blocks, the product of one A and one
+// B value with a single fused multiply-add (K = 1; the operation fmaf performs), so a chain of
+// them over h is the fmaf chain of every (token, expert) element. The four blocks of h make four
+// times as many independent chains as there are logits, enough to keep every SIMD on its own
+// chains: a workgroup of four waves owns 64 tokens x 32 experts, wave w runs block w's chains
+// (lanes 0-31 feed tokens 0-31 and lanes 32-63 tokens 32-63, both against the same 32 experts),
+// and the four partial chains are added in block order at the end through LDS.
+// Each wave streams its block's x [64 tokens][32 h] and W_g [32 h][32 experts] in 32-h chunks
+// through a 3-deep LDS ring of its own (no barrier between waves in the loop); the 16-byte pieces
+// of each 64-byte x row are XOR-swizzled by row so that the 64 lanes reading one h of their own
+// rows spread over 16 bank groups, and the W_g value of a lane's expert is a broadcast read.
+// The operands reach the matrix cores without a conversion instruction (on this chip a vector
+// instruction between two MFMAs of a wave costs as much issue time as a tenth of an MFMA): every
+// operand register keeps a zero low half, and ds_read_u16_d16_hi replaces only its high half, so
+// the register holds exactly the fp32 value of the bf16 number. Groups of 8 h run back to back on
+// one of two register sets while the other set is loaded for the next 8 h.
+constexpr int kRtTok = 64, kRtExp = 32, kRtHc = 32;
+
+typedef __attribute__((ext_vector_type(4))) int rt_i32x4;
+// raw buffer descriptor over [p, p + bytes): 32-bit offsets, loads past the end return zero
+__device__ __forceinline__ rt_i32x4 rt_rsrc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)p;
+  rt_i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRawBufferWord3;
+  return r;
+}
+// One wave-wide 1 KB DMA: 16 bytes per lane from rs + voff into LDS at lds + 16 * lane. Written
+// as asm so that the compiler does not wait for it before every LDS read: the kernel counts the
+// loads itself (s_waitcnt vmcnt).
+__device__ __forceinline__ void rt_dma16(const rt_i32x4& rs, int voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "s"(lds)
+               : "memory", "m0");
+}
+
+// waits until at most `ahead` chunks of this wave's DMA (6 loads each) are in flight
+template <int N>
+__device__ __forceinline__ void rt_wait_chunks(int ahead) {
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (ahead >= N)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * N) : "memory");
+    else
+      rt_wait_chunks<N - 1>(ahead);
+  }
+}
+
+typedef __attribute__((ext_vector_type(32))) float rt_f32x32;
+#define RT_MFMA(a, b) "v_mfma_f32_32x32x1_2b_f32 %0, " a ", " b ", %0\n"
+#define RT_LD(d, a, off) "ds_read_u16_d16_hi " d ", " a " offset:" #off "\n"
+// Loads 8 h into a register set: x[token = lane][h0 .. h0 + 7] (2-byte steps from xa) and
+// W_g[h0 .. h0 + 7][expert] (64-byte steps from wa), into the high halves of nx and nw.
+__device__ __forceinline__ void rt_load(uint32_t (&nx)[8], uint32_t (&nw)[8], uint32_t xa, uint32_t wa) {
+  asm volatile(RT_LD("%0", "%16", 0) RT_LD("%1", "%16", 2) RT_LD("%2", "%16", 4) RT_LD("%3", "%16", 6)
+               RT_LD("%4", "%16", 8) RT_LD("%5", "%16", 10) RT_LD("%6", "%16", 12) RT_LD("%7", "%16", 14)
+               RT_LD("%8", "%17", 0) RT_LD("%9", "%17", 64) RT_LD("%10", "%17", 128) RT_LD("%11", "%17", 192)
+               RT_LD("%12", "%17", 256) RT_LD("%13", "%17", 320) RT_LD("%14", "%17", 384) RT_LD("%15", "%17", 448)
+               : "+v"(nx[0]), "+v"(nx[1]), "+v"(nx[2]), "+v"(nx[3]), "+v"(nx[4]), "+v"(nx[5]), "+v"(nx[6]),
+                 "+v"(nx[7]), "+v"(nw[0]), "+v"(nw[1]), "+v"(nw[2]), "+v"(nw[3]), "+v"(nw[4]), "+v"(nw[5]),
+                 "+v"(nw[6]), "+v"(nw[7])
+               : "v"(xa), "v"(wa)
+               : "memory");
+}
+// Eight chain steps on the set (cx, cw) once its loads have landed; with LOAD, the loads of the
+// next 8 h into (nx, nw) are issued after the first MFMA (by then every MFMA that read that set
+// has started) and land while the other seven run.
+template <bool LOAD>
+__device__ __forceinline__ void rt_group(rt_f32x32& acc, const uint32_t (&cx)[8], const uint32_t (&cw)[8],
+                                         uint32_t (&nx)[8], uint32_t (&nw)[8], uint32_t xa, uint32_t wa) {
+  if constexpr (LOAD) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n" RT_MFMA("%17", "%25")
+                 RT_LD("%1", "%33", 0) RT_LD("%2", "%33", 2) RT_LD("%3", "%33", 4) RT_LD("%4", "%33", 6)
+                 RT_LD("%5", "%33", 8) RT_LD("%6", "%33", 10) RT_LD("%7", "%33", 12) RT_LD("%8", "%33", 14)
+                 RT_LD("%9", "%34", 0) RT_LD("%10", "%34", 64) RT_LD("%11", "%34", 128) RT_LD("%12", "%34", 192)
+                 RT_LD("%13", "%34", 256) RT_LD("%14", "%34", 320) RT_LD("%15", "%34", 384) RT_LD("%16", "%34", 448)
+                 RT_MFMA("%18", "%26") RT_MFMA("%19", "%27") RT_MFMA("%20", "%28") RT_MFMA("%21", "%29")
+                 RT_MFMA("%22", "%30") RT_MFMA("%23", "%31") RT_MFMA("%24", "%32")
+                 : "+a"(acc), "+v"(nx[0]), "+v"(nx[1]), "+v"(nx[2]), "+v"(nx[3]), "+v"(nx[4]), "+v"(nx[5]),
+                   "+v"(nx[6]), "+v"(nx[7]), "+v"(nw[0]), "+v"(nw[1]), "+v"(nw[2]), "+v"(nw[3]), "+v"(nw[4]),
+                   "+v"(nw[5]), "+v"(nw[6]), "+v"(nw[7])
+                 : "v"(cx[0]), "v"(cx[1]), "v"(cx[2]), "v"(cx[3]), "v"(cx[4]), "v"(cx[5]), "v"(cx[6]), "v"(cx[7]),
+                   "v"(cw[0]), "v"(cw[1]), "v"(cw[2]), "v"(cw[3]), "v"(cw[4]), "v"(cw[5]), "v"(cw[6]), "v"(cw[7]),
+                   "v"(xa), "v"(wa)
+                 : "memory");
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)\n" RT_MFMA("%1", "%9") RT_MFMA("%2", "%10") RT_MFMA("%3", "%11")
+                 RT_MFMA("%4", "%12") RT_MFMA("%5", "%13") RT_MFMA("%6", "%14") RT_MFMA("%7", "%15")
+                 RT_MFMA("%8", "%16")
+                 : "+a"(acc)
+                 : "v"(cx[0]), "v"(cx[1]), "v"(cx[2]), "v"(cx[3]), "v"(cx[4]), "v"(cx[5]), "v"(cx[6]), "v"(cx[7]),
+                   "v"(cw[0]), "v"(cw[1]), "v"(cw[2]), "v"(cw[3]), "v"(cw[4]), "v"(cw[5]), "v"(cw[6]), "v"(cw[7])
+                 : "memory");
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wg, int T, int H, int E,
+                                                                 int hblk, float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sx[4][D][kRtTok * kRtHc * 2];   // 4 KB each
+  __shared__ __attribute__((aligned(1024))) uint8_t sw[4][D][kRtHc * kRtExp * 2];   // 2 KB each
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int t0 = blockIdx.x * kRtTok, e0 = blockIdx.y * kRtExp;
+  const int hb0 = min(H, wave * hblk), hb1 = min(H, (wave + 1) * hblk);
+  const int nch = (hb1 - hb0) / kRtHc;
+  const int rows = min(kRtTok, T - t0);
+  const rt_i32x4 rsx = rt_rsrc(x + (int64_t)t0 * H, rows * H * 2);
+  const rt_i32x4 rsw = rt_rsrc(wg, H * E * 2);
+  // DMA lanes: x instruction i fills rows 16 i .. 16 i + 15 (64-byte rows, 4 pieces of 8 h); the
+  // lane at LDS piece p of row r fetches piece p ^ ((r >> 2) & 3). W_g instruction i fills h-rows
+  // 16 i .. 16 i + 15 (64-byte rows of 32 experts).
+  int xo[4], wo[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 16 + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
+    xo[i] = (r * H + c * 8) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = i * 16 + (lane >> 2);
+    wo[i] = (r * E + e0 + (lane & 3) * 8) * 2;
+  }
+  const uint32_t sx0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)sx[wave][0]);
+  const uint32_t sw0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)sw[wave][0]);
+  auto issue = [&](int c, int slot) {
+    const int h0 = hb0 + c * kRtHc;
+    const uint32_t bx = sx0 + slot * (kRtTok * kRtHc * 2), bw = sw0 + slot * (kRtHc * kRtExp * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rt_dma16(rsx, xo[i] + h0 * 2, bx + i * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rt_dma16(rsw, wo[i] + h0 * E * 2, bw + i * 1024);
+  };
+  rt_f32x32 acc;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
+  // two operand register sets, low halves zero for the whole kernel
+  uint32_t xA[8], wA[8], xB[8], wB[8];
+  {
+    uint32_t z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xA[j] = wA[j] = xB[j] = wB[j] = z;
+  }
+  // this lane's x row (token t0 + lane, pieces swizzled) and W_g column (expert e0 + lane % 32)
+  const uint32_t xrow = sx0 + lane * 64, xs = (lane >> 2) & 3, wcol = sw0 + (lane & 31) * 2;
+  auto xaddr = [&](int slot, int q) { return xrow + slot * (kRtTok * kRtHc * 2) + ((q ^ xs) << 4); };
+  auto waddr = [&](int slot, int q) { return wcol + slot * (kRtHc * kRtExp * 2) + q * 512; };
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (d < nch) issue(d, d);
+  if (nch > 0) {
+    rt_wait_chunks<D - 2>(min(nch - 1, D - 2));  // chunk 0 has landed
+    rt_load(xA, wA, xaddr(0, 0), waddr(0, 0));
+  }
+  asm volatile("s_nop 7" : "+a"(acc));  // the accumulator's initial writes settle before the first MFMA
+  // chunks 0 .. nch - 2; the last group of each loads the first 8 h of the next chunk
+  for (int c = 0; c + 1 < nch; ++c) {
+    const int slot = c % D, nslot = (c + 1) % D;
+    rt_group<true>(acc, xA, wA, xB, wB, xaddr(slot, 1), waddr(slot, 1));
+    // every LDS read of chunk c - 1 has completed (the group above began with lgkmcnt(0)): its
+    // slot takes chunk c + D - 1
+    if (c + D - 1 < nch) issue(c + D - 1, (c + D - 1) % D);
+    rt_group<true>(acc, xB, wB, xA, wA, xaddr(slot, 2), waddr(slot, 2));
+    rt_group<true>(acc, xA, wA, xB, wB, xaddr(slot, 3), waddr(slot, 3));
+    rt_wait_chunks<D - 2>(min(nch - 1, c + D - 1) - (c + 1));  // chunk c + 1 has landed
+    rt_group<true>(acc, xB, wB, xA, wA, xaddr(nslot, 0), waddr(nslot, 0));
+  }
+  if (nch > 0) {  // the last chunk
+    const int slot = (nch - 1) % D;
+    rt_group<true>(acc, xA, wA, xB, wB, xaddr(slot, 1), waddr(slot, 1));
+    rt_group<true>(acc, xB, wB, xA, wA, xaddr(slot, 2), waddr(slot, 2));
+    rt_group<true>(acc, xA, wA, xB, wB, xaddr(slot, 3), waddr(slot, 3));
+    rt_group<false>(acc, xB, wB, xA, wA, 0, 0);
+  }
+  // the last MFMA's result is complete before the accumulator is read
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+  // the four blocks' chains, added in block order: element i of the accumulator of this lane is
+  // (token 32 (i / 16) + 8 ((i % 16) / 4) + 4 (lane / 32) + i % 4, expert lane % 32)
+  __syncthreads();  // every wave is done with its chunks; sx becomes the partial sums
+  float* part = reinterpret_cast<float*>(&sx[0][0][0]);  // [4 blocks][64 tokens][32 experts]
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int tok = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * (lane >> 5) + (i & 3);
+    part[(wave * kRtTok + tok) * kRtExp + (lane & 31)] = acc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kRtTok * kRtExp / 256; ++j) {
+    const int idx = tid + 256 * j;
+    const int tok = idx / kRtExp, ex = idx % kRtExp;
+    float v = part[tok * kRtExp + ex];
+#pragma unroll
+    for (int b = 1; b < 4; ++b) v = v + part[(b * kRtTok + tok) * kRtExp + ex];
+    if (t0 + tok < T && e0 + ex < E) logits[(int64_t)(t0 + tok) * E + e0 + ex] = v;
   }
 }
 
@@ -715,7 +951,7 @@ static void launch_logits_t(const void* x, const void* w_gate, int T, int H, int
   const bool vec_w = E % (16 / sizeof(TIn)) == 0 && ((uintptr_t)w_gate & 15) == 0;
   dim3 grid((T + kLogitTok - 1) / kLogitTok, (E + EB - 1) / EB);
   hipLaunchKernelGGL((router_logits_kernel<TIn, EQ>), grid, dim3(kLogitWaves * kWave), 0, s, (const TIn*)x,
-                     (const TIn*)w_gate, T, H, E, logits, (int)vec_x, (int)vec_w);
+                     (const TIn*)w_gate, T, H, E, logits, (int)vec_x, (int)vec_w, logit_block(H));
 }
 
 // Eight chains per lane when that still gives a workgroup per CU, else four (twice the
@@ -731,6 +967,15 @@ static void launch_logits_dt(const void* x, const void* w_gate, int T, int H, in
 
 hipError_t launch_router_logits(const void* x, const void* w_gate, int dt, int T, int H, int E, float* logits,
                                 hipStream_t s) {
+  const bool mfma_ok = dt == kBF16 && H % kRtHc == 0 && E % 8 == 0 && ((uintptr_t)x & 15) == 0 &&
+                       ((uintptr_t)w_gate & 15) == 0 && (int64_t)T * H * 2 < (1LL << 31) &&
+                       (int64_t)H * E * 2 < (1LL << 31);
+  if (mfma_ok) {
+    const dim3 grid((T + kRtTok - 1) / kRtTok, (E + kRtExp - 1) / kRtExp);
+    hipLaunchKernelGGL(router_logits_mfma_kernel<3>, grid, dim3(256), 0, s, (const uint16_t*)x, (const uint16_t*)w_gate,
+                       T, H, E, logit_block(H), logits);
+    return hipGetLastError();
+  }
   if (dt == kF32)
     launch_logits_dt<float>(x, w_gate, T, H, E, logits, s);
   else

@@ -88,6 +88,13 @@ def max_threads() -> int:
     return int(f())
 
 
+def router_logit_block(H: int) -> int:
+    """Hidden units per block of the router's four fp32 chains."""
+    f = _load().orc_router_logit_block
+    f.restype = ctypes.c_int
+    return int(f(I64(H)))
+
+
 def router_logits(x: np.ndarray, w_gate: np.ndarray) -> np.ndarray:
     x, w_gate = _c(x), _c(w_gate)
     T, H = x.shape

@@ -42,15 +42,26 @@ static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
 /* ------------------------------------------------------------------------------------------ */
 /* Router logits: gate applied to the token, in fp32 ("FP32 softmax" consumes fp32 logits).    */
+/* Four fixed blocks of the hidden dimension, each an fmaf chain from 0 in ascending h, then the */
+/* four partial sums added in block order: ((c0 + c1) + c2) + c3. Block b covers                */
+/* [b*HB, min((b+1)*HB, H)), HB = 128 * ceil(H / 512); an empty block contributes +0.0.         */
+int orc_router_logit_block(int64_t H) { return (int)(128 * ((H + 511) / 512)); }
+
 int orc_router_logits(const void* x, const void* w_gate, int dt, int64_t T, int64_t H, int64_t E,
                       float* logits) {
     if (!x || !w_gate || !logits || bad_dt(dt) || T < 0 || H < 0 || E < 1) return -1;
+    const int64_t hb = orc_router_logit_block(H);
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t e = 0; e < E; ++e) {
-            float acc = 0.0f;
-            for (int64_t h = 0; h < H; ++h) acc = fmaf(elf(x, dt, t * H + h), elf(w_gate, dt, h * E + e), acc);
-            logits[t * E + e] = acc;
+            float total = 0.0f;
+            for (int64_t b = 0; b < 4; ++b) {
+                float acc = 0.0f;
+                for (int64_t h = b * hb; h < (b + 1) * hb && h < H; ++h)
+                    acc = fmaf(elf(x, dt, t * H + h), elf(w_gate, dt, h * E + e), acc);
+                total = b == 0 ? acc : total + acc;
+            }
+            logits[t * E + e] = total;
         }
     }
     return 0;

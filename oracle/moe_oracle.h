@@ -14,8 +14,9 @@
  *     forward ends by summing the experts' outputs weighted by the gate weights; its VeOmni
  *     section orders the permuted rows expert-major, tokens ascending inside an expert.
  *
- * Precision: fp64 throughout, except the router logits, which are an fp32 fused-multiply-add
- * chain over h ascending so that both sides take the top-k decision on identical fp32 values.
+ * Precision: fp64 throughout, except the router logits, which are fp32 fused-multiply-add
+ * chains over four fixed blocks of h (ascending inside a block), added in block order, so that
+ * both sides take the top-k decision on identical fp32 values.
  * bf16 inputs are passed as raw 16-bit patterns and widened exactly.
  *
  * Every function returns 0 on success and a negative value on a bad argument.
@@ -34,7 +35,10 @@ int orc_max_threads(void);
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 
-/* logits[t*E+e] = fp32 chain: acc = 0; for h = 0..H-1: acc = fmaf(x[t,h], w_gate[h,e], acc) */
+/* logits[t*E+e] = ((c0 + c1) + c2) + c3 in fp32, where c_b is the chain acc = 0;
+ * for h in block b ascending: acc = fmaf(x[t,h], w_gate[h,e], acc); block b = [b*HB, min((b+1)*HB, H)),
+ * HB = orc_router_logit_block(H) = 128 * ceil(H / 512) (empty blocks give +0.0). */
+int orc_router_logit_block(int64_t H);
 int orc_router_logits(const void* x, const void* w_gate, int dt, int64_t T, int64_t H, int64_t E,
                       float* logits);
 

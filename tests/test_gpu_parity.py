@@ -34,7 +34,11 @@ def routing(T, E, k, key, skew=None):
 
 # ---- router -----------------------------------------------------------------------------------
 @pytest.mark.parametrize("T,H,E,dtype", [(64, 64, 8, "f32"), (300, 136, 72, "bf16"), (1, 8, 1, "bf16"),
-                                         (513, 2048, 128, "bf16"), (37, 7168, 256, "bf16"), (70, 24, 130, "f32")])
+                                         (513, 2048, 128, "bf16"), (37, 7168, 256, "bf16"), (70, 24, 130, "f32"),
+                                         # matrix-core kernel: bf16, H % 32 == 0, E % 8 == 0; empty hidden
+                                         # blocks (H < 384), a ragged expert tile, ragged token tiles
+                                         (100, 96, 8, "bf16"), (257, 640, 40, "bf16"), (65, 1056, 200, "bf16"),
+                                         (4096, 2048, 128, "bf16")])
 def test_router_logits_bit_exact(T, H, E, dtype):
     x = normal((T, H), 1.0, (950, T, H), dtype)
     w = normal((H, E), 0.02, (951, H, E), dtype)
@@ -57,6 +61,17 @@ def test_router_logits_subnormal_products():
     T, H, E = 130, 200, 40
     x = normal((T, H), 1e-20, (955, T, H), "f32")
     w = normal((H, E), 1e-20, (956, H, E), "f32")
+    want = oracle.router_logits(x, w)
+    assert np.count_nonzero((want != 0) & (np.abs(want) < np.finfo(np.float32).tiny)) > T * E // 2
+    got = host(moe.moe_router_logits(dev(x), dev(w)))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_router_logits_subnormal_products_matrix_cores():
+    # the same on the bf16 matrix-core kernel: subnormal products and partial sums are kept, not flushed
+    T, H, E = 130, 256, 40
+    x = normal((T, H), 1e-20, (957, T, H), "bf16")
+    w = normal((H, E), 1e-20, (958, H, E), "bf16")
     want = oracle.router_logits(x, w)
     assert np.count_nonzero((want != 0) & (np.abs(want) < np.finfo(np.float32).tiny)) > T * E // 2
     got = host(moe.moe_router_logits(dev(x), dev(w)))

@@ -48,6 +48,18 @@ def exact_fma_chain(xrow, wcol):
     return acc
 
 
+def exact_blocked_logit(xrow, wcol):
+    """Four blocks of HB = 128 * ceil(H / 512) hidden units, each an exactly replayed fmaf chain
+    from 0, then ((c0 + c1) + c2) + c3 with each addition rounded to fp32."""
+    H = len(xrow)
+    hb = 128 * ((H + 511) // 512)
+    total = 0.0
+    for b in range(4):
+        c = exact_fma_chain(xrow[b * hb:(b + 1) * hb], wcol[b * hb:(b + 1) * hb])
+        total = c if b == 0 else round_f32(Fraction(total) + Fraction(c))
+    return total
+
+
 def test_round_f32_helper_against_numpy():
     # the helper itself: rounding exact float64 values must agree with numpy's fp64->fp32 cast
     rng = np.random.default_rng(7)
@@ -57,16 +69,20 @@ def test_round_f32_helper_against_numpy():
         assert round_f32(Fraction(float(v))) == float(np.float32(v)), v
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_logits_are_the_ordered_fp32_fma_chain(dtype):
-    T, H, E = 5, 37, 6
-    x = normal((T, H), 1.0, (901, 1), dtype)
-    w = normal((H, E), 0.3, (901, 2), dtype)
+@pytest.mark.parametrize("dtype,H", [("f32", 37), ("bf16", 37), ("f32", 300), ("bf16", 1100), ("bf16", 2048)])
+def test_logits_are_the_blocked_fp32_fma_chains(dtype, H):
+    T, E = 3 if H > 500 else 5, 6
+    x = normal((T, H), 1.0, (901, 1, H), dtype)
+    w = normal((H, E), 0.3, (901, 2, H), dtype)
     got = oracle.router_logits(x, w)
     xf = x if dtype == "f32" else bf16_bits_to_f32(x)
     wf = w if dtype == "f32" else bf16_bits_to_f32(w)
-    want = np.array([[exact_fma_chain(xf[t], wf[:, e]) for e in range(E)] for t in range(T)], np.float32)
+    want = np.array([[exact_blocked_logit(xf[t], wf[:, e]) for e in range(E)] for t in range(T)], np.float32)
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert oracle.router_logit_block(H) == 128 * ((H + 511) // 512)
+    if H > 128:   # the block split is not vacuous: one chain over all of h gives other bits somewhere
+        one = np.array([[exact_fma_chain(xf[t], wf[:, e]) for e in range(E)] for t in range(T)], np.float32)
+        assert not np.array_equal(one.view(np.uint32), want.view(np.uint32))
     # the pin is not vacuous: an unfused chain (round after multiply, then after add) differs
     if dtype == "f32":
         unfused = np.zeros((T, E), np.float32)
