@@ -197,7 +197,7 @@ def main():
     ap.add_argument("--separate-routing", action="store_true",
                     help="forward: moe_router_topk then moe_permute as two calls instead of moe_router_topk_permute")
     ap.add_argument("--no-mall-cold", dest="mall_cold", action="store_false",
-                    help="skip the per-kernel pass with a 512 MiB write before every call (last-level cache cold)")
+                    help="skip the per-kernel pass with a 512 MiB read before every call (last-level cache cold)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 512 MiB device copy before the warm-up (counter calibration)")
     args = ap.parse_args()
