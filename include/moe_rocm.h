@@ -61,7 +61,10 @@ typedef enum {
   MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Element type of inputs, weights and activations. A plain int, so that any value a caller passes
+ * is a valid argument value: values other than these two are rejected with MOE_ERR_INVALID_ARG. */
+typedef int moe_dtype;
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
 /* Message for the calling thread's last non-OK status ("" if none). Never NULL. */
 const char* moe_last_error(void);

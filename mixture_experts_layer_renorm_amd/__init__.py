@@ -16,7 +16,8 @@ import re
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_rocm.so")
+# MOE_SANITIZE_LIB=1 loads the host-sanitized build (tests/sanitizers.py); nothing else does
+LIB_PATH = os.path.join(_PKG, "libmoe_rocm_san.so" if os.environ.get("MOE_SANITIZE_LIB") == "1" else "libmoe_rocm.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "moe_rocm.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)

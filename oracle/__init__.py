@@ -16,23 +16,30 @@ import subprocess
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(HERE, "liborc_moe.so")
 SRC = os.path.join(HERE, "moe_oracle.c")
+# MOE_SANITIZE_ORACLE=1 loads the AddressSanitizer + UBSan build (tests/sanitizers.py preloads gcc's
+# ASan runtime for it)
+SANITIZE = os.environ.get("MOE_SANITIZE_ORACLE") == "1"
+LIB = os.path.join(HERE, "liborc_moe_san.so" if SANITIZE else "liborc_moe.so")
+SAN_FLAGS = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 
 F32, BF16 = 0, 1
 
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the oracle with gcc (no fast-math, no FP contraction, OpenMP over tokens)."""
+def build(verbose: bool = False, sanitize: bool = None) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction, OpenMP over tokens); with
+    sanitize, the AddressSanitizer + UBSan build liborc_moe_san.so."""
+    san = SANITIZE if sanitize is None else sanitize
+    out = os.path.join(HERE, "liborc_moe_san.so" if san else "liborc_moe.so")
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", *(SAN_FLAGS if san else []), "-o", out + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def _load():
