@@ -126,8 +126,8 @@ moe_status moe_permute(const void* x, moe_dtype dt, int T, int H, const int32_t*
 
 /* moe_permute without a workspace argument, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments and
- * results as moe_permute; its scratch (the per-chunk expert counts) is a fixed 1 MiB device array
- * inside the library, one per GPU, held until the process ends. Limit: ceil(T/64) * E <= 262144
+ * results as moe_permute; its scratch (the expert counts per 16 tokens) is a fixed 4 MiB device array
+ * inside the library, one per GPU, held until the process ends. Limit: ceil(T/16) * E <= 1048576
  * (e.g. T <= 131072 at E = 128, T <= 16384 at E = 1024), else MOE_ERR_WORKSPACE. The call allocates
  * nothing; its first call on a device looks the array's address up. Every call on one GPU shares the
  * array: calls that overlap on one GPU (concurrent streams, threads) race and must be ordered by the
@@ -138,7 +138,7 @@ moe_status moe_permute_noalloc(const void* x, moe_dtype dt, int T, int H, const 
 
 /* (2)+(3) in one call: the selection and weights of moe_router_topk, then the layout handle (and
  * x_perm unless NULL) of moe_permute, with the same results bit for bit. For E <= 256 the top-k
- * kernel also counts each 64-token chunk's expert choices, so the permute skips its counting pass.
+ * kernel also counts the expert choices of every 16 tokens, so the permute skips its counting pass.
  * Arguments as in (2) and (3); workspace: moe_permute_workspace_bytes(T, k, E) bytes.           */
 moe_status moe_router_topk_permute(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
                                    float* topk_w, const void* x, moe_dtype dt, int H, void* x_perm, int32_t* counts,

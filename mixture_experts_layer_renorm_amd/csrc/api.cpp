@@ -136,9 +136,9 @@ moe_status moe_permute_noalloc(const void* x, moe_dtype dt, int T, int H, const 
   REQUIRE(k >= 1 && k <= E && k <= kMaxK, MOE_ERR_INVALID_ARG, "%s: k=%d outside [1, min(E=%d, %d)]", fn, k, E,
           kMaxK);
   REQUIRE((int64_t)T * k <= 0x7fffffffLL, MOE_ERR_INVALID_ARG, "%s: T*k overflows int32", fn);
-  const int64_t need = (int64_t)moe::permute_nchunks(T) * E;
+  const int64_t need = (int64_t)moe::permute_ncount(T) * E;
   REQUIRE(need <= moe::kPermuteScratchInts, MOE_ERR_WORKSPACE,
-          "%s: ceil(T/64)*E = %lld chunk counts exceed the fixed scratch of %lld (T=%d E=%d); use moe_permute with a "
+          "%s: ceil(T/16)*E = %lld chunk counts exceed the fixed scratch of %lld (T=%d E=%d); use moe_permute with a "
           "workspace",
           fn, (long long)need, (long long)moe::kPermuteScratchInts, T, E);
   REQUIRE(counts && offsets, MOE_ERR_INVALID_ARG, "%s: null counts/offsets", fn);

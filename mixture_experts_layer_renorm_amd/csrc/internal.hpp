@@ -17,19 +17,24 @@ hipError_t launch_router_logits(const void* x, const void* w_gate, int dt, int T
 size_t router_stats_workspace_bytes(int T, int E);
 hipError_t launch_router_stats(const float* logits, const int32_t* topk_idx, int T, int E, int k, float* probs,
                                float* mean_prob, int32_t* load, void* workspace, hipStream_t s);
-// chunk_counts (may be NULL): the expert histogram of every kPermuteChunk tokens, [nchunks, E], as
-// permute_count_kernel writes it; returns false in *counted when this E takes the separate count
+// chunk_counts (may be NULL): the expert histogram of every kCountTok tokens, [permute_ncount(T), E],
+// as permute_count_kernel writes it; returns false in *counted when this E takes the separate count
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w,
                               hipStream_t s, int32_t* chunk_counts = nullptr, bool* counted = nullptr);
 
 // permute.hip
 constexpr int kPermuteChunk = 64;   // tokens per plan chunk (64 measured faster than 128 or 256)
 inline int permute_nchunks(int T) { return (T + kPermuteChunk - 1) / kPermuteChunk; }
-inline size_t permute_workspace_bytes(int T, int E) { return (size_t)permute_nchunks(T) * (size_t)E * sizeof(int32_t); }
+// The expert histograms are kept per kCountTok tokens (four rows per plan chunk), the granularity at
+// which the top-k kernel's workgroups own tokens: 16-token workgroups spread the top-k over every CU.
+constexpr int kCountTok = 16;
+constexpr int kCountPerChunk = kPermuteChunk / kCountTok;
+inline int permute_ncount(int T) { return (T + kCountTok - 1) / kCountTok; }
+inline size_t permute_workspace_bytes(int T, int E) { return (size_t)permute_ncount(T) * (size_t)E * sizeof(int32_t); }
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 // allocation-free permute: its chunk counts in a fixed device array of kPermuteScratchInts int32
-// (1 MiB) per GPU; *out = this device's address of it (looked up once per device)
-constexpr int64_t kPermuteScratchInts = 1 << 18;
+// (4 MiB) per GPU; *out = this device's address of it (looked up once per device)
+constexpr int64_t kPermuteScratchInts = 1 << 20;
 hipError_t permute_noalloc_scratch(int32_t** out);
 hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,

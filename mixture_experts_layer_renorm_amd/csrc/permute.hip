@@ -5,9 +5,9 @@
 // tokens stay in ascending order; per-expert counts come from summing the routing mask.
 //
 // Three kernels, no host synchronisation and no atomics that decide an order:
-//  1. count : per chunk of kPermuteChunk tokens, an LDS histogram of the chunk's expert choices.
-//  2. plan  : per chunk, global bases = exclusive scan over experts of the totals + the counts of
-//             earlier chunks; in-chunk ranks from per-expert token bitmaps (popcount of the
+//  1. count : per kCountTok tokens, an LDS histogram of their expert choices.
+//  2. plan  : per chunk of kPermuteChunk tokens, global bases = exclusive scan over experts of the
+//             totals + the counts of earlier tokens; in-chunk ranks from per-expert token bitmaps (popcount of the
 //             tokens before this one). Writes counts, offsets, row_of_slot, slot_of_row. A chunk
 //             in which a token names one expert in two slots ranks by counting earlier slots
 //             instead, so every slot gets its own row in (expert, token, slot) order.
@@ -32,8 +32,8 @@ __global__ __launch_bounds__(kPlanThreads) void permute_count_kernel(const int32
   const int c = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += kPlanThreads) cnt[e] = 0;
   __syncthreads();
-  const int64_t s0 = (int64_t)c * kPermuteChunk * k;
-  const int64_t s1 = (int64_t)min(T, (c + 1) * kPermuteChunk) * k;
+  const int64_t s0 = (int64_t)c * kCountTok * k;
+  const int64_t s1 = (int64_t)min(T, (c + 1) * kCountTok) * k;
   for (int64_t s = s0 + threadIdx.x; s < s1; s += kPlanThreads) {
     const int e = idx[s];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kPlanThreads) void permute_count_kernel(const int32
 }
 
 __global__ __launch_bounds__(kPlanThreads) void permute_plan_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int E, const int32_t* __restrict__ chunk_counts, int nchunks,
+    const int32_t* __restrict__ idx, int T, int k, int E, const int32_t* __restrict__ chunk_counts, int ncount,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of_slot,
     int32_t* __restrict__ slot_of_row) {
   __shared__ int scan[kMaxE + 1];
@@ -51,34 +51,83 @@ __global__ __launch_bounds__(kPlanThreads) void permute_plan_kernel(
   __shared__ uint32_t mask[kMaxE * kMaskWords];
   __shared__ int s_idx[kMaxChunkSlots];      // the chunk's expert choices, slot order
   __shared__ int p_tot[kPlanThreads], p_bef[kPlanThreads];
+  __shared__ int4 p_tot4[kPlanThreads], p_bef4[kPlanThreads];
   __shared__ int wave_tot[kPlanThreads / kWave];
   __shared__ int s_dup;
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
-  // per expert: its total over all chunks and over the chunks before this one. With E < 256 the
-  // chunks of an expert are split over G = 256 / E threads, each issuing its loads as one batch
-  // (the loads are independent; one chain of them per expert would be a chain of L2 round trips).
+  // per expert: its total over all count rows and over the rows before this chunk's first. With
+  // E < 256 the rows of an expert are split over G = 256 / E threads, each issuing its loads as one
+  // batch (the loads are independent; one chain of them per expert would be a chain of L2 round
+  // trips).
+  const int first = c * kCountPerChunk;
   auto sum_chunks = [&](int e, int g, int G, int& tot, int& before) {
     tot = 0;
     before = 0;
     int cc = g;
-    for (; cc + 15 * G < nchunks; cc += 16 * G) {
+    for (; cc + 15 * G < ncount; cc += 16 * G) {
       int v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) v[u] = chunk_counts[(int64_t)(cc + u * G) * E + e];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         tot += v[u];
-        if (cc + u * G < c) before += v[u];
+        if (cc + u * G < first) before += v[u];
       }
     }
-    for (; cc < nchunks; cc += G) {
+    for (; cc < ncount; cc += G) {
       const int v = chunk_counts[(int64_t)cc * E + e];
       tot += v;
-      if (cc < c) before += v;
+      if (cc < first) before += v;
     }
   };
-  if (E >= kPlanThreads) {
+  // the chunk's expert choices (their loads overlap the count loads below)
+  for (int i = tid; i < E * kMaskWords; i += kPlanThreads) mask[i] = 0u;
+  const int t0 = c * kPermuteChunk;
+  const int64_t s0 = (int64_t)t0 * k;
+  const int ns = (int)((int64_t)min(T, t0 + kPermuteChunk) * k - s0);
+  for (int i = tid; i < ns; i += kPlanThreads) s_idx[i] = idx[s0 + i];
+  if (tid == 0) s_dup = 0;
+  const bool vec = (E % 4 == 0) && ((uintptr_t)chunk_counts % 16 == 0);
+  if (vec) {
+    // 16-byte loads of 4 experts' counts: thread (phase ph, expert quad ev) sums the rows
+    // ph, ph + P, ... with 16 loads in flight at a time (the rows were written by other XCDs, so
+    // each batch is a round trip to the last-level cache), then the P phases are added in LDS
+    const int EV = E / 4, P = kPlanThreads / EV;
+    int4 tot = make_int4(0, 0, 0, 0), bef = make_int4(0, 0, 0, 0);
+    if (tid < P * EV) {
+      const int ev = tid % EV, ph = tid / EV;
+      const int4* cc4 = reinterpret_cast<const int4*>(chunk_counts) + ev;
+      int r = ph;
+      for (; r + 15 * P < ncount; r += 16 * P) {
+        int4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = cc4[(int64_t)(r + u * P) * EV];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          tot.x += v[u].x, tot.y += v[u].y, tot.z += v[u].z, tot.w += v[u].w;
+          if (r + u * P < first) bef.x += v[u].x, bef.y += v[u].y, bef.z += v[u].z, bef.w += v[u].w;
+        }
+      }
+      for (; r < ncount; r += P) {
+        const int4 v = cc4[(int64_t)r * EV];
+        tot.x += v.x, tot.y += v.y, tot.z += v.z, tot.w += v.w;
+        if (r < first) bef.x += v.x, bef.y += v.y, bef.z += v.z, bef.w += v.w;
+      }
+    }
+    p_tot4[tid] = tot;
+    p_bef4[tid] = bef;
+    __syncthreads();
+    for (int e = tid; e < E; e += kPlanThreads) {
+      int a = 0, b = 0;
+      for (int ph = 0; ph < P; ++ph) {
+        a += reinterpret_cast<const int*>(&p_tot4[ph * EV + e / 4])[e % 4];
+        b += reinterpret_cast<const int*>(&p_bef4[ph * EV + e / 4])[e % 4];
+      }
+      scan[e] = a;
+      base[e] = b;
+    }
+  } else if (E >= kPlanThreads) {
     for (int e = tid; e < E; e += kPlanThreads) sum_chunks(e, 0, 1, scan[e], base[e]);
   } else {
     const int G = kPlanThreads / E;
@@ -97,12 +146,6 @@ __global__ __launch_bounds__(kPlanThreads) void permute_plan_kernel(
       base[tid] = b;
     }
   }
-  for (int i = tid; i < E * kMaskWords; i += kPlanThreads) mask[i] = 0u;
-  const int t0 = c * kPermuteChunk;
-  const int64_t s0 = (int64_t)t0 * k;
-  const int ns = (int)((int64_t)min(T, t0 + kPermuteChunk) * k - s0);
-  for (int i = tid; i < ns; i += kPlanThreads) s_idx[i] = idx[s0 + i];
-  if (tid == 0) s_dup = 0;
   __syncthreads();
   if (c == 0)
     for (int e = tid; e < E; e += kPlanThreads) counts[e] = scan[e];
@@ -215,7 +258,7 @@ static hipError_t plan_and_scatter(const void* x, int dt, int T, int H, const in
   const int64_t row_bytes = (int64_t)H * (int64_t)dtype_bytes(dt);
   const int vec16 = (row_bytes % 16 == 0) && (((uintptr_t)x | (uintptr_t)x_perm) % 16 == 0);
   hipLaunchKernelGGL(permute_plan_kernel, dim3(nchunks), dim3(kPlanThreads), 0, s, topk_idx, T, k, E, chunk_counts,
-                     nchunks, counts, offsets, row_of_slot, slot_of_row);
+                     permute_ncount(T), counts, offsets, row_of_slot, slot_of_row);
   if (x_perm)  // else the plan only: a gathering GEMM reads the rows from x itself
     hipLaunchKernelGGL(permute_scatter_kernel, dim3((T + kScatterWaves - 1) / kScatterWaves),
                        dim3(kScatterWaves * kWave), 0, s, (const uint8_t*)x, T, row_bytes, k, row_of_slot,
@@ -226,7 +269,7 @@ static hipError_t plan_and_scatter(const void* x, int dt, int T, int H, const in
 hipError_t launch_permute(const void* x, int dt, int T, int H, const int32_t* topk_idx, int k, int E, void* x_perm,
                           int32_t* counts, int32_t* offsets, int32_t* row_of_slot, int32_t* slot_of_row,
                           int32_t* chunk_counts, hipStream_t s) {
-  hipLaunchKernelGGL(permute_count_kernel, dim3(permute_nchunks(T)), dim3(kPlanThreads), 0, s, topk_idx, T, k, E,
+  hipLaunchKernelGGL(permute_count_kernel, dim3(permute_ncount(T)), dim3(kPlanThreads), 0, s, topk_idx, T, k, E,
                      chunk_counts);
   return plan_and_scatter(x, dt, T, H, topk_idx, k, E, x_perm, counts, offsets, row_of_slot, slot_of_row,
                           chunk_counts, s);

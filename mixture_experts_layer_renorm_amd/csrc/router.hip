@@ -686,8 +686,9 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void router_topk_kernel(
 // token's group holds experts e = q * L + sub, q = 0..VPL-1 (ascending e per lane), so a round's
 // argmax is a local scan plus log2(L) exchanges inside a 16-lane row (DPP quad permutes and the
 // row mirrors, a few cycles each, against the 64-lane shuffles above). Slot j is kept by lane
-// j % L. A workgroup holds kPermuteChunk tokens (L waves of 64 / L tokens), so it can also write
-// the chunk's expert histogram that the permute's plan takes (permute_count_kernel's output).
+// j % L. A workgroup of 4 waves holds kCountTok = 16 tokens (L = 16: 4 tokens per wave), so it can
+// also write those tokens' expert histogram that the permute's plan takes (permute_count_kernel's
+// output), and the 256 workgroups of a 4096-token batch spread the k argmax rounds over every CU.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
@@ -717,6 +718,20 @@ __device__ __forceinline__ void group_best(float& bv, int& be) {
   xchg_better<0x141>(bv, be);
   if constexpr (L == 16) xchg_better<0x140>(bv, be);
 }
+template <int CTRL>
+__device__ __forceinline__ void xchg_max64(uint64_t& x) {
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)x), hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(x >> 32));
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  x = o > x ? o : x;
+}
+// all-reduce max of 64-bit keys over groups of L lanes (the same exchanges as group_best)
+template <int L>
+__device__ __forceinline__ void group_max64(uint64_t& x) {
+  xchg_max64<0xB1>(x);
+  xchg_max64<0x4E>(x);
+  xchg_max64<0x141>(x);
+  if constexpr (L == 16) xchg_max64<0x140>(x);
+}
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
   v += dpp_f<0xB1>(v);
@@ -726,33 +741,33 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+constexpr int kTopkGroupWaves = 4;
 template <int L, int VPL>
-__global__ __launch_bounds__(L * kWave) void router_topk_group_kernel(const float* __restrict__ logits, int T, int E,
-                                                                      int k, int renorm, int32_t* __restrict__ topk_idx,
-                                                                      float* __restrict__ topk_w,
-                                                                      int32_t* __restrict__ chunk_counts) {
+__global__ __launch_bounds__(kTopkGroupWaves * kWave) void router_topk_group_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ chunk_counts) {
   static_assert(L == 8 || L == 16, "a token's lanes stay inside one 16-lane row");
   constexpr int TPW = kWave / L;  // tokens per wave
   constexpr int KR = 32 / L;      // slots kept per lane (k <= 32)
+  static_assert(kTopkGroupWaves * TPW == kCountTok, "a workgroup owns one row of the expert histogram");
   __shared__ int cnt[L * VPL];
   const int lane = lane_id(), sub = lane & (L - 1);
-  const int t = blockIdx.x * kPermuteChunk + (int)(threadIdx.x / kWave) * TPW + lane / L;
+  const int t = blockIdx.x * kCountTok + (int)(threadIdx.x / kWave) * TPW + lane / L;
   const bool live = t < T;
   if (chunk_counts) {
-    for (int e = threadIdx.x; e < E; e += L * kWave) cnt[e] = 0;
+    for (int e = threadIdx.x; e < E; e += kTopkGroupWaves * kWave) cnt[e] = 0;
     __syncthreads();
   }
   const float* l = logits + (int64_t)t * E;
   float v[VPL];
-  uint32_t avail = 0;
+  uint32_t valid = 0;
 #pragma unroll
   for (int q = 0; q < VPL; ++q) {
     const int e = q * L + sub;
     const bool ok = live && e < E;
     v[q] = ok ? l[e] : 0.0f;
-    avail |= ok ? 1u << q : 0u;
+    valid |= ok ? 1u << q : 0u;
   }
-  const uint32_t valid = avail;
   float sv[KR];
   int se[KR];
 #pragma unroll
@@ -760,19 +775,29 @@ __global__ __launch_bounds__(L * kWave) void router_topk_group_kernel(const floa
     sv[r] = 0.0f;
     se[r] = -1;
   }
-  float m = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int be = kNoExpert;
+  // Order-preserving 64-bit keys: the high word maps the float's bits to an unsigned order (-0 is
+  // folded into +0 first, since the two compare equal), the low word is 0xffff - e, so that equal
+  // values rank the lower expert higher. A valid expert's key is > 0; absent experts have key 0.
+  // Round j takes the largest key below round j-1's: no per-round bookkeeping, no branches.
+  uint64_t key[VPL];
 #pragma unroll
-    for (int q = 0; q < VPL; ++q) {  // ascending e: strict > keeps the lower index on ties
-      const bool take = ((avail >> q) & 1u) && (be == kNoExpert || v[q] > bv);
-      bv = take ? v[q] : bv;
-      be = take ? q * L + sub : be;
-    }
-    group_best<L>(bv, be);
+  for (int q = 0; q < VPL; ++q) {
+    const uint32_t b = __float_as_uint(v[q] + 0.0f);
+    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    key[q] = ((valid >> q) & 1u) ? ((uint64_t)o << 32) | (uint32_t)(0xffff - (q * L + sub)) : 0ull;
+  }
+  float m = 0.0f;
+  uint64_t prev = ~0ull;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) best = (key[q] < prev && key[q] > best) ? key[q] : best;
+    group_max64<L>(best);
+    prev = best;
+    const uint32_t o = (uint32_t)(best >> 32);
+    const float bv = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+    const int be = 0xffff - (int)(uint32_t)best;  // k <= E: every round finds a valid expert
     if (j == 0) m = bv;
-    if (be != kNoExpert && (be & (L - 1)) == sub) avail &= ~(1u << (be / L));
 #pragma unroll
     for (int r = 0; r < KR; ++r)
       if (j == r * L + sub) {
@@ -808,7 +833,7 @@ __global__ __launch_bounds__(L * kWave) void router_topk_group_kernel(const floa
         if (r * L + sub < k) atomicAdd(&cnt[se[r]], 1);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += L * kWave) chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+    for (int e = threadIdx.x; e < E; e += kTopkGroupWaves * kWave) chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
   }
 }
 
@@ -986,20 +1011,18 @@ hipError_t launch_router_logits(const void* x, const void* w_gate, int dt, int T
 hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int32_t* idx, float* w,
                               hipStream_t s, int32_t* chunk_counts, bool* counted) {
   if (E <= 256) {
-    const dim3 grid(permute_nchunks(T));
-#define MOE_TOPK_GROUP(L, V) \
-  hipLaunchKernelGGL((router_topk_group_kernel<L, V>), grid, dim3(L * kWave), 0, s, logits, T, E, k, renorm, idx, w, \
-                     chunk_counts)
-    if (E <= 8)
-      MOE_TOPK_GROUP(8, 1);
-    else if (E <= 16)
-      MOE_TOPK_GROUP(8, 2);
+    const dim3 grid(permute_ncount(T));
+#define MOE_TOPK_GROUP(L, V)                                                                                     \
+  hipLaunchKernelGGL((router_topk_group_kernel<L, V>), grid, dim3(kTopkGroupWaves * kWave), 0, s, logits, T, E, k, \
+                     renorm, idx, w, chunk_counts)
+    if (E <= 16)
+      MOE_TOPK_GROUP(16, 1);
     else if (E <= 32)
-      MOE_TOPK_GROUP(8, 4);
+      MOE_TOPK_GROUP(16, 2);
     else if (E <= 64)
-      MOE_TOPK_GROUP(8, 8);
+      MOE_TOPK_GROUP(16, 4);
     else if (E <= 128)
-      MOE_TOPK_GROUP(8, 16);
+      MOE_TOPK_GROUP(16, 8);
     else
       MOE_TOPK_GROUP(16, 16);
 #undef MOE_TOPK_GROUP

@@ -32,10 +32,10 @@ def test_header_is_plain_c():
 
 
 def test_workspace_size_arithmetic(lib):
-    # one int32 per (64-token chunk, expert)
-    assert moe.moe_permute_workspace_bytes(4096, 8, 128) == 64 * 128 * 4
+    # one int32 per (16 tokens, expert)
+    assert moe.moe_permute_workspace_bytes(4096, 8, 128) == 256 * 128 * 4
     assert moe.moe_permute_workspace_bytes(1, 1, 1) == 4
-    assert moe.moe_permute_workspace_bytes(257, 2, 3) == 5 * 3 * 4
+    assert moe.moe_permute_workspace_bytes(257, 2, 3) == 17 * 3 * 4
     assert moe.moe_router_stats_workspace_bytes(4096, 128) == 32 * 128 * 8
     assert moe.moe_permute_workspace_bytes(0, 2, 3) == 0
 

@@ -63,8 +63,8 @@ def test_noalloc_plan_only_and_size_limit():
     moe.moe_permute_noalloc(x, idx, E, None, plan, rows=False)
     torch.cuda.synchronize()
     assert _same(plan.row_of_slot, plan_ref.row_of_slot) and _same(plan.slot_of_row, plan_ref.slot_of_row)
-    # ceil(T/64) * E above 2^18 chunk counts: refused before anything is launched
-    Tb, Eb = 64 * 257, 1024
+    # ceil(T/16) * E above 2^20 chunk counts: refused before anything is launched
+    Tb, Eb = 16 * 1025, 1024
     xb = torch.zeros((Tb, 8), dtype=torch.bfloat16, device="cuda")
     ib = torch.zeros((Tb, 1), dtype=torch.int32, device="cuda")
     xpb, planb = _buffers(Tb, 8, Eb, 1)
