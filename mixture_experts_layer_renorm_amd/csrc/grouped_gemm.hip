@@ -1318,6 +1318,18 @@ __device__ __forceinline__ void dma_16i_nt(const i32x4& rsrc, int voff, uint32_t
                "s"(lds), "n"(IMM)
                : "memory", "m0", "scc");
 }
+// The descriptor of the same buffer starting `bytes` further on (bytes >= 0, wave-uniform): base +
+// bytes, records - bytes (at least 0), so every offset keeps its range check against the buffer's
+// original end and the per-lane offsets need no per-step arithmetic.
+__device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, int bytes) {
+  const uint64_t b = ((uint64_t)(uint32_t)r[0] | ((uint64_t)((uint32_t)r[1] & 0xffffu) << 32)) + (uint32_t)bytes;
+  i32x4 o;
+  o[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  o[1] = __builtin_amdgcn_readfirstlane((int)(((uint32_t)r[1] & 0xffff0000u) | ((uint32_t)(b >> 32) & 0xffffu)));
+  o[2] = __builtin_amdgcn_readfirstlane(max(0, r[2] - bytes));
+  o[3] = r[3];
+  return o;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Forward row-grouped products, persistent: gate_up + SwiGLU (EPI = kEpiSwiglu) and down
@@ -1339,7 +1351,7 @@ __device__ __forceinline__ void dma_16i_nt(const i32x4& rsrc, int voff, uint32_t
 //    flight: they drain while the next tile computes;
 //  - with gathered rows, the slot map of the next tile's rows is brought into LDS by one DMA of
 //    wave 0 in the current tile's first step.
-template <int EPI, bool GATHER>
+template <int EPI, bool GATHER, bool KF>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const GemmArgs g) {
   static_assert(EPI == kEpiSwiglu || EPI == kEpiStore, "the forward epilogues");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA2], sA1[kTileA2];
@@ -1469,6 +1481,17 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
   auto dma_a = [&](const Ops& o, int st, uint8_t* sa) {
     const int k0 = st * kBK2;
     const uint32_t base = lds_addr(sa) + wa;
+    if constexpr (KF) {
+      // K a multiple of 128: no K tail. The step moves the descriptor (scalar arithmetic) instead of
+      // every lane's offset; rows past the tile keep their out-of-range offset
+      const i32x4 rs = rsrc_advance(o.rsA, k0 * 2);
+      if (o.band) dma_16i<0>(rs, o.x_off, lds_addr(sa) + wx);
+      dma_16i<0>(rs, o.a_off[0], base);
+      dma_16i<1024>(rs, o.a_off[1], base);
+      dma_16i<2048>(rs, o.a_off[2], base);
+      dma_16i<3072>(rs, o.a_off[3], base);
+      return;
+    }
     if (o.band) {
       const int off = k0 + x_kc < K ? (int)((uint32_t)o.x_off + (uint32_t)(k0 * 2)) : kOutOfRange;
       dma_16i<0>(o.rsA, off, lds_addr(sa) + wx);
@@ -1485,6 +1508,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
   auto dma_b = [&](const Ops& o, int kt, uint8_t* sb) {
     const int kb = kt * kBK * g.ldb * 2;  // k-rows past K are past the expert's block
     const uint32_t base = lds_addr(sb) + wb;
+    if constexpr (KF) {
+      const i32x4 rs = rsrc_advance(o.rsB, kb);
+      dma_16i_nt<0>(rs, o.b_off[0], base);
+      dma_16i_nt<1024>(rs, o.b_off[1], base);
+      return;
+    }
     const int off0 = o.b_off[0] == kOutOfRange ? kOutOfRange : o.b_off[0] + kb;
     const int off1 = o.b_off[1] == kOutOfRange ? kOutOfRange : o.b_off[1] + kb;
     dma_16i_nt<0>(o.rsB, off0, base);
@@ -1868,7 +1897,13 @@ static int cu_count() {
 template <int EPI, bool GATHER>
 static void launch_fwd(GemmArgs g, int64_t tiles, hipStream_t s) {
   const int64_t grid = std::min<int64_t>(round_up8(tiles), std::max(8, cu_count() / 8 * 8));
-  hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EPI, GATHER>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
+  // K a multiple of four K steps (no tail, whole groups of four steps): per-step descriptor moves
+  if (g.K % (kStages * kBK) == 0)
+    hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EPI, GATHER, true>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
+                       g);
+  else
+    hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EPI, GATHER, false>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
+                       g);
 }
 
 template <bool A_ROWS, bool B_ROWS, int EPI>
