@@ -26,7 +26,9 @@
  *   - Tensors are contiguous and row-major. bf16 data is raw bfloat16 (16-bit) storage.
  *     Routing weights are always fp32; indices and row maps are int32.
  *   - Sizes: T, H, I, N >= 0 (a zero size enqueues nothing); 1 <= E <= 1024; 1 <= k <= min(E, 32).
- *     The bf16 grouped FFN needs H and I to be multiples of 8 and 16-byte aligned buffers.
+ *     Any H, I >= 1 in either dtype: the grouped FFN and its backward run on the matrix cores for
+ *     bf16 with H and I multiples of 8 and 16-byte aligned buffers, and on generic kernels (one
+ *     thread per output element, fp32 accumulation, much slower) for everything else.
  *   - Results are bitwise deterministic run to run (no floating-point atomics).
  *   - Errors: a moe_status is returned; arguments are checked on the host before any launch and a
  *     failed check enqueues nothing. moe_last_error() gives the calling thread's last message.
@@ -56,7 +58,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned buffer */
-  MOE_ERR_UNSUPPORTED = 2, /* legal request this build does not implement (e.g. H % 8 != 0 in bf16) */
+  MOE_ERR_UNSUPPORTED = 2, /* legal request this build does not implement (e.g. sizes past 32-bit offsets) */
   MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } moe_status;
@@ -209,7 +211,7 @@ moe_status moe_unpermute_combine_bwd(const void* d_out, const void* y, moe_dtype
                                      const int32_t* row_of_slot, const float* topk_w, void* d_y, float* d_w,
                                      hipStream_t stream);
 
-/* ---- (7) grouped SwiGLU FFN backward (bf16) --------------------------------------------------------
+/* ---- (7) grouped SwiGLU FFN backward ------------------------------------------------------------------
  * [MM 2, 8.3] the transposed products of the experts' permute -> grouped_matmul -> SwiGLU ->
  * grouped_matmul path over the same fused weights; [FT 3] experts without rows get zero weight
  * gradients. For each expert e and its rows r (g, u = the forward pre-activations saved in gu_saved, s = sigmoid(g)):
@@ -218,9 +220,9 @@ moe_status moe_unpermute_combine_bwd(const void* d_out, const void* y, moe_dtype
  *   d_down_e    = h_e^T @ d_y_e        [I, H]   (zeros for an expert without rows)
  *   d_gate_up_e = x_perm_e^T @ d_gu_e  [H, 2I]  (zeros for an expert without rows)
  *   d_y, x_perm [N,H]; gu_saved, d_gu [N,2I] (d_gu: caller scratch, also an output); h [N,I];
- *   gate_up, d_gate_up [E*H, 2I]; down, d_down [E*I, H]; d_x_perm [N,H]. All bf16, 16-byte aligned.
+ *   gate_up, d_gate_up [E*H, 2I]; down, d_down [E*I, H]; d_x_perm [N,H]. All of dtype dt.
  * A shared expert is the same call with E = 1 and expert_offsets = {0, T}.
- * MOE_ERR_UNSUPPORTED for fp32 data.                                                                 */
+ * fp32 and bf16 shapes outside the matrix-core kernels' (see the conventions) take the generic kernels. */
 moe_status moe_grouped_swiglu_ffn_bwd(const void* d_y, const void* x_perm, const void* gu_saved, const void* h,
                                       const void* gate_up, const void* down, moe_dtype dt, int N, int H, int I, int E,
                                       const int32_t* expert_offsets, void* d_x_perm, void* d_gate_up, void* d_down,
@@ -234,8 +236,9 @@ moe_status moe_grouped_swiglu_ffn_bwd(const void* d_y, const void* x_perm, const
  *       P [N, M] and Q [N, Nq] row-major with the rows grouped by expert; d_w [E*M, Nq].
  *       max_workgroups > 0 caps the product's workgroups (rounded down to a multiple of 8, at least 8;
  *       each holds one CU until the product ends), leaving the other CUs to kernels on other streams;
- *       0 = one per CU. M and Nq multiples of 8; N*max(M, Nq)*2 and M*Nq*2 below 2^31, else
- *       MOE_ERR_UNSUPPORTED. All bf16 (fp32: MOE_ERR_UNSUPPORTED), 16-byte aligned.                 */
+ *       0 = one per CU (the generic kernels ignore it). N*max(M, Nq)*2 and M*Nq*2 below 2^31, else
+ *       MOE_ERR_UNSUPPORTED. fp32, or bf16 with M or Nq not a multiple of 8 or unaligned buffers, take
+ *       the generic kernels.                                                                        */
 moe_status moe_grouped_gemm_down_bwd(const void* d_y, const void* down, const void* gu_saved, moe_dtype dt, int N,
                                      int H, int I, int E, const int32_t* expert_offsets, void* d_gu,
                                      hipStream_t stream);

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_rocm.so")
-SOURCES = ["api.cpp", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "backward.hip"]
+SOURCES = ["api.cpp", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "backward.hip", "generic.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

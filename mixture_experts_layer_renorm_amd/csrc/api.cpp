@@ -29,7 +29,6 @@ moe_status hip_status(hipError_t e, const char* what) {
 }
 
 bool bad_dt(moe_dtype dt) { return dt != MOE_F32 && dt != MOE_BF16; }
-bool misaligned16(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
@@ -196,9 +195,6 @@ moe_status check_ffn(const char* fn, moe_dtype dt, int N, int H, int I, int E) {
   REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   REQUIRE(N >= 0 && H >= 1 && I >= 1, MOE_ERR_INVALID_ARG, "%s: N=%d H=%d I=%d out of range", fn, N, H, I);
   REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
-  if (dt == MOE_BF16)
-    REQUIRE(H % 8 == 0 && I % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: bf16 needs H and I multiples of 8 (H=%d I=%d)", fn, H,
-            I);
   // the bf16 kernels address one expert's weight block with 32-bit byte offsets
   REQUIRE((int64_t)H * 2 * I * 4 < 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "%s: H*I=%lld too large", fn,
           (long long)H * I);
@@ -213,9 +209,6 @@ moe_status moe_grouped_gemm_swiglu(const void* x_perm, const void* gate_up, moe_
   if (st != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE(x_perm && gate_up && expert_offsets && h, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  if (dt == MOE_BF16)
-    REQUIRE(!misaligned16(x_perm) && !misaligned16(gate_up) && !misaligned16(h) && !misaligned16(gu_saved),
-            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   return hip_status(moe::launch_gemm_gate_up(x_perm, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream),
                     fn);
 }
@@ -241,9 +234,6 @@ moe_status moe_grouped_gemm_swiglu_gather(const void* x, const int32_t* slot_of_
   if (st != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE(x && slot_of_row && gate_up && expert_offsets && h, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  if (dt == MOE_BF16)
-    REQUIRE(!misaligned16(x) && !misaligned16(gate_up) && !misaligned16(h) && !misaligned16(gu_saved),
-            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   return hip_status(moe::launch_gemm_gate_up(x, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream,
                                              slot_of_row, k, T),
                     fn);
@@ -259,10 +249,6 @@ moe_status moe_grouped_swiglu_ffn_gather(const void* x, const int32_t* slot_of_r
   if (st != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE(x && slot_of_row && gate_up && down && expert_offsets && h && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  if (dt == MOE_BF16)
-    REQUIRE(!misaligned16(x) && !misaligned16(gate_up) && !misaligned16(down) && !misaligned16(h) &&
-                !misaligned16(y) && !misaligned16(gu_saved),
-            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   hipError_t e = moe::launch_gemm_gate_up(x, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream,
                                           slot_of_row, k, T);
   if (e == hipSuccess) e = moe::launch_gemm_down(h, down, (int)dt, N, H, I, E, expert_offsets, y, stream);
@@ -276,9 +262,6 @@ moe_status moe_grouped_gemm_down(const void* h, const void* down, moe_dtype dt, 
   if (st != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE(h && down && expert_offsets && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  if (dt == MOE_BF16)
-    REQUIRE(!misaligned16(h) && !misaligned16(down) && !misaligned16(y), MOE_ERR_INVALID_ARG,
-            "%s: bf16 buffers must be 16-byte aligned", fn);
   return hip_status(moe::launch_gemm_down(h, down, (int)dt, N, H, I, E, expert_offsets, y, stream), fn);
 }
 
@@ -290,10 +273,6 @@ moe_status moe_grouped_swiglu_ffn(const void* x_perm, const void* gate_up, const
   if (st != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE(x_perm && gate_up && down && expert_offsets && h && y, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  if (dt == MOE_BF16)
-    REQUIRE(!misaligned16(x_perm) && !misaligned16(gate_up) && !misaligned16(down) && !misaligned16(h) &&
-                !misaligned16(y) && !misaligned16(gu_saved),
-            MOE_ERR_INVALID_ARG, "%s: bf16 buffers must be 16-byte aligned", fn);
   hipError_t e = moe::launch_gemm_gate_up(x_perm, gate_up, (int)dt, N, H, I, E, expert_offsets, h, gu_saved, stream);
   if (e == hipSuccess) e = moe::launch_gemm_down(h, down, (int)dt, N, H, I, E, expert_offsets, y, stream);
   return hip_status(e, fn);
@@ -330,25 +309,31 @@ moe_status moe_grouped_swiglu_ffn_bwd(const void* d_y, const void* x_perm, const
   const char* fn = "moe_grouped_swiglu_ffn_bwd";
   moe_status st = check_ffn(fn, dt, N, H, I, E);
   if (st != MOE_OK) return st;
-  REQUIRE(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: the backward is implemented for bf16", fn);
   // the weight-gradient products address all rows of one expert with 32-bit byte offsets
   REQUIRE((int64_t)N * (H > 2 * I ? H : 2 * I) * 2 < 0x7fffffffLL, MOE_ERR_UNSUPPORTED,
           "%s: N*max(H, 2I) too large for one call (N=%d H=%d I=%d)", fn, N, H, I);
   REQUIRE(d_gate_up && d_down && expert_offsets, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  REQUIRE(!misaligned16(d_y) && !misaligned16(x_perm) && !misaligned16(gu_saved) && !misaligned16(h) &&
-              !misaligned16(gate_up) && !misaligned16(down) && !misaligned16(d_x_perm) && !misaligned16(d_gate_up) &&
-              !misaligned16(d_down) && !misaligned16(d_gu),
-          MOE_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
   if (N > 0) REQUIRE(d_y && x_perm && gu_saved && h && gate_up && down && d_x_perm && d_gu, MOE_ERR_INVALID_ARG,
                      "%s: null pointer", fn);
   hipError_t e = hipSuccess;
-  if (N > 0) {
-    e = moe::launch_gemm_down_bwd(d_y, down, gu_saved, N, H, I, E, expert_offsets, d_gu, stream);
-    if (e == hipSuccess) e = moe::launch_gemm_gate_up_bwd(d_gu, gate_up, N, H, I, E, expert_offsets, d_x_perm, stream);
+  if (moe::mfma_shapes_ok((int)dt, H, I, d_y, x_perm, gu_saved, h, gate_up, down, d_x_perm, d_gu) &&
+      moe::mfma_shapes_ok((int)dt, H, I, d_gate_up, d_down)) {
+    if (N > 0) {
+      e = moe::launch_gemm_down_bwd(d_y, down, gu_saved, N, H, I, E, expert_offsets, d_gu, stream);
+      if (e == hipSuccess) e = moe::launch_gemm_gate_up_bwd(d_gu, gate_up, N, H, I, E, expert_offsets, d_x_perm, stream);
+    }
+    // weight gradients cover every expert (zeros for experts without rows, and for N == 0)
+    if (e == hipSuccess) e = moe::launch_gemm_wgrad(h, d_y, I, H, E, expert_offsets, d_down, stream);
+    if (e == hipSuccess) e = moe::launch_gemm_wgrad(x_perm, d_gu, H, 2 * I, E, expert_offsets, d_gate_up, stream);
+  } else {  // fp32, or bf16 widths / alignments the matrix-core kernels do not take
+    if (N > 0) {
+      e = moe::launch_gen_down_bwd(d_y, down, gu_saved, (int)dt, N, H, I, E, expert_offsets, d_gu, stream);
+      if (e == hipSuccess)
+        e = moe::launch_gen_gate_up_bwd(d_gu, gate_up, (int)dt, N, H, I, E, expert_offsets, d_x_perm, stream);
+    }
+    if (e == hipSuccess) e = moe::launch_gen_wgrad(h, d_y, (int)dt, I, H, E, expert_offsets, d_down, stream);
+    if (e == hipSuccess) e = moe::launch_gen_wgrad(x_perm, d_gu, (int)dt, H, 2 * I, E, expert_offsets, d_gate_up, stream);
   }
-  // weight gradients cover every expert (zeros for experts without rows, and for N == 0)
-  if (e == hipSuccess) e = moe::launch_gemm_wgrad(h, d_y, I, H, E, expert_offsets, d_down, stream);
-  if (e == hipSuccess) e = moe::launch_gemm_wgrad(x_perm, d_gu, H, 2 * I, E, expert_offsets, d_gate_up, stream);
   return hip_status(e, fn);
 }
 
@@ -356,7 +341,6 @@ namespace {
 moe_status check_bwd(const char* fn, moe_dtype dt, int N, int H, int I, int E) {
   moe_status st = check_ffn(fn, dt, N, H, I, E);
   if (st != MOE_OK) return st;
-  REQUIRE(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: the backward is implemented for bf16", fn);
   return MOE_OK;
 }
 }  // namespace
@@ -369,8 +353,9 @@ moe_status moe_grouped_gemm_down_bwd(const void* d_y, const void* down, const vo
   if (st != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE(d_y && down && gu_saved && expert_offsets && d_gu, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  REQUIRE(!misaligned16(d_y) && !misaligned16(down) && !misaligned16(gu_saved) && !misaligned16(d_gu),
-          MOE_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  if (!moe::mfma_shapes_ok((int)dt, H, I, d_y, down, gu_saved, d_gu))
+    return hip_status(moe::launch_gen_down_bwd(d_y, down, gu_saved, (int)dt, N, H, I, E, expert_offsets, d_gu, stream),
+                      fn);
   return hip_status(moe::launch_gemm_down_bwd(d_y, down, gu_saved, N, H, I, E, expert_offsets, d_gu, stream), fn);
 }
 
@@ -381,8 +366,9 @@ moe_status moe_grouped_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, m
   if (st != MOE_OK) return st;
   if (N == 0) return ok();
   REQUIRE(d_gu && gate_up && expert_offsets && d_x_perm, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  REQUIRE(!misaligned16(d_gu) && !misaligned16(gate_up) && !misaligned16(d_x_perm), MOE_ERR_INVALID_ARG,
-          "%s: buffers must be 16-byte aligned", fn);
+  if (!moe::mfma_shapes_ok((int)dt, H, I, d_gu, gate_up, d_x_perm))
+    return hip_status(moe::launch_gen_gate_up_bwd(d_gu, gate_up, (int)dt, N, H, I, E, expert_offsets, d_x_perm, stream),
+                      fn);
   return hip_status(moe::launch_gemm_gate_up_bwd(d_gu, gate_up, N, H, I, E, expert_offsets, d_x_perm, stream), fn);
 }
 
@@ -390,18 +376,15 @@ moe_status moe_grouped_gemm_wgrad(const void* P, const void* Q, moe_dtype dt, in
                                   const int32_t* expert_offsets, void* d_w, int max_workgroups, hipStream_t stream) {
   const char* fn = "moe_grouped_gemm_wgrad";
   REQUIRE(!bad_dt(dt), MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
-  REQUIRE(dt == MOE_BF16, MOE_ERR_UNSUPPORTED, "%s: implemented for bf16", fn);
   REQUIRE(N >= 0 && M >= 1 && Nq >= 1, MOE_ERR_INVALID_ARG, "%s: N=%d M=%d Nq=%d out of range", fn, N, M, Nq);
   REQUIRE(E >= 1 && E <= kMaxE, MOE_ERR_INVALID_ARG, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
-  REQUIRE(M % 8 == 0 && Nq % 8 == 0, MOE_ERR_UNSUPPORTED, "%s: M and Nq must be multiples of 8 (M=%d Nq=%d)", fn, M,
-          Nq);
   // rows of one expert and one expert's output block are addressed with 32-bit byte offsets
   REQUIRE((int64_t)N * (M > Nq ? M : Nq) * 2 < 0x7fffffffLL && (int64_t)M * Nq * 2 < 0x7fffffffLL,
           MOE_ERR_UNSUPPORTED, "%s: N*max(M, Nq) or M*Nq too large for one call (N=%d M=%d Nq=%d)", fn, N, M, Nq);
   REQUIRE(expert_offsets && d_w, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (N > 0) REQUIRE(P && Q, MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-  REQUIRE(!misaligned16(P) && !misaligned16(Q) && !misaligned16(d_w), MOE_ERR_INVALID_ARG,
-          "%s: buffers must be 16-byte aligned", fn);
+  if (!moe::mfma_shapes_ok((int)dt, M, Nq, P, Q, d_w))
+    return hip_status(moe::launch_gen_wgrad(P, Q, (int)dt, M, Nq, E, expert_offsets, d_w, stream), fn);
   return hip_status(moe::launch_gemm_wgrad(P, Q, M, Nq, E, expert_offsets, d_w, stream, max_workgroups), fn);
 }
 

@@ -1246,59 +1246,6 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_res_kernel(const G
     walk(std::false_type{});
 }
 
-// ---------------------------------------------------------------------------------------------
-// fp32 path: one thread per output element, fp32 fused multiply-add over k ascending.
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int E, int r) {
-  int lo = 0, hi = E;  // find e with offsets[e] <= r < offsets[e+1]
-  if (r < offsets[0] || r >= offsets[E]) return -1;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= r)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
-__global__ __launch_bounds__(256) void grouped_ffn1_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
-                                                               const int32_t* __restrict__ offsets, int E, int N, int K,
-                                                               int I, float* __restrict__ h, float* __restrict__ gu_saved,
-                                                               const int32_t* __restrict__ a_slot, int a_div) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)N * I) return;
-  const int r = (int)(gid / I), j = (int)(gid % I);
-  const int e = expert_of_row(offsets, E, r);
-  if (e < 0) return;
-  const float* a = A + (int64_t)(a_slot ? a_slot[r] / a_div : r) * K;
-  const float* w = W + (int64_t)e * K * 2 * I;
-  float g = 0.0f, u = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    g = __builtin_fmaf(a[k], w[(int64_t)k * 2 * I + j], g);
-    u = __builtin_fmaf(a[k], w[(int64_t)k * 2 * I + I + j], u);
-  }
-  h[(int64_t)r * I + j] = g / (1.0f + expf(-g)) * u;
-  if (gu_saved) {
-    gu_saved[(int64_t)r * 2 * I + j] = g;
-    gu_saved[(int64_t)r * 2 * I + I + j] = u;
-  }
-}
-
-__global__ __launch_bounds__(256) void grouped_ffn2_f32_kernel(const float* __restrict__ Hh, const float* __restrict__ D,
-                                                               const int32_t* __restrict__ offsets, int E, int N, int I,
-                                                               int H, float* __restrict__ y) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)N * H) return;
-  const int r = (int)(gid / H), c = (int)(gid % H);
-  const int e = expert_of_row(offsets, E, r);
-  if (e < 0) return;
-  const float* a = Hh + (int64_t)r * I;
-  const float* d = D + (int64_t)e * I * H;
-  float acc = 0.0f;
-  for (int i = 0; i < I; ++i) acc = __builtin_fmaf(a[i], d[(int64_t)i * H + c], acc);
-  y[(int64_t)r * H + c] = acc;
-}
-
 // 16 bytes per lane from rsrc + voff into LDS at lds + IMM + 16 * lane; the immediate keeps one
 // scalar register per LDS buffer instead of one per DMA instruction. The add writes SCC, which the
 // clobber list must say: the compiler keeps loop conditions in SCC across code like this.
@@ -1920,7 +1867,7 @@ static inline int64_t row_tiles_bound(int N, int E) { return ((int64_t)N + (int6
 hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, int N, int H, int I, int E,
                                const int32_t* offsets, void* h, void* gu_saved, hipStream_t s,
                                const int32_t* slot_of_row, int k, int T) {
-  if (dt == kBF16) {
+  if (mfma_shapes_ok(dt, H, I, x_perm, gate_up, h, gu_saved)) {
     GemmArgs g{};
     g.A = (const uint16_t*)x_perm;
     g.a_slot = slot_of_row;
@@ -1944,17 +1891,14 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
     else
       launch_fwd<kEpiSwiglu, false>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
-    const int64_t n1 = (int64_t)N * I;
-    hipLaunchKernelGGL(grouped_ffn1_f32_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s,
-                       (const float*)x_perm, (const float*)gate_up, offsets, E, N, H, I, (float*)h, (float*)gu_saved,
-                       slot_of_row, k);
+    return launch_gen_ffn1(x_perm, gate_up, dt, offsets, E, N, H, I, h, gu_saved, slot_of_row, k, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int H, int I, int E, const int32_t* offsets,
                             void* y, hipStream_t s) {
-  if (dt == kBF16) {
+  if (mfma_shapes_ok(dt, H, I, h, down, y)) {
     GemmArgs g{};
     g.A = (const uint16_t*)h;
     g.B = (const uint16_t*)down;
@@ -1971,9 +1915,7 @@ hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int 
     g.ntiles_n = (H + kBN - 1) / kBN;
     launch_fwd<kEpiStore, false>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   } else {
-    const int64_t n2 = (int64_t)N * H;
-    hipLaunchKernelGGL(grouped_ffn2_f32_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, (const float*)h,
-                       (const float*)down, offsets, E, N, I, H, (float*)y);
+    return launch_gen_ffn2(h, down, dt, offsets, E, N, H, I, y, s);
   }
   return hipGetLastError();
 }

@@ -59,6 +59,27 @@ hipError_t launch_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, int N,
 hipError_t launch_gemm_wgrad(const void* P, const void* Q, int M, int Nq, int E, const int32_t* offsets, void* d_w,
                              hipStream_t s, int max_wg = 0);
 
+// generic.hip: the expert FFN products for fp32 and for bf16 shapes the matrix-core kernels do not
+// take (H or I not a multiple of 8, buffers not 16-byte aligned); one thread per output element
+hipError_t launch_gen_ffn1(const void* A, const void* W, int dt, const int32_t* offsets, int E, int N, int H, int I,
+                           void* h, void* gu_saved, const int32_t* a_slot, int a_div, hipStream_t s);
+hipError_t launch_gen_ffn2(const void* Hh, const void* D, int dt, const int32_t* offsets, int E, int N, int H, int I,
+                           void* y, hipStream_t s);
+hipError_t launch_gen_down_bwd(const void* d_y, const void* down, const void* gu_saved, int dt, int N, int H, int I,
+                               int E, const int32_t* offsets, void* d_gu, hipStream_t s);
+hipError_t launch_gen_gate_up_bwd(const void* d_gu, const void* gate_up, int dt, int N, int H, int I, int E,
+                                  const int32_t* offsets, void* d_x, hipStream_t s);
+hipError_t launch_gen_wgrad(const void* P, const void* Q, int dt, int M, int Nq, int E, const int32_t* offsets,
+                            void* d_w, hipStream_t s);
+// the matrix-core kernels take bf16 with every width a multiple of 8 and 16-byte aligned buffers
+inline bool mfma_shapes_ok(int dt, int a, int b, const void* p0, const void* p1 = nullptr, const void* p2 = nullptr,
+                           const void* p3 = nullptr, const void* p4 = nullptr, const void* p5 = nullptr,
+                           const void* p6 = nullptr, const void* p7 = nullptr) {
+  const uintptr_t m = (uintptr_t)p0 | (uintptr_t)p1 | (uintptr_t)p2 | (uintptr_t)p3 | (uintptr_t)p4 | (uintptr_t)p5 |
+                      (uintptr_t)p6 | (uintptr_t)p7;
+  return dt == kBF16 && a % 8 == 0 && b % 8 == 0 && (m & 15u) == 0;
+}
+
 // backward.hip
 hipError_t launch_combine_bwd(const void* d_out, const void* y, int dt, int T, int H, int k, const int32_t* row_of_slot,
                               const float* topk_w, void* d_y, float* d_w, hipStream_t s);

@@ -104,50 +104,56 @@ def test_router_logits_bwd_no_tokens():
     assert torch.all(dwg == 0) and dx.shape == (0, H)
 
 
-@pytest.mark.parametrize("counts,H,I", [
-    ([0, 300, 1, 0, 257, 142], 136, 40),
-    ([256, 256, 256, 256], 256, 192),
-    ([1000], 64, 24),
-    ([3, 0, 0, 517, 31, 64, 0, 1], 512, 128),
-    ([0, 0, 0], 64, 32),
-    ([600, 5], 7168, 256),
-    ([288, 289, 270, 0, 257], 136, 40),                # tiles with an extra band of one or two blocks
-    ([320, 321, 300, 0, 641], 136, 40),                # two-block bands and 320-row tiles
+@pytest.mark.parametrize("counts,H,I,dtype", [
+    ([0, 300, 1, 0, 257, 142], 136, 40, "bf16"),
+    ([256, 256, 256, 256], 256, 192, "bf16"),
+    ([1000], 64, 24, "bf16"),
+    ([3, 0, 0, 517, 31, 64, 0, 1], 512, 128, "bf16"),
+    ([0, 0, 0], 64, 32, "bf16"),
+    ([600, 5], 7168, 256, "bf16"),
+    ([288, 289, 270, 0, 257], 136, 40, "bf16"),        # tiles with an extra band of one or two blocks
+    ([320, 321, 300, 0, 641], 136, 40, "bf16"),        # two-block bands and 320-row tiles
+    # the generic kernels: fp32, and bf16 widths that are not multiples of 8
+    ([17, 0, 40], 64, 32, "f32"),
+    ([5, 9, 0, 2], 24, 12, "f32"),
+    ([0, 30, 1, 0, 25, 14], 36, 20, "bf16"),
 ])
-def test_grouped_swiglu_ffn_bwd(counts, H, I):
+def test_grouped_swiglu_ffn_bwd(counts, H, I, dtype):
     E = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     N = int(offsets[-1])
-    xp = normal((N, H), 1.0, (981, N, H), "bf16")
-    gu = normal((E * H, 2 * I), 0.08, (982, E, H, I), "bf16")
-    dn = normal((E * I, H), 0.08, (983, E, H, I), "bf16")
-    d_y = normal((N, H), 1.0, (984, N, H), "bf16")
-    gu_saved = torch.empty((N, 2 * I), dtype=torch.bfloat16, device="cuda")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xp = normal((N, H), 1.0, (981, N, H), dtype)
+    gu = normal((E * H, 2 * I), 0.08, (982, E, H, I), dtype)
+    dn = normal((E * I, H), 0.08, (983, E, H, I), dtype)
+    d_y = normal((N, H), 1.0, (984, N, H), dtype)
+    gu_saved = torch.empty((N, 2 * I), dtype=tdt, device="cuda")
     _, h = moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), dev(offsets), gu_saved=gu_saved)
-    d_gate_up = torch.full((E * H, 2 * I), 7.0, dtype=torch.bfloat16, device="cuda")
-    d_down = torch.full((E * I, H), 7.0, dtype=torch.bfloat16, device="cuda")
+    d_gate_up = torch.full((E * H, 2 * I), 7.0, dtype=tdt, device="cuda")
+    d_down = torch.full((E * I, H), 7.0, dtype=tdt, device="cuda")
     d_xp, d_gate_up, d_down, d_gu = moe.moe_grouped_swiglu_ffn_bwd(dev(d_y), dev(xp), gu_saved, h, dev(gu), dev(dn),
                                                                    dev(offsets), d_gate_up=d_gate_up, d_down=d_down)
     g_dgu, g_ddn = as64(host(d_gate_up)), as64(host(d_down))
     if N:
         ref_dx, ref_dgu = oracle.expert_rows_bwd(xp, d_y, offsets, gu, dn, want_gu=True)
-        assert rel_err(host(d_gu), ref_dgu) <= TOL["bf16"]
-        assert rel_err(host(d_xp), ref_dx) <= TOL["bf16"]
+        assert rel_err(host(d_gu), ref_dgu) <= TOL[dtype]
+        assert rel_err(host(d_xp), ref_dx) <= TOL[dtype]
     for e in range(E):
         blk_gu, blk_dn = g_dgu[e * H:(e + 1) * H], g_ddn[e * I:(e + 1) * I]
         if counts[e] == 0:                         # experts without rows: exact zeros
             assert np.all(blk_gu == 0.0) and np.all(blk_dn == 0.0)
             continue
         r_gu, r_dn = oracle.expert_weight_grads(xp, d_y, offsets, gu, dn, e)
-        assert rel_err(blk_gu, r_gu) <= TOL["bf16"], f"d_gate_up of expert {e}"
-        assert rel_err(blk_dn, r_dn) <= TOL["bf16"], f"d_down of expert {e}"
+        assert rel_err(blk_gu, r_gu) <= TOL[dtype], f"d_gate_up of expert {e}"
+        assert rel_err(blk_dn, r_dn) <= TOL[dtype], f"d_down of expert {e}"
 
 
-@pytest.mark.parametrize("T,H,I,E,k,shared", [(300, 136, 40, 16, 4, 1), (257, 256, 64, 64, 8, 0),
-                                              (64, 64, 32, 8, 2, 1), (1, 64, 32, 8, 8, 1)])
+@pytest.mark.parametrize("T,H,I,E,k,shared,dtype", [(300, 136, 40, 16, 4, 1, "bf16"), (257, 256, 64, 64, 8, 0, "bf16"),
+                                                    (64, 64, 32, 8, 2, 1, "bf16"), (1, 64, 32, 8, 8, 1, "bf16"),
+                                                    (96, 48, 24, 8, 2, 1, "f32"), (40, 36, 20, 4, 2, 0, "bf16")])
 @pytest.mark.parametrize("renorm", [True, False])
-def test_layer_backward(T, H, I, E, k, shared, renorm):
-    d = make_layer_inputs(T, H, I, E, k, "bf16", (985, T, E), w_std=0.08, wg_std=0.3, shared=shared,
+def test_layer_backward(T, H, I, E, k, shared, dtype, renorm):
+    d = make_layer_inputs(T, H, I, E, k, dtype, (985, T, E), w_std=0.08, wg_std=0.3, shared=shared,
                           backward=True)
     sgu = dev(d["shared_gate_up"]) if shared else None
     sdn = dev(d["shared_down"]) if shared else None
@@ -159,15 +165,15 @@ def test_layer_backward(T, H, I, E, k, shared, renorm):
     ref_out, ridx, _, _ = oracle.moe_forward(d["x"], d["gate_up"], d["down"], k, w_gate=d["w_gate"], renorm=renorm,
                                              shared_gate_up=d.get("shared_gate_up"), shared_down=d.get("shared_down"))
     assert np.array_equal(host(bufs.topk_idx), ridx)
-    assert rel_err(host(out), ref_out) <= TOL["bf16"]
+    assert rel_err(host(out), ref_out) <= TOL[dtype]
     r = oracle.moe_backward(d["x"], d["gate_up"], d["down"], k, d["d_out"], w_gate=d["w_gate"], renorm=renorm,
                             shared_gate_up=d.get("shared_gate_up"), shared_down=d.get("shared_down"))
-    assert rel_err(host(g.d_w), r["d_w"]) <= TOL["bf16"]
-    assert rel_err(host(g.d_logits), r["d_logits"]) <= TOL["bf16"]
-    assert rel_err(host(g.d_w_gate), r["d_w_gate"]) <= TOL["bf16"]
-    assert rel_err(host(g.d_x), r["d_x"]) <= TOL["bf16"]
-    assert rel_err(host(g.d_gate_up), np.concatenate([r["d_gate_up"][e] for e in range(E)])) <= TOL["bf16"]
-    assert rel_err(host(g.d_down), np.concatenate([r["d_down"][e] for e in range(E)])) <= TOL["bf16"]
+    assert rel_err(host(g.d_w), r["d_w"]) <= TOL[dtype]
+    assert rel_err(host(g.d_logits), r["d_logits"]) <= TOL[dtype]
+    assert rel_err(host(g.d_w_gate), r["d_w_gate"]) <= TOL[dtype]
+    assert rel_err(host(g.d_x), r["d_x"]) <= TOL[dtype]
+    assert rel_err(host(g.d_gate_up), np.concatenate([r["d_gate_up"][e] for e in range(E)])) <= TOL[dtype]
+    assert rel_err(host(g.d_down), np.concatenate([r["d_down"][e] for e in range(E)])) <= TOL[dtype]
     if shared:
-        assert rel_err(host(g.d_shared_gate_up), r["d_shared_gate_up"]) <= TOL["bf16"]
-        assert rel_err(host(g.d_shared_down), r["d_shared_down"]) <= TOL["bf16"]
+        assert rel_err(host(g.d_shared_gate_up), r["d_shared_gate_up"]) <= TOL[dtype]
+        assert rel_err(host(g.d_shared_down), r["d_shared_down"]) <= TOL[dtype]

@@ -219,6 +219,9 @@ def test_router_topk_permute(T, H, E, k, rows, renorm):
     ([290, 0, 300, 17, 320], 56, 72, "bf16"),
     ([301, 64, 0, 289], 120, 200, "bf16"),
     ([257, 33, 1], 200, 56, "bf16"),
+    # bf16 widths that are not multiples of 8: the generic kernels
+    ([0, 30, 1, 0, 25, 14], 36, 20, "bf16"),
+    ([70, 3], 100, 13, "bf16"),
 ])
 def test_grouped_swiglu_ffn(counts, H, I, dtype):
     E = len(counts)
