@@ -13,9 +13,11 @@ Prints ONE JSON line. `value` is tokens/s of the layer. The timed region is brac
 torch.cuda.synchronize(). An eager pass with HIP events recorded on the launch stream between the
 calls gives each stage's duration, from which the roofline of the dominant kernel (the gate_up
 grouped GEMM) is computed; the timed step is then the same one-stream sequence captured once in a
-HIP graph and replayed (--no-graph: the eager pass is the timed step). The CPU baseline is the oracle (C, fp64, OpenMP) timed on a bounded sample of the same
-tokens. --copy-calibration runs one 512 MiB device-to-device copy first, the known-size kernel
-that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters into HBM bytes.
+HIP graph and replayed (--no-graph: the eager pass is the timed step). Every timed region follows
+its own untimed warm-up (by default about one second of steps: from idle, the clocks take that long
+to settle at the board's power limit). The CPU baseline is the oracle (C, fp64, OpenMP) timed on a
+bounded sample of the same tokens. --copy-calibration runs one 512 MiB device-to-device copy first,
+the known-size kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters into HBM bytes.
 """
 from __future__ import annotations
 
@@ -34,6 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
+WARMUP_SECONDS = 1.0         # default warm-up length (see --warmup)
 METRIC = "MoE layer tokens/s at 1 GPU; grouped-GEMM MFMA util %; permute/combine HBM GB/s"
 KERNEL_SOURCES = ["mixture_experts_layer_renorm_amd/csrc/grouped_gemm.hip",
                   "mixture_experts_layer_renorm_amd/csrc/common.hpp"]   # the dominant kernel's sources
@@ -173,8 +176,11 @@ def pct(a, q):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before each timed region (default: as many as fill about "
+                         f"{WARMUP_SECONDS:g} s; from idle the clocks take that long to settle at the board's power "
+                         "limit, and a shorter warm-up times the ramp rather than the layer)")
     ap.add_argument("--workload", default="qwen3_moe",
                     choices=["qwen3_moe", "long_seq", "tiny_f32", "fine_grained", "ep_rank_zipf"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0 = skip)")
@@ -321,7 +327,20 @@ def main():
         if evs is not None:
             evs[ns].record(stream)
 
-    for _ in range(args.warmup):
+    done = 0
+    if args.warmup is None:
+        # after a first step (module loading, first-touch), three steps give the step time from which
+        # the default warm-up length follows; all four are part of the warm-up
+        step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        per_step = (time.perf_counter() - t0) / 3
+        args.warmup = max(5, int(np.ceil(WARMUP_SECONDS / per_step)))
+        done = 4
+    for _ in range(args.warmup - done):
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
