@@ -10,17 +10,16 @@ constexpr int kWave = 64;
 // bf16 is carried as its raw 16-bit pattern.
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// fp32 -> bf16, round to nearest, ties to even, fp32 subnormals kept; NaN stays NaN (quieted). One
+// v_cvt_pk_bf16_f32 per pair: for every non-NaN fp32 pattern the same bits as rounding in integer
+// arithmetic (add 0x7fff plus the lowest kept bit, drop the low half).
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_hw f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_hw));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -1291,11 +1291,12 @@ __device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, int bytes) {
 //  - the last three K steps issue the next tile's first A stage and B steps 0-2 (where the
 //    one-tile kernel issues zero-filling DMAs past K), so the next tile's data is on its way
 //    during the epilogue;
-//  - the epilogue stages the finished tile through the A stage the last two steps used, one
-//    64-row quarter at a time, and writes whole rows with buffer stores. Every wave issues the
-//    same number of stores (rows past the tile are dropped by the descriptor), and the stores
-//    are issued after the prefetches, so the next tile's first wait leaves exactly them in
-//    flight: they drain while the next tile computes;
+//  - the epilogue stages the finished tile through the A stage the last two steps used, each
+//    wave its own block through its own part of it (no workgroup barrier but one at the end),
+//    and writes whole 128-byte row segments with buffer stores. Every wave issues the same
+//    number of stores (rows past the tile are dropped by the descriptor), and the stores are
+//    issued after the prefetches, so the next tile's first wait leaves exactly them in flight:
+//    they drain while the next tile computes;
 //  - with gathered rows, the slot map of the next tile's rows is brought into LDS by one DMA of
 //    wave 0 in the current tile's first step.
 template <int EPI, bool GATHER, bool KF>
@@ -1693,64 +1694,61 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
       }
     }
 
-    // ---- epilogue: 64-row quarters through sA1 (free after the last step's barrier; the
-    // prefetches went to sA0 and sB0..sB2). Lane holds row (lane & 31) of each 32-row block and,
-    // per 32-column block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for element q. The lane
-    // terms are built from a value the compiler cannot see through, so that they are computed
-    // here rather than hoisted out of the tile loop (where they would stay live through K).
+    // ---- epilogue: every wave writes its bf16 block (SwiGLU: 64 rows x 64 h columns; store: 64 x
+    // 128) as 32 x 64 pieces, each transposed through the wave's own 4 KB of sA1 (free after the
+    // last step's barrier; the prefetches went to sA0 and sB0..sB2), so that each store writes
+    // whole 128-byte row segments. Lane holds row (lane & 31) of each 32-row block and, per
+    // 32-column block, columns (q / 4) * 8 + (lane / 32) * 4 + q % 4 for element q; in the wave's
+    // buffer, 16-byte chunk c of row r sits at chunk c ^ (r & 7). Only the wave itself reads what it
+    // wrote, so no workgroup barrier is needed until the end. The lane terms are built from a value
+    // the compiler cannot see through, so that they are computed here rather than hoisted out of
+    // the tile loop (where they would stay live through K).
     int zv;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zv));
     const int lane_e = lane + zv;
     const int lr = lane_e & 31;
+    uint8_t* const wbuf = sA1 + wave * 4096;
+    const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(g.C + (int64_t)cur.m0 * g.ldc), (short)0, min(cur.mvalid, kBM) * g.ldc * 2, kBufferWord3);
+    // rows row0 .. row0 + 31 of the tile, global columns col0 .. col0 + 63 (rows past the tile are
+    // dropped by the descriptor, columns past N by their offset): 4 buffer stores per lane
+    auto piece_out = [&](const uint2 (&v)[2][4], int row0, int col0) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          *reinterpret_cast<uint2*>(wbuf + lr * 128 + (((nb * 4 + gq) ^ (lr & 7)) << 4) + (lane_e >> 5) * 8) =
+              v[nb][gq];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = j * 8 + (lane_e >> 3), c = lane_e & 7;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(wbuf + r * 128 + ((c ^ (r & 7)) << 4));
+        const int col = col0 + c * 8;
+        const int off = col < g.N ? ((row0 + r) * g.ldc + col) * 2 : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(w, rsC, off, 0, 0);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read back before the buffer is rewritten
+    };
     if constexpr (EPI == kEpiStore) {
-      // rounded to bf16 first, so that the quarter loop keeps 64 packed registers live, not the
-      // 128 accumulators; quarter qb = rows 64 qb .. +63 (waves 2 qb, 2 qb + 1), 512-byte rows in
-      // sA1, 16-byte chunk c of row r at chunk c ^ (r & 31); then every wave writes 8 rows, 2 per
-      // 1 KB store
-      uint2 pk[2][4][4];
+      // pieces are the wave's column halves of each 32-row block, rounded to bf16 one at a time
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nh = 0; nh < 2; ++nh) {
+          uint2 pk[2][4];
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            pk[mb][nb][gq] = make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
-                                        pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
-      const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(g.C + (int64_t)cur.m0 * g.ldc), (short)0, min(cur.mvalid, kBM) * g.ldc * 2, kBufferWord3);
-#pragma unroll 1
-      for (int qb = 0; qb < 4; ++qb) {
-        if (wm == qb) {
+          for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const int r = mb * 32 + lr;
-            uint8_t* rowp = sA1 + r * 512 + (lane_e >> 5) * 8;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-              for (int gq = 0; gq < 4; ++gq) {
-                const int chunk = (wn * 16 + nb * 4 + gq) ^ (r & 31);
-                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = pk[mb][nb][gq];
-              }
-          }
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x16& a = acc[mb][2 * nh + nb];
+              pk[nb][gq] = make_uint2(pack_bf16x2(a[gq * 4 + 0], a[gq * 4 + 1]), pack_bf16x2(a[gq * 4 + 2], a[gq * 4 + 3]));
+            }
+          piece_out(pk, wm * 64 + mb * 32, cur.nt * kBN + wn * 128 + nh * 64);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = wave * 8 + j * 2 + (lane_e >> 5);
-          const int c = lane_e & 31;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sA1 + r * 512 + ((c ^ (r & 31)) << 4));
-          const int col = cur.nt * kBN + c * 8;
-          const int off = col < g.N ? ((qb * 64 + r) * g.ldc + col) * 2 : kOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 0);
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
     } else {
       // The saved g | u (training only) go out straight from the accumulators; then h = silu(g) u
-      // is rounded to bf16 (32 packed registers) and staged: quarter qb = rows 64 qb .. +63,
-      // 256-byte rows (128 columns) in sA1, chunk c of row r at chunk c ^ (r & 15); every wave then
-      // writes 8 rows, 4 per 1 KB store.
+      // is rounded to bf16 (32 packed registers), one piece per 32-row block
       if (g.gu_out) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -1785,37 +1783,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
             for (int qq = 0; qq < 4; ++qq) hv[qq] = silu_f(acc[mb][nb][gq * 4 + qq]) * acc[mb][nb + 2][gq * 4 + qq];
             hp[mb][nb][gq] = make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
           }
-      const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(g.C + (int64_t)cur.m0 * g.ldc), (short)0, min(cur.mvalid, kBM) * g.ldc * 2, kBufferWord3);
-#pragma unroll 1
-      for (int qb = 0; qb < 4; ++qb) {
-        if (wm == qb) {
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const int r = mb * 32 + lr;
-            uint8_t* rowp = sA1 + r * 256 + (lane_e >> 5) * 8;
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-              for (int gq = 0; gq < 4; ++gq) {
-                const int chunk = (wn * 8 + nb * 4 + gq) ^ (r & 15);
-                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = hp[mb][nb][gq];
-              }
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = wave * 8 + j * 4 + (lane_e >> 4);
-          const int c = lane_e & 15;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sA1 + r * 256 + ((c ^ (r & 15)) << 4));
-          const int col = cur.nt * 128 + c * 8;
-          const int off = col < g.N ? ((qb * 64 + r) * g.ldc + col) * 2 : kOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 0);
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
+      for (int mb = 0; mb < 2; ++mb) piece_out(hp[mb], wm * 64 + mb * 32, cur.nt * 128 + wn * 64);
     }
+    // every wave is done with sA1 before the next tile's first step refills it
+    asm volatile("s_barrier" ::: "memory");
     if (!has_next) break;
     cur = nxt;
     L = Ln;
