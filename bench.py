@@ -507,7 +507,11 @@ def main():
         roof = {"bound": "mfma", "achieved": round(gu_flops / t_gu / 1e12, 1), "peak": peak_tf, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = load_traffic(wl.name, "gathered" if gather else "x_perm")
-    roof["kernel"] = f"grouped_gemm_fwd_kernel<0, {'true' if gather else 'false'}> (gate_up + SwiGLU)"
+    if tdt == torch.bfloat16 and H % 8 == 0 and I % 8 == 0:
+        kf = "true" if H % 128 == 0 else "false"   # K = H a multiple of four K steps
+        roof["kernel"] = f"grouped_gemm_fwd_kernel<0, {'true' if gather else 'false'}, {kf}> (gate_up + SwiGLU)"
+    else:
+        roof["kernel"] = "gen_ffn1_kernel (gate_up + SwiGLU, generic path)"
     roof["algorithmic_bytes"] = gu_bytes
     roof["algorithmic_flops"] = gu_flops
     roof["avg_launch_us"] = round(t_gu * 1e6, 2)
