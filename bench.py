@@ -142,31 +142,45 @@ def cpu_baseline(wl, d, budget_s: float):
             "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
-def tile_schedule(counts, N_cols, bm=320, bn=256, xcds=8):
-    """The row-grouped GEMMs' tile list as the kernel derives it on the device: an expert with c rows
-    gets ceil(c / bm) row tiles of near-equal height (none when c = 0), each with ceil(N_cols / bn)
-    column tiles; tile L goes to XCD L // Q with Q = ceil(tiles / 8). Returns per-expert tile counts
-    and per-XCD tile counts and row-tile work (rows x columns)."""
+def tile_schedule(counts, N_cols, bm=320, bn=256, xcds=8, cus=256, sort_max_e=256):
+    """The persistent forward GEMMs' tile list and walk as the kernel derives them on the device: an
+    expert with c rows gets n = ceil(c / bm) row tiles of near-equal height (none when c = 0), each
+    with ceil(N_cols / bn) column tiles. With whole rounds on every XCD (or more than four rounds on
+    average) XCD x takes the contiguous eighth of the list in expert order; otherwise ("balance")
+    the experts are listed tallest first (ties by index, up to sort_max_e experts) and row tile R
+    goes to XCD R mod 8. Each XCD deals its tiles to its cus / 8 workgroups in rounds, back and
+    forth. Returns per-expert tile counts, per-XCD tile counts and row-tile work (rows x columns),
+    the most tiles any workgroup runs, and whether the walk balanced."""
     ntn = (N_cols + bn - 1) // bn
     rt = [(c + bm - 1) // bm if c > 0 else 0 for c in counts]
-    tiles = []
-    for e, c in enumerate(counts):
+    height = [(c + r - 1) // r if r > 0 else 0 for c, r in zip(counts, rt)]
+    G = max(8, cus // 8 * 8)
+    nbx = G // xcds
+    RT = sum(rt)
+    total = RT * ntn
+    whole = RT % xcds == 0 and (RT // xcds * ntn) % nbx == 0
+    balance = not whole and total <= 4 * G
+    order = (sorted(range(len(counts)), key=lambda e: (-height[e], e))
+             if balance and len(counts) <= sort_max_e else list(range(len(counts))))
+    row_tiles = []
+    for e in order:
+        c = counts[e]
         for j in range(rt[e]):
-            r0, r1 = j * c // rt[e], (j + 1) * c // rt[e]
-            for nt in range(ntn):
-                tiles.append((e, r1 - r0, min(bn, N_cols - nt * bn)))
-    total = len(tiles)
-    Q = (total + xcds - 1) // xcds
+            row_tiles.append((j + 1) * c // rt[e] - j * c // rt[e])
+    tiles = [rows for rows in row_tiles for _ in range(ntn)]
     per_xcd = [0] * xcds
     work = [0] * xcds
-    for L, (_, rows, cols) in enumerate(tiles):
-        per_xcd[L // Q] += 1
-        work[L // Q] += rows * cols
+    Q = (total + xcds - 1) // xcds
+    for L, rows in enumerate(tiles):
+        x = (L // ntn) % xcds if balance else L // Q
+        per_xcd[x] += 1
+        work[x] += rows * N_cols
     mean_w = sum(work) / xcds if xcds else 0
-    return {"tiles": total, "tiles_per_expert": [r * ntn for r in rt],
+    return {"tiles": total, "tiles_per_expert": [int(r * ntn) for r in rt],
             "empty_experts": int(sum(1 for c in counts if c == 0)),
             "tiles_of_empty_experts": int(sum(r * ntn for r, c in zip(rt, counts) if c == 0)),
-            "tiles_per_xcd": per_xcd, "xcd_work_max_over_mean": round(max(work) / mean_w, 4) if mean_w else None}
+            "tiles_per_xcd": per_xcd, "xcd_work_max_over_mean": round(max(work) / mean_w, 4) if mean_w else None,
+            "workgroup_tiles_max": max((n + nbx - 1) // nbx for n in per_xcd), "balanced_walk": balance}
 
 
 def pct(a, q):

@@ -55,6 +55,7 @@ constexpr int kTileB = kBK * kBN * 2;
 constexpr int kWaves = kGemmThreads / 64;
 constexpr int kDmaB = kTileB / 1024 / kWaves;  // DMA instructions (1 KB each) per wave per step, operand B
 constexpr int kGemmMaxE = 1024;
+constexpr int kSortMaxE = 256;  // the persistent forward lists its experts tallest first up to this many
 // Row-grouped products: a tile holds up to kBMX = 320 rows, the regular 256 plus an extra band of
 // up to 64 rows, so an expert with 257..320 rows (E = 128, k = 8, T = 4096 gives counts of 256 with
 // a standard deviation near 16) is one tile instead of a full tile plus a nearly empty one that
@@ -1283,11 +1284,14 @@ __device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, int bytes) {
 // (EPI = kEpiStore), the rows from the grouped buffer or (GATHER) from the token matrix through
 // the slot map.
 //
-// One workgroup per CU walks a slice of the same tile list as grouped_gemm_bf16_kernel, with the
-// same split over the XCDs (XCD x owns the contiguous range [x Q, (x+1) Q); its workgroups take
-// those tiles in turn). Per tile the K loop is the one above. What changes is the tile boundary,
-// where the one-tile kernel leaves every CU idle at once (set-up, pipeline fill, epilogue):
-//  - the tile list is built once per workgroup (expert offsets and row-tile prefix in LDS);
+// One workgroup per CU walks the tiles of grouped_gemm_bf16_kernel's list: each XCD takes an
+// eighth of the list and deals it to its workgroups in rounds, back and forth; when a few rounds
+// would end in a partial one, the experts are listed tallest first and the row tiles dealt
+// round-robin to the XCDs instead (see the tile list and the walk below), so that skewed expert
+// sizes end in a last round of short tiles. Per tile the K loop is the one above. What changes is the tile boundary, where the one-tile kernel leaves every CU
+// idle at once (set-up, pipeline fill, epilogue):
+//  - the tile list is built once per workgroup (expert offsets, list order and row-tile prefix
+//    in LDS);
 //  - the last three K steps issue the next tile's first A stage and B steps 0-2 (where the
 //    one-tile kernel issues zero-filling DMAs past K), so the next tile's data is on its way
 //    during the epilogue;
@@ -1306,7 +1310,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
   __shared__ __attribute__((aligned(1024))) int s_slot[512];  // slot map of the next tile's rows (gathered)
   __shared__ int s_off[kGemmMaxE + 1];
-  __shared__ int s_pref[kGemmMaxE + 1];
+  __shared__ __attribute__((aligned(16))) int s_pref[kGemmMaxE + 4];
+  __shared__ short s_ord[kGemmMaxE];  // the expert at each position of the tile list
   __shared__ int s_wtot[kGemmThreads / kWave];
 
   const int tid = threadIdx.x;
@@ -1314,24 +1319,88 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = (wave >> 1) & 3, wn = wave & 1;
 
-  // ---- the tile list: expert e owns ceil(c_e / kBMX) row tiles of near-equal height, each with
-  // ntiles_n column tiles; s_pref = exclusive prefix of the row tiles over the experts
+  // ---- the tile list: expert e owns n_e = ceil(c_e / kBMX) row tiles of near-equal height (at
+  // most h_e = ceil(c_e / n_e) rows), each with ntiles_n column tiles; s_pref = exclusive prefix of
+  // the row tiles over the list. The experts are listed in index order, or tallest first (ties by
+  // index) when the walk below balances (and there are at most kSortMaxE experts).
   for (int i = tid; i <= g.E; i += kGemmThreads) s_off[i] = g.offsets[i];
   __syncthreads();
-  for (int e = tid; e < g.E; e += kGemmThreads) {
-    const int c = s_off[e + 1] - s_off[e];
-    s_pref[e] = c > 0 ? (c + kBMX - 1) / kBMX : 0;
+  for (int i = tid; i < g.E; i += kGemmThreads) {
+    const int c = s_off[i + 1] - s_off[i];
+    s_ord[i] = (short)i;
+    s_pref[i] = c > 0 ? (c + kBMX - 1) / kBMX : 0;
   }
   __syncthreads();
   block_exclusive_scan<kGemmThreads>(s_pref, g.E, s_wtot);
   const int ntn = g.ntiles_n;
-  const int total = __builtin_amdgcn_readfirstlane(s_pref[g.E]) * ntn;
-  const int xcd = blockIdx.x & 7;
+  const int RT = __builtin_amdgcn_readfirstlane(s_pref[g.E]);  // row tiles in the list
+  const int total = RT * ntn;
   const int nbx = (int)(gridDim.x >> 3);  // workgroups per XCD (the grid is a multiple of 8)
+  // The walk deals each XCD's tiles to its nbx workgroups in rounds. With whole rounds on every XCD,
+  // or more than four rounds on average, XCD x takes the contiguous eighth [x Q, (x + 1) Q) of the
+  // list in index order, Q = ceil(tiles / 8): an expert's row tiles share one XCD's L2 (its weights
+  // are streamed once per XCD) and both forward products split the experts alike. Otherwise the
+  // last round is partial and, with few rounds, costs a large share of the product: then the walk
+  // balances. The experts are listed tallest first and row tile R goes to XCD R mod 8, so each XCD
+  // gets every eighth of the heights and its partial last round holds its shortest tiles.
+  const bool whole = (RT & 7) == 0 && ((RT >> 3) * ntn) % nbx == 0;
+  const bool balance = !whole && total <= 4 * (int)gridDim.x;
+  if (balance && g.E <= kSortMaxE) {
+    static_assert(kSortMaxE <= kGemmThreads, "one expert per thread");
+    __syncthreads();  // every thread has read the row-tile total
+    if (tid < g.E) {
+      const int c = s_off[tid + 1] - s_off[tid];
+      const int n = c > 0 ? (c + kBMX - 1) / kBMX : 0;
+      s_pref[tid] = n > 0 ? (c + n - 1) / n : 0;
+    }
+    __syncthreads();
+    int rk = 0;  // the expert's position: taller experts, then equal ones of lower index
+    if (tid < g.E) {
+      const int h = s_pref[tid];
+#pragma unroll 4
+      for (int j0 = 0; j0 < g.E; j0 += 4) {  // four heights per LDS read (entries past E are masked)
+        const int4 hv = *reinterpret_cast<const int4*>(s_pref + j0);
+        const int hs[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int j = j0 + k4;
+          rk += (j < g.E && (hs[k4] > h || (hs[k4] == h && j < tid))) ? 1 : 0;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < g.E) s_ord[rk] = (short)tid;
+    __syncthreads();
+    if (tid < g.E) {
+      const int e = s_ord[tid];
+      const int c = s_off[e + 1] - s_off[e];
+      s_pref[tid] = c > 0 ? (c + kBMX - 1) / kBMX : 0;
+    }
+    __syncthreads();
+    block_exclusive_scan<kGemmThreads>(s_pref, g.E, s_wtot);
+  }
+
+  // ---- the walk. Workgroup b runs on XCD b mod 8 and is workgroup j = b div 8 of that XCD; of the
+  // XCD's n_x tiles it takes tile r nbx + j in an even round r and r nbx + nbx - 1 - j in an odd
+  // one (back and forth: a workgroup that took one of the last tiles of a round takes one of the
+  // first of the next).
+  const int xcd = (int)(blockIdx.x & 7);
+  const int wj = (int)(blockIdx.x >> 3);
   const int Q = (total + 7) >> 3;
-  const int t_end = min((xcd + 1) * Q, total);
-  int L = xcd * Q + (int)(blockIdx.x >> 3);
-  if (L >= t_end) return;
+  const int n_x = balance ? (RT > xcd ? (RT - xcd + 7) >> 3 : 0) * ntn : max(0, min(Q, total - xcd * Q));
+  // the list index (row tile * ntn + column tile) of this workgroup's tile in round r, or -1
+  auto pos = [&](int r) -> int {
+    const int q = r * nbx + ((r & 1) ? nbx - 1 - wj : wj);
+    if (q >= n_x) return -1;
+    if (!balance) return xcd * Q + q;
+    int dn;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(dn) : "s"(ntn));
+    const int l = (int)((uint32_t)q / (uint32_t)dn);
+    return (l * 8 + xcd) * ntn + (q - l * dn);
+  };
+  int rnd = 0;
+  int L = pos(0);
+  if (L < 0) return;
 
   struct Tile {
     int e, m0, mvalid, nt;
@@ -1343,7 +1412,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
     asm volatile("s_mov_b32 %0, %1" : "=s"(dn) : "s"(ntn));
     const int mt_g = (int)((uint32_t)LL / (uint32_t)dn);
     t.nt = __builtin_amdgcn_readfirstlane(LL - mt_g * dn);
-    int lo = 0, hi = g.E;  // the last expert whose row tiles start at or before mt_g
+    int lo = 0, hi = g.E;  // the last list position whose row tiles start at or before mt_g
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_pref[mid] <= mt_g)
@@ -1351,9 +1420,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
       else
         hi = mid;
     }
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int p0 = __builtin_amdgcn_readfirstlane(s_pref[e]);
-    const int nte = __builtin_amdgcn_readfirstlane(s_pref[e + 1]) - p0;
+    const int e = __builtin_amdgcn_readfirstlane((int)s_ord[lo]);
+    const int p0 = __builtin_amdgcn_readfirstlane(s_pref[lo]);
+    const int nte = __builtin_amdgcn_readfirstlane(s_pref[lo + 1]) - p0;
     const int o0 = __builtin_amdgcn_readfirstlane(s_off[e]);
     const int c = __builtin_amdgcn_readfirstlane(s_off[e + 1]) - o0;
     // the expert's c rows in nte contiguous pieces, the first c % nte one row longer
@@ -1620,8 +1689,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
   using P1 = std::integral_constant<int, 1>;
   constexpr int kEpiStores = EPI == kEpiStore ? 16 : 8;  // buffer stores per wave per epilogue
   while (true) {
-    const int Ln = L + nbx;
-    const bool has_next = Ln < t_end;
+    const int Ln = pos(rnd + 1);
+    const bool has_next = Ln >= 0;
     // A stage 0 and B step 0 of this tile have landed (B 1, B 2 and the previous epilogue's
     // stores may still be in flight)
     if (pending_stores)
@@ -1791,6 +1860,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
     if (!has_next) break;
     cur = nxt;
     L = Ln;
+    ++rnd;
     pending_stores = 1;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last zero-filling DMAs into LDS
@@ -1812,10 +1882,11 @@ static int cu_count() {
   return cus;
 }
 
-// persistent forward product: one workgroup per CU (at most one per tile), a multiple of 8
+// persistent forward product: one workgroup per CU, a multiple of 8 (workgroups of an XCD without
+// a tile exit after building the tile list)
 template <int EPI, bool GATHER>
-static void launch_fwd(GemmArgs g, int64_t tiles, hipStream_t s) {
-  const int64_t grid = std::min<int64_t>(round_up8(tiles), std::max(8, cu_count() / 8 * 8));
+static void launch_fwd(GemmArgs g, hipStream_t s) {
+  const int64_t grid = std::max(8, cu_count() / 8 * 8);
   // K a multiple of four K steps (no tail, whole groups of four steps): per-step descriptor moves
   if (g.K % (kStages * kBK) == 0)
     hipLaunchKernelGGL((grouped_gemm_fwd_kernel<EPI, GATHER, true>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
@@ -1859,9 +1930,9 @@ hipError_t launch_gemm_gate_up(const void* x_perm, const void* gate_up, int dt, 
     g.b_rows = H;
     g.ntiles_n = (I + 127) / 128;
     if (slot_of_row)
-      launch_fwd<kEpiSwiglu, true>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+      launch_fwd<kEpiSwiglu, true>(g, s);
     else
-      launch_fwd<kEpiSwiglu, false>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+      launch_fwd<kEpiSwiglu, false>(g, s);
   } else {
     return launch_gen_ffn1(x_perm, gate_up, dt, offsets, E, N, H, I, h, gu_saved, slot_of_row, k, s);
   }
@@ -1885,7 +1956,7 @@ hipError_t launch_gemm_down(const void* h, const void* down, int dt, int N, int 
     g.b_expert = (int64_t)I * H;
     g.b_rows = I;
     g.ntiles_n = (H + kBN - 1) / kBN;
-    launch_fwd<kEpiStore, false>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+    launch_fwd<kEpiStore, false>(g, s);
   } else {
     return launch_gen_ffn2(h, down, dt, offsets, E, N, H, I, y, s);
   }
