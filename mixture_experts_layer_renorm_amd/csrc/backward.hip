@@ -293,7 +293,24 @@ static void launch_small_gemm(const SmallGemm<TA, TB, TC>& p, hipStream_t s) {
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kMmK = 32, kMmPitch = 96;
 
-template <typename TA, typename TB, typename TC>
+// 8 consecutive elements from a 16-byte aligned address, as fp32
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+}
+
+// VEC: A contiguous in m and B contiguous in n (dW_g = x^T dl), M and N multiples of 8 and every
+// 8-element group 16-byte aligned: a thread loads 8 consecutive m (n) of one k with vector loads.
+template <typename TA, typename TB, typename TC, bool VEC>
 __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA, TB, TC> p) {
   __shared__ float as[2][kMmK][kMmPitch];
   __shared__ float bs[2][kMmK][kMmPitch];
@@ -307,6 +324,20 @@ __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA
   float ra[2][8], rb[2][8];
   auto load = [&](int c, float* pa, float* pb) {
     const int k0 = c * kMmK;
+    if constexpr (VEC) {
+      const int k = k0 + (tid >> 3), m = m0 + (tid & 7) * 8, n = n0 + (tid & 7) * 8;
+      if (k < p.K && m < p.M)
+        load8(p.a + (int64_t)m + (int64_t)k * p.a_k, pa);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pa[j] = 0.0f;
+      if (k < p.K && n < p.N)
+        load8(p.b + (int64_t)k * p.b_k + (int64_t)n, pb);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = 0.0f;
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = tid + 256 * j;
@@ -323,6 +354,15 @@ __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA
     }
   };
   auto put = [&](int buf, const float* pa, const float* pb) {
+    if constexpr (VEC) {
+      const int kk = tid >> 3, o = (tid & 7) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        as[buf][kk][o + j] = pa[j];
+        bs[buf][kk][o + j] = pb[j];
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = tid + 256 * j;
@@ -387,7 +427,13 @@ __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA
 template <typename TA, typename TB, typename TC>
 static void launch_small_gemm_mfma(const SmallGemm<TA, TB, TC>& p, hipStream_t s) {
   dim3 grid((p.N + 63) / 64, (p.M + 63) / 64);
-  hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC>), grid, dim3(256), 0, s, p);
+  const bool vec = p.a_m == 1 && p.b_n == 1 && p.M % 8 == 0 && p.N % 8 == 0 && ((uintptr_t)p.a & 15) == 0 &&
+                   ((uintptr_t)p.b & 15) == 0 && (p.a_k * (int64_t)sizeof(TA)) % 16 == 0 &&
+                   (p.b_k * (int64_t)sizeof(TB)) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC, false>), grid, dim3(256), 0, s, p);
 }
 
 // ---------------------------------------------------------------------------------------------
