@@ -268,7 +268,8 @@ moe_status moe_router_topk_bwd(const float* logits, const int32_t* topk_idx, con
  * [MM 8.2/8.3] gradient of the gate logits = x @ w_gate of (1):
  *   d_w_gate = x^T @ d_logits   [H,E] fp32   (skipped when NULL; zeros when T = 0)
  *   d_x      = d_x_in + d_logits @ w_gate^T   [T,H] dt   (skipped when NULL; d_x_in may be NULL)
- * fp32 accumulation: d_w_gate on the matrix cores (fp32 MFMA), d_x on the vector ALU.                 */
+ * fp32 accumulation on the matrix cores (fp32 MFMA); d_x on the vector ALU when E is not a multiple
+ * of 8 or the buffers are not 16-byte aligned.                                                       */
 moe_status moe_router_logits_bwd(const void* x, const void* w_gate, const float* d_logits, moe_dtype dt, int T,
                                  int H, int E, float* d_w_gate, const void* d_x_in, void* d_x, hipStream_t stream);
 

@@ -308,9 +308,10 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
   v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
 }
 
-// VEC: A contiguous in m and B contiguous in n (dW_g = x^T dl), M and N multiples of 8 and every
-// 8-element group 16-byte aligned: a thread loads 8 consecutive m (n) of one k with vector loads.
-template <typename TA, typename TB, typename TC, bool VEC>
+// VEC = 1: A contiguous in m and B contiguous in n (dW_g = x^T dl), M and N multiples of 8; a thread
+// loads 8 consecutive m (n) of one k. VEC = 2: both contiguous in k (dX = dl W_g^T), K a multiple of
+// 8; a thread loads 8 consecutive k of one m (n). Every 8-element group is 16-byte aligned.
+template <typename TA, typename TB, typename TC, int VEC>
 __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA, TB, TC> p) {
   __shared__ float as[2][kMmK][kMmPitch];
   __shared__ float bs[2][kMmK][kMmPitch];
@@ -324,7 +325,21 @@ __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA
   float ra[2][8], rb[2][8];
   auto load = [&](int c, float* pa, float* pb) {
     const int k0 = c * kMmK;
-    if constexpr (VEC) {
+    if constexpr (VEC == 2) {
+      const int k = k0 + (tid & 3) * 8, m = m0 + (tid >> 2), n = n0 + (tid >> 2);
+      if (k < p.K && m < p.M)
+        load8(p.a + (int64_t)m * p.a_m + (int64_t)k, pa);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pa[j] = 0.0f;
+      if (k < p.K && n < p.N)
+        load8(p.b + (int64_t)k + (int64_t)n * p.b_n, pb);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = 0.0f;
+      return;
+    }
+    if constexpr (VEC == 1) {
       const int k = k0 + (tid >> 3), m = m0 + (tid & 7) * 8, n = n0 + (tid & 7) * 8;
       if (k < p.K && m < p.M)
         load8(p.a + (int64_t)m + (int64_t)k * p.a_k, pa);
@@ -354,7 +369,16 @@ __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA
     }
   };
   auto put = [&](int buf, const float* pa, const float* pb) {
-    if constexpr (VEC) {
+    if constexpr (VEC == 2) {
+      const int kk = (tid & 3) * 8, o = tid >> 2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        as[buf][kk + j][o] = pa[j];
+        bs[buf][kk + j][o] = pb[j];
+      }
+      return;
+    }
+    if constexpr (VEC == 1) {
       const int kk = tid >> 3, o = (tid & 7) * 8;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -427,13 +451,17 @@ __global__ __launch_bounds__(256) void small_gemm_mfma_kernel(const SmallGemm<TA
 template <typename TA, typename TB, typename TC>
 static void launch_small_gemm_mfma(const SmallGemm<TA, TB, TC>& p, hipStream_t s) {
   dim3 grid((p.N + 63) / 64, (p.M + 63) / 64);
-  const bool vec = p.a_m == 1 && p.b_n == 1 && p.M % 8 == 0 && p.N % 8 == 0 && ((uintptr_t)p.a & 15) == 0 &&
-                   ((uintptr_t)p.b & 15) == 0 && (p.a_k * (int64_t)sizeof(TA)) % 16 == 0 &&
-                   (p.b_k * (int64_t)sizeof(TB)) % 16 == 0;
-  if (vec)
-    hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC, true>), grid, dim3(256), 0, s, p);
+  const bool aligned = ((uintptr_t)p.a & 15) == 0 && ((uintptr_t)p.b & 15) == 0;
+  const bool mn = aligned && p.a_m == 1 && p.b_n == 1 && p.M % 8 == 0 && p.N % 8 == 0 &&
+                  (p.a_k * (int64_t)sizeof(TA)) % 16 == 0 && (p.b_k * (int64_t)sizeof(TB)) % 16 == 0;
+  const bool kc = aligned && p.a_k == 1 && p.b_k == 1 && p.K % 8 == 0 && (p.a_m * (int64_t)sizeof(TA)) % 16 == 0 &&
+                  (p.b_n * (int64_t)sizeof(TB)) % 16 == 0;
+  if (mn)
+    hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC, 1>), grid, dim3(256), 0, s, p);
+  else if (kc)
+    hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC, 2>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((small_gemm_mfma_kernel<TA, TB, TC, 0>), grid, dim3(256), 0, s, p);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -528,7 +556,12 @@ static void router_logits_bwd_t(const void* x, const void* w_gate, const float* 
     p.M = T;
     p.N = H;
     p.K = E;
-    launch_small_gemm(p, s);  // K = E is short: the vector-ALU tiles measured faster here
+    // on the matrix cores with 16-byte loads along K when the rows allow them; else the vector-ALU tiles
+    const bool kc = E % 8 == 0 && ((uintptr_t)dl & 15) == 0 && ((uintptr_t)w_gate & 15) == 0;
+    if (kc)
+      launch_small_gemm_mfma(p, s);
+    else
+      launch_small_gemm(p, s);
   }
 }
 
