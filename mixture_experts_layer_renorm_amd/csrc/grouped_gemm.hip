@@ -1303,9 +1303,13 @@ __device__ __forceinline__ i32x4 rsrc_advance(const i32x4& r, int bytes) {
 //    they drain while the next tile computes;
 //  - with gathered rows, the slot map of the next tile's rows is brought into LDS by one DMA of
 //    wave 0 in the current tile's first step.
-template <int EPI, bool GATHER, bool KF>
+// BR: the weights are a row tile (K contiguous: row n of the expert's block holds column n of the
+// product, as in the backward input gradient dX = dGU gate_up_e^T), staged [256 n][32 k] per step in
+// 64-byte rows and read with ds_read_b128; only with K a multiple of four steps and the plain store.
+template <int EPI, bool GATHER, bool KF, bool BR = false>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const GemmArgs g) {
   static_assert(EPI == kEpiSwiglu || EPI == kEpiStore, "the forward epilogues");
+  static_assert(!BR || (KF && EPI == kEpiStore && !GATHER), "row-tile weights: whole K steps, plain store");
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[kTileA2], sA1[kTileA2];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[kTileB], sB1[kTileB], sB2[kTileB], sB3[kTileB];
   __shared__ __attribute__((aligned(1024))) int s_slot[512];  // slot map of the next tile's rows (gathered)
@@ -1473,6 +1477,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
       o.x_off = (x_r * g.lda + xc * 8) * 2;
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
+      if constexpr (BR) {  // rows (wave kDmaB + i) 16 .. +16 of the tile's 256 weight rows, 4 lanes per row
+        const int r = (wave * kDmaB + i) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz_a(r);
+        const int n = t.nt * kBN + r;
+        o.b_off[i] = n < g.N ? (n * g.ldb + c * 8) * 2 : kOutOfRange;
+        continue;
+      }
       const int kr = (wave * kDmaB + i) * 2 + (lane >> 5);
       const int cb = (lane & 31) ^ swz_b(kr);
       int col;
@@ -1525,6 +1536,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
   auto dma_b = [&](const Ops& o, int kt, uint8_t* sb) {
     const int kb = kt * kBK * g.ldb * 2;  // k-rows past K are past the expert's block
     const uint32_t base = lds_addr(sb) + wb;
+    if constexpr (BR) {  // the step's 32 k of every row: the descriptor moves 64 bytes along the rows
+      // (plain loads: an expert's rows are read by each of its row tiles)
+      const i32x4 rs = rsrc_advance(o.rsB, kt * kBK * 2);
+      dma_16i<0>(rs, o.b_off[0], base);
+      dma_16i<1024>(rs, o.b_off[1], base);
+      return;
+    }
     if constexpr (KF) {
       const i32x4 rs = rsrc_advance(o.rsB, kb);
       dma_16i_nt<0>(rs, o.b_off[0], base);
@@ -1565,13 +1583,17 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
     const int col = col32 + (q & 1) * 16 + 4 * (sl & 3);
     return kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
   };
+  // row-tile weights: row r's 16-byte chunk c (k = 8 c) at chunk c ^ swz_a(r) of its 64-byte row; the
+  // lane's chunk is kk * 2 + lane / 32, so the second 16-deep sub-step's address is the first's with
+  // bit 5 flipped
+  auto brow_rd = [&](int r) { return r * 64 + (((lane >> 5) ^ swz_a(r)) << 4); };
   int a_rd[2][2], b_rd[4];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) a_rd[kk][mb] = arow_rd(wm * 64 + mb * 32 + (lane & 31), kk);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) b_rd[nb] = krow_rd(bcol[nb]);
+  for (int nb = 0; nb < 4; ++nb) b_rd[nb] = BR ? brow_rd(bcol[nb] + (lane & 31)) : krow_rd(bcol[nb]);
   const int g0 = (wn * 4 + wm) * 16;
   int xa_rd[2], xb_rd;
 #pragma unroll
@@ -1580,6 +1602,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
     const int kr = (q >> 1) * 8 + (sl >> 2);
     const int col = (q & 1) * 128 + g0 + 4 * (sl & 3);
     xb_rd = kr * 512 + (((col >> 3) ^ swz_b(kr)) << 4) + (col & 7) * 2;
+  } else if constexpr (BR) {
+    xb_rd = brow_rd(wn * 128 + wm * 32 + (lane & 31));
   } else {
     xb_rd = krow_rd(wn * 128 + wm * 32);
   }
@@ -1589,6 +1613,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
     bf16x8 a[2], b[4], xa[2], xb;
   };
   auto frag_b = [&](const uint8_t* base, int rd, int kk) -> bf16x8 {
+    if constexpr (BR) return *reinterpret_cast<const bf16x8*>(base + (rd ^ (kk << 5)));
     const uint8_t* p = base + rd + kk * 8192;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2048));
@@ -1896,6 +1921,13 @@ static void launch_fwd(GemmArgs g, hipStream_t s) {
                        g);
 }
 
+// the persistent kernel with row-tile weights (K a multiple of four K steps)
+static void launch_fwd_rows(GemmArgs g, hipStream_t s) {
+  const int64_t grid = std::max(8, cu_count() / 8 * 8);
+  hipLaunchKernelGGL((grouped_gemm_fwd_kernel<kEpiStore, false, true, true>), dim3((unsigned)grid), dim3(kGemmThreads),
+                     0, s, g);
+}
+
 template <bool A_ROWS, bool B_ROWS, int EPI>
 static void launch_generic(GemmArgs g, int64_t grid, hipStream_t s) {
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<A_ROWS, B_ROWS, EPI>), dim3(round_up8(grid)), dim3(kGemmThreads), 0, s,
@@ -2004,7 +2036,10 @@ hipError_t launch_gemm_gate_up_bwd(const void* d_gu, const void* gate_up, int N,
   g.b_expert = (int64_t)H * 2 * I;
   g.b_rows = H;
   g.ntiles_n = (H + kBN - 1) / kBN;
-  launch_generic<true, true, kEpiStore>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
+  if ((2 * I) % (kStages * kBK) == 0)
+    launch_fwd_rows(g, s);
+  else
+    launch_generic<true, true, kEpiStore>(g, row_tiles_bound(N, E) * g.ntiles_n, s);
   return hipGetLastError();
 }
 
