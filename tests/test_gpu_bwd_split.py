@@ -108,3 +108,27 @@ def test_overlapped_backward(T, H, I, E, k, shared, renorm, cus):
     ref64 = oracle.moe_backward(d["x"], d["gate_up"], d["down"], k, d["d_out"], w_gate=d["w_gate"], renorm=renorm,
                                 shared_gate_up=d.get("shared_gate_up"), shared_down=d.get("shared_down"), experts=[])
     assert rel_err(host(got.d_x), ref64["d_x"]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("counts,H,I", [([0, 300, 1, 0, 257, 142, 640, 33], 200, 64), ([290, 0, 17, 700], 520, 128),
+                                        ([256] * 12 + [0, 321], 264, 192)])
+def test_gate_up_bwd_row_tile_weights(counts, H, I):
+    """dX = dGU gate_up_e^T with 2I a multiple of 128 runs on the persistent kernel with the weights
+    staged as row tiles: empty experts, 1-row, band (257-320-row) and multi-row-tile experts, and an
+    H that is not a multiple of the 256-column tile. Against the oracle's input gradient."""
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    xp = normal((N, H), 1.0, (1311, N, H), "bf16")
+    gu = normal((E * H, 2 * I), 0.08, (1312, E, H, I), "bf16")
+    dn = normal((E * I, H), 0.08, (1313, E, H, I), "bf16")
+    d_y = normal((N, H), 1.0, (1314, N, H), "bf16")
+    offs = dev(offsets)
+    gu_saved = torch.empty((N, 2 * I), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), offs, gu_saved=gu_saved)
+    d_gu = moe.moe_grouped_gemm_down_bwd(dev(d_y), dev(dn), gu_saved, offs)
+    d_xp = torch.full((N + 3, H), 5.0, dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm_gate_up_bwd(d_gu, dev(gu), offs, d_x_perm=d_xp[:N])
+    ref_dx, _ = oracle.expert_rows_bwd(xp, d_y, offsets, gu, dn, want_gu=True)
+    assert rel_err(host(d_xp[:N]), ref_dx) <= TOL["bf16"]
+    assert np.all(as64(host(d_xp[N:])) == 5.0)
