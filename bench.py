@@ -527,7 +527,7 @@ def main():
     roof["traffic"] = load_traffic(wl.name, "gathered" if gather else "x_perm")
     if tdt == torch.bfloat16 and H % 8 == 0 and I % 8 == 0:
         kf = "true" if H % 128 == 0 else "false"   # K = H a multiple of four K steps
-        roof["kernel"] = f"grouped_gemm_fwd_kernel<0, {'true' if gather else 'false'}, {kf}> (gate_up + SwiGLU)"
+        roof["kernel"] = f"grouped_gemm_fwd_kernel<0, {'true' if gather else 'false'}, {kf}, false> (gate_up + SwiGLU)"
     else:
         roof["kernel"] = "gen_ffn1_kernel (gate_up + SwiGLU, generic path)"
     roof["algorithmic_bytes"] = gu_bytes
