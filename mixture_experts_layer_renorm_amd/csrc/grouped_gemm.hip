@@ -716,19 +716,15 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
 // in-order counter per wave, so if one wave did both, waiting for a K step's loads would also
 // wait for the previous tile's stores; split this way the stores of tile i drain while tile i+1
 // loads and computes. During the last three K steps of a tile the DMAs for the first three steps
-// of the next tile are issued. The epilogue is staged through ring slot 3 (sA3 = rows 0-31,
-// sB3 = rows 32-63 of a 64-row quarter): slot 3 held the last K step, which every wave has read
-// by that step's barrier, while slots 0-2 already receive the next tile's first steps. Per
-// quarter, the two waves of that 64-row band write their accumulators as bf16 (16-byte chunk c
-// of row r at chunk position c ^ (r & 31), so the 32 rows of one write fall on different banks);
-// after a barrier the store waves copy the quarter out as whole 512-byte rows, two rows (1 KB)
-// per buffer store, and a second barrier frees the staging area.
+// of the next tile are issued. The epilogue (wgrad_store_tile) is staged through the two 16 KB
+// halves of ring slot 3: slot 3 held the last K step, which every wave has read by that step's
+// barrier, while slots 0-2 already receive the next tile's first steps.
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 constexpr int kWgLoaders = 4;                              // waves 0-3 load, waves 4-7 store
 constexpr int kWgDmaA = kTileA / 1024 / kWgLoaders;        // DMA instructions per loader per step
 constexpr int kWgDmaB = kTileB / 1024 / kWgLoaders;
 constexpr int kWgDma = kWgDmaA + kWgDmaB;
-constexpr int kWgRowsPerStore = 64 / (kWaves - kWgLoaders) / 2;  // 1 KB stores per store wave per quarter
+constexpr int kWgStoresPerEighth = 32 / (kWaves - kWgLoaders) / 2;  // 1 KB stores per store wave per 32 rows
 
 constexpr int kMaxExperts = 1024;  // the library's limit on E (checked on the host)
 typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -777,6 +773,70 @@ __device__ __forceinline__ int unit_expert(const int* s_pref, int E, int u) {
       hi = mid;
   }
   return __builtin_amdgcn_readfirstlane(lo);
+}
+
+// Epilogue of a weight-gradient tile: rows m0 .. m0 + 255, columns n0 .. n0 + 255 of dW_e (rsC),
+// through two free 16 KB LDS buffers, in eighths of 32 rows. Eighth i (rows 32 i ..) is held by the
+// waves with wm = i / 2, accumulator half i % 2. While its owners write eighth i + 1 into one buffer
+// as bf16 rows (16-byte chunk c of row r at chunk position c ^ r, so the 32 rows of one write fall on
+// different banks), the store waves copy eighth i out of the other as whole 512-byte rows, two rows
+// (1 KB) per buffer store, non-temporal (the gradients are not re-read); one barrier per eighth. A
+// lane's accumulator holds 4-column runs of one row: lanes l and l + 32 hold the two halves of each
+// 8-column chunk, and one v_permlane32_swap per register pair gives every lane a whole 16-byte chunk
+// (of an even run pair on lanes 0-31, an odd one on lanes 32-63), written with one 16-byte LDS store.
+// Every wave of the workgroup calls it (one barrier per eighth, nine in all); the caller has made sure
+// that nothing else reads or writes the two buffers until it returns.
+template <bool LOADER>
+__device__ __forceinline__ void wgrad_store_tile(const f32x16 (&acc)[2][4], uint8_t* buf0, uint8_t* buf1,
+                                                 const __amdgpu_buffer_rsrc_t& rsC, int m0, int n0, int M, int N,
+                                                 int ldc, int wave, int lane, int wm, int wn) {
+  int z;  // (lane offsets computed here, not hoisted out of the caller's tile loop)
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  const int lr = (lane & 31) + z;
+  // round to bf16 first: 64 packed registers stay live through the eighths, not 128
+  u32x4 pw[2][4][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const uint32_t x0 = pack_bf16x2(acc[mb][nb][gp * 8 + 0], acc[mb][nb][gp * 8 + 1]);
+        const uint32_t x1 = pack_bf16x2(acc[mb][nb][gp * 8 + 2], acc[mb][nb][gp * 8 + 3]);
+        const uint32_t y0 = pack_bf16x2(acc[mb][nb][gp * 8 + 4], acc[mb][nb][gp * 8 + 5]);
+        const uint32_t y1 = pack_bf16x2(acc[mb][nb][gp * 8 + 6], acc[mb][nb][gp * 8 + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        pw[mb][nb][gp] = u32x4{(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
+      }
+#pragma unroll
+  for (int e8 = -1; e8 < 8; ++e8) {
+    if (e8 + 1 < 8 && wm == ((e8 + 1) >> 1)) {  // stage eighth e8 + 1
+      uint8_t* rowp = (((e8 + 1) & 1) ? buf1 : buf0) + lr * 512;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int chunk = (wn * 16 + nb * 4 + gp * 2 + (lane >> 5)) ^ lr;
+          *reinterpret_cast<u32x4*>(rowp + (chunk << 4)) = pw[(e8 + 1) & 1][nb][gp];
+        }
+    }
+    if constexpr (!LOADER) {
+      if (e8 >= 0) {  // store eighth e8
+        const uint8_t* sp = (e8 & 1) ? buf1 : buf0;
+#pragma unroll
+        for (int j = 0; j < kWgStoresPerEighth; ++j) {
+          const int r = ((wave - kWgLoaders) * kWgStoresPerEighth + j) * 2 + (lane >> 5) + z;
+          const int c = lane & 31;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sp + r * 512 + ((c ^ r) << 4));
+          const int m = m0 + e8 * 32 + r, col = n0 + c * 8;
+          const int off = (m < M && col < N) ? (m * ldc + col) * 2 : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 2);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
 }
 
 struct WgTile {
@@ -948,55 +1008,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmA
       }
       meet();
     };
-    // Epilogue (see above). The lane offsets are built from a value the compiler cannot see
-    // through, so that they are computed here instead of being hoisted out of the tile loop.
+    // Epilogue: the previous tile's stores are waited for first (the store waves' counter then
+    // holds only this tile's), then wgrad_store_tile through ring slot 3.
     auto store = [&](const WgTile& w) {
-      int z;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-      const int lr = (lane & 31) + z;
-      const int wr_lo = lr * 512 + (lane >> 5) * 8;  // row lr, half-chunk lane / 32
       const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(g.C + (int64_t)w.e * g.c_expert), (short)0, g.M * g.N * 2, kBufferWord3);
-      if constexpr (!LOADER) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the previous tile's stores
-      // round to bf16 first: the quarter loop then keeps 64 packed registers live, not 128
-      uint2 pk[2][4][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            pk[mb][nb][gq] = make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
-                                        pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
-#pragma unroll 1
-      for (int qb = 0; qb < 4; ++qb) {
-        if (wm == qb) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            uint8_t* rowp = (mb == 0 ? sA3 : sB3) + wr_lo;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-              for (int gq = 0; gq < 4; ++gq) {
-                const int chunk = (wn * 16 + nb * 4 + gq) ^ lr;
-                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = pk[mb][nb][gq];
-              }
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if constexpr (!LOADER) {
-#pragma unroll
-          for (int j = 0; j < kWgRowsPerStore; ++j) {
-            const int r = ((wave - kWgLoaders) * kWgRowsPerStore + j) * 2 + (lane >> 5) + z;
-            const int c = lane & 31;
-            const u32x4 v = *reinterpret_cast<const u32x4*>((r < 32 ? sA3 : sB3) + (r & 31) * 512 + ((c ^ (r & 31)) << 4));
-            const int m = w.m0 + qb * 64 + r, col = w.n0 + c * 8;
-            const int off = (m < g.M && col < g.N) ? (m * g.ldc + col) * 2 : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 2);  // nt: gradients are not re-read
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
+      if constexpr (!LOADER) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wgrad_store_tile<LOADER>(acc, sA3, sB3, rsC, w.m0, w.n0, g.M, g.N, g.ldc, wave, lane, wm, wn);
     };
 
     int t = t0;
@@ -1136,54 +1154,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_res_kernel(const G
         asm volatile("s_barrier" ::: "memory");
       }
     };
-    // epilogue of tile nt into staging slots st0 (rows 0-31 of a 64-row quarter), st1 (32-63)
+    // epilogue of tile nt through the free ring slots st0 and st1
     auto store = [&](int nt, uint8_t* st0, uint8_t* st1) {
-      int z;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-      const int lr = (lane & 31) + z;
-      const int wr_lo = lr * 512 + (lane >> 5) * 8;
       const __amdgpu_buffer_rsrc_t rsC = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(g.C + (int64_t)e * g.c_expert), (short)0, g.M * g.N * 2, kBufferWord3);
       if constexpr (!LOADER) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      uint2 pk[2][4][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            pk[mb][nb][gq] = make_uint2(pack_bf16x2(acc[mb][nb][gq * 4 + 0], acc[mb][nb][gq * 4 + 1]),
-                                        pack_bf16x2(acc[mb][nb][gq * 4 + 2], acc[mb][nb][gq * 4 + 3]));
-      const int n0 = nt * kBN;
-#pragma unroll 1
-      for (int qb = 0; qb < 4; ++qb) {
-        if (wm == qb) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            uint8_t* rowp = (mb == 0 ? st0 : st1) + wr_lo;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-              for (int gq = 0; gq < 4; ++gq) {
-                const int chunk = (wn * 16 + nb * 4 + gq) ^ lr;
-                *reinterpret_cast<uint2*>(rowp + (chunk << 4)) = pk[mb][nb][gq];
-              }
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if constexpr (!LOADER) {
-#pragma unroll
-          for (int j = 0; j < kWgRowsPerStore; ++j) {
-            const int r = ((wave - kWgLoaders) * kWgRowsPerStore + j) * 2 + (lane >> 5) + z;
-            const int c = lane & 31;
-            const u32x4 v = *reinterpret_cast<const u32x4*>((r < 32 ? st0 : st1) + (r & 31) * 512 + ((c ^ (r & 31)) << 4));
-            const int m = m0 + qb * 64 + r, col = n0 + c * 8;
-            const int off = (m < g.M && col < g.N) ? (m * g.ldc + col) * 2 : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rsC, off, 0, 2);  // nt: gradients are not re-read
-          }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
+      wgrad_store_tile<LOADER>(acc, st0, st1, rsC, m0, nt * kBN, g.M, g.N, g.ldc, wave, lane, wm, wn);
     };
 
     for (int u = u0; u < u_end; u += stride) {
