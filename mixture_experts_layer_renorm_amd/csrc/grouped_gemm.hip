@@ -680,25 +680,61 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(const G
     }
     return;
   }
-  // SwiGLU backward: dG | dU from the accumulators and the saved g, u (8-byte pieces, read and written)
+  // SwiGLU backward: dG | dU from the accumulators and the saved g, u (read in 8-byte pieces), staged
+  // like the plain store, in two rounds (accumulator half mb = 0, then 1): each wave writes dG of its
+  // 32 rows into 16 KB block wm and dU into block 4 + wm, then wave w copies block w out as whole
+  // 512-byte rows (dG into columns [0, N), dU into [N, 2N)).
   if constexpr (EPI == kEpiSwigluBwd) {
+    auto blk = [&](int j) -> uint8_t* {
+      return j == 0 ? sA0 : j == 1 ? sA0 + 16384 : j == 2 ? sA1 : j == 3 ? sA1 + 16384 : j == 4 ? sB0 : j == 5 ? sB1 : j == 6 ? sB2 : sB3;
+    };
+    const int lr = lane & 31, c = lane & 31;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int mloc = wm * 64 + mb * 32 + (lane & 31);
-      if (mloc >= mvalid) continue;
-      const int64_t m = m0 + mloc;
+      asm volatile("s_barrier" ::: "memory");  // the operand buffers (or the previous round's rows) are free
+      const int mloc = wm * 64 + mb * 32 + lr;
+      const uint16_t* gr = g.gu + (int64_t)(m0 + min(mloc, max(mvalid - 1, 0))) * 2 * g.N;
+      uint8_t* sg_ = blk(wm) + lr * 512 + (lane >> 5) * 8;
+      uint8_t* su_ = blk(4 + wm) + lr * 512 + (lane >> 5) * 8;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int col = n0 + wn * 128 + nb * 32 + gq * 8 + (lane >> 5) * 4;
-          if (col >= g.N) continue;
-          float v[4];
+          uint2 gp = make_uint2(0u, 0u), up = make_uint2(0u, 0u);
+          if (mloc < mvalid && col < g.N) {
+            gp = *reinterpret_cast<const uint2*>(gr + col);
+            up = *reinterpret_cast<const uint2*>(gr + g.N + col);
+          }
+          const float gv[4] = {bf16_to_f32(gp.x & 0xffffu), bf16_to_f32(gp.x >> 16), bf16_to_f32(gp.y & 0xffffu),
+                               bf16_to_f32(gp.y >> 16)};
+          const float uv[4] = {bf16_to_f32(up.x & 0xffffu), bf16_to_f32(up.x >> 16), bf16_to_f32(up.y & 0xffffu),
+                               bf16_to_f32(up.y >> 16)};
+          float dg[4], du[4];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) v[qq] = acc[mb][nb][gq * 4 + qq];
-          store_swiglu_bwd(g, g.C, m, col, v);
+          for (int qq = 0; qq < 4; ++qq) {
+            const float v = acc[mb][nb][gq * 4 + qq];
+            const float sg = sigmoid_f(gv[qq]);
+            dg[qq] = v * uv[qq] * sg * (1.0f + gv[qq] * (1.0f - sg));
+            du[qq] = v * gv[qq] * sg;
+          }
+          const int chunk = (wn * 16 + nb * 4 + gq) ^ lr;
+          *reinterpret_cast<uint2*>(sg_ + (chunk << 4)) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(su_ + (chunk << 4)) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const uint8_t* src = blk(wave);
+      const int wb = wave & 3, coff = wave < 4 ? 0 : g.N;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 2 * i + (lane >> 5);
+        const int ml = wb * 64 + mb * 32 + r, col = n0 + c * 8;
+        if (ml < mvalid && col < g.N) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + r * 512 + ((c ^ r) << 4));
+          *reinterpret_cast<uint4*>(g.C + (int64_t)(m0 + ml) * g.ldc + coff + col) = v;
         }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 }
