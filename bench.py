@@ -142,23 +142,38 @@ def cpu_baseline(wl, d, budget_s: float):
             "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
-def tile_schedule(counts, N_cols, bm=320, bn=256, xcds=8, cus=256, sort_max_e=256):
+def tile_schedule(counts, N_cols, bm=320, bm_min=256, bn=256, xcds=8, cus=256, sort_max_e=256):
     """The persistent forward GEMMs' tile list and walk as the kernel derives them on the device: an
-    expert with c rows gets n = ceil(c / bm) row tiles of near-equal height (none when c = 0), each
-    with ceil(N_cols / bn) column tiles. With whole rounds on every XCD (or more than four rounds on
-    average) XCD x takes the contiguous eighth of the list in expert order; otherwise ("balance")
-    the experts are listed tallest first (ties by index, up to sort_max_e experts) and row tile R
-    goes to XCD R mod 8. Each XCD deals its tiles to its cus / 8 workgroups in rounds, back and
-    forth. Returns per-expert tile counts, per-XCD tile counts and row-tile work (rows x columns),
-    the most tiles any workgroup runs, and whether the walk balanced."""
+    expert with c rows gets n = ceil(c / hm) row tiles of near-equal height (none when c = 0), each
+    with ceil(N_cols / bn) column tiles; hm = bm, or (one expert) bm_min when that list differs, takes
+    as many rounds, and either only it splits into whole rounds on every XCD or there are two or more.
+    With whole rounds on every XCD (or more
+    than four rounds on average) XCD x takes the contiguous eighth of the list in expert order;
+    otherwise ("balance") the experts are listed tallest first (ties by index, up to sort_max_e
+    experts) and row tile R goes to XCD R mod 8. Each XCD deals its tiles to its cus / 8 workgroups
+    in rounds, back and forth. Returns per-expert tile counts, per-XCD tile counts and row-tile work
+    (rows x columns), the most tiles any workgroup runs, and whether the walk balanced."""
     ntn = (N_cols + bn - 1) // bn
-    rt = [(c + bm - 1) // bm if c > 0 else 0 for c in counts]
-    height = [(c + r - 1) // r if r > 0 else 0 for c, r in zip(counts, rt)]
     G = max(8, cus // 8 * 8)
     nbx = G // xcds
+
+    def row_tiles_at(h):
+        return [(c + h - 1) // h if c > 0 else 0 for c in counts]
+
+    def whole_rounds(RT):
+        return RT % xcds == 0 and (RT // xcds * ntn) % nbx == 0
+
+    def rounds(RT):
+        return (RT * ntn + G - 1) // G
+
+    rx, rb = sum(row_tiles_at(bm)), sum(row_tiles_at(bm_min))
+    hm = bm_min if (len(counts) == 1 and rb != rx and rounds(rb) == rounds(rx) and
+                    ((whole_rounds(rb) and not whole_rounds(rx)) or rounds(rx) >= 2)) else bm
+    rt = row_tiles_at(hm)
+    height = [(c + r - 1) // r if r > 0 else 0 for c, r in zip(counts, rt)]
     RT = sum(rt)
     total = RT * ntn
-    whole = RT % xcds == 0 and (RT // xcds * ntn) % nbx == 0
+    whole = whole_rounds(RT)
     balance = not whole and total <= 4 * G
     order = (sorted(range(len(counts)), key=lambda e: (-height[e], e))
              if balance and len(counts) <= sort_max_e else list(range(len(counts))))
@@ -180,7 +195,8 @@ def tile_schedule(counts, N_cols, bm=320, bn=256, xcds=8, cus=256, sort_max_e=25
             "empty_experts": int(sum(1 for c in counts if c == 0)),
             "tiles_of_empty_experts": int(sum(r * ntn for r, c in zip(rt, counts) if c == 0)),
             "tiles_per_xcd": per_xcd, "xcd_work_max_over_mean": round(max(work) / mean_w, 4) if mean_w else None,
-            "workgroup_tiles_max": max((n + nbx - 1) // nbx for n in per_xcd), "balanced_walk": balance}
+            "workgroup_tiles_max": max((n + nbx - 1) // nbx for n in per_xcd), "balanced_walk": balance,
+            "tile_rows_max": hm}
 
 
 def pct(a, q):

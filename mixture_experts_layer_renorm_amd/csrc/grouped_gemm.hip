@@ -1335,23 +1335,41 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = (wave >> 1) & 3, wn = wave & 1;
 
-  // ---- the tile list: expert e owns n_e = ceil(c_e / kBMX) row tiles of near-equal height (at
-  // most h_e = ceil(c_e / n_e) rows), each with ntiles_n column tiles; s_pref = exclusive prefix of
-  // the row tiles over the list. The experts are listed in index order, or tallest first (ties by
-  // index) when the walk below balances (and there are at most kSortMaxE experts).
+  // ---- the tile list: expert e owns n_e = ceil(c_e / hm) row tiles of near-equal height (at most
+  // h_e = ceil(c_e / n_e) rows), each with ntiles_n column tiles; s_pref = exclusive prefix of the
+  // row tiles over the list. The tile height limit hm is kBMX (band tiles: fewest row tiles), or, for
+  // one expert (a dense product, whose weights every row tile reads whichever the height), kBM when
+  // the kBM list takes as many rounds of the grid and either only it splits into whole rounds on
+  // every XCD (see the walk below) or there are two or more. E.g. 4096 rows with 16 column tiles on
+  // 256 workgroups: 256 tiles of 256 rows instead of 208 of 315 (a fifth of the chip idle, each tile a
+  // fifth more work); with 28 column tiles, two rounds either way: 11-15 % faster measured. Not for
+  // several experts: one split into more row tiles streams its weights into more XCDs (one
+  // expert-parallel rank's Zipf share: 14 % slower with kBM in its two rounds).
+  // The experts are listed in index order, or tallest first (ties by index) when the walk below
+  // balances (and there are at most kSortMaxE experts).
+  const int ntn = g.ntiles_n;
+  const int nbx = (int)(gridDim.x >> 3);  // workgroups per XCD (the grid is a multiple of 8)
   for (int i = tid; i <= g.E; i += kGemmThreads) s_off[i] = g.offsets[i];
   __syncthreads();
+  int hm = kBMX;
+  if (g.E == 1) {  // one expert: a dense product
+    auto whole_rounds = [&](int rt) { return (rt & 7) == 0 && ((rt >> 3) * ntn) % nbx == 0; };
+    const int c = __builtin_amdgcn_readfirstlane(s_off[1] - s_off[0]), G = (int)gridDim.x;
+    const int rt_x = (c + kBMX - 1) / kBMX, rt_b = (c + kBM - 1) / kBM;
+    const int rounds_x = (rt_x * ntn + G - 1) / G, rounds_b = (rt_b * ntn + G - 1) / G;
+    if (c > 0 && rt_b != rt_x && rounds_b == rounds_x &&
+        ((whole_rounds(rt_b) && !whole_rounds(rt_x)) || rounds_x >= 2))
+      hm = kBM;
+  }
   for (int i = tid; i < g.E; i += kGemmThreads) {
     const int c = s_off[i + 1] - s_off[i];
     s_ord[i] = (short)i;
-    s_pref[i] = c > 0 ? (c + kBMX - 1) / kBMX : 0;
+    s_pref[i] = c <= 0 ? 0 : hm == kBM ? (c + kBM - 1) / kBM : (c + kBMX - 1) / kBMX;
   }
   __syncthreads();
   block_exclusive_scan<kGemmThreads>(s_pref, g.E, s_wtot);
-  const int ntn = g.ntiles_n;
   const int RT = __builtin_amdgcn_readfirstlane(s_pref[g.E]);  // row tiles in the list
   const int total = RT * ntn;
-  const int nbx = (int)(gridDim.x >> 3);  // workgroups per XCD (the grid is a multiple of 8)
   // The walk deals each XCD's tiles to its nbx workgroups in rounds. With whole rounds on every XCD,
   // or more than four rounds on average, XCD x takes the contiguous eighth [x Q, (x + 1) Q) of the
   // list in index order, Q = ceil(tiles / 8): an expert's row tiles share one XCD's L2 (its weights
@@ -1366,7 +1384,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
     __syncthreads();  // every thread has read the row-tile total
     if (tid < g.E) {
       const int c = s_off[tid + 1] - s_off[tid];
-      const int n = c > 0 ? (c + kBMX - 1) / kBMX : 0;
+      const int n = c <= 0 ? 0 : hm == kBM ? (c + kBM - 1) / kBM : (c + kBMX - 1) / kBMX;
       s_pref[tid] = n > 0 ? (c + n - 1) / n : 0;
     }
     __syncthreads();
@@ -1390,7 +1408,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_fwd_kernel(const Ge
     if (tid < g.E) {
       const int e = s_ord[tid];
       const int c = s_off[e + 1] - s_off[e];
-      s_pref[tid] = c > 0 ? (c + kBMX - 1) / kBMX : 0;
+      s_pref[tid] = c <= 0 ? 0 : hm == kBM ? (c + kBM - 1) / kBM : (c + kBMX - 1) / kBMX;
     }
     __syncthreads();
     block_exclusive_scan<kGemmThreads>(s_pref, g.E, s_wtot);

@@ -128,3 +128,38 @@ def test_ffn_balanced_walk(E, N, H, I, key):
     assert rel_err(host(h), ra) <= TOL["bf16"]
     y2, h2 = moe.moe_grouped_swiglu_ffn_gather(dev(x), dev(sor), k, dev(gu), dev(dn), dev(offsets), N=N)
     assert np.array_equal(host(h2), host(h)) and np.array_equal(host(y2), host(y))
+
+
+@pytest.mark.parametrize("counts,H,I,short", [([4096], 64, 2048, True), ([4096], 7168, 64, True),
+                                              ([2048, 0, 2048], 64, 2048, False)])
+def test_tile_height_dense(counts, H, I, short):
+    """One expert (a dense product) takes 256-row tiles when they need no more rounds of the grid and
+    either split into whole rounds on every XCD where the 320-row list does not, or take two or more:
+    4096 rows with 16 column tiles are 256 tiles of 256 rows instead of 208 of 315; with 28 column
+    tiles 448 instead of 364, two rounds either way. Several experts keep 320-row tiles. Forward
+    (permuted and gathered rows) and the input gradient (row-tile weights) against the oracle."""
+    import bench
+    E = len(counts)
+    scheds = [bench.tile_schedule(counts, cols) for cols in (2 * I, H)]
+    assert any(s["tile_rows_max"] == 256 for s in scheds) == short
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    key = (1130, N, H, I, E)
+    x = normal((N, H), 1.0, key + (1,), "bf16")
+    sor = generator(key + (2,)).permutation(N).astype(np.int32)
+    xp = x[sor]
+    gu = normal((E * H, 2 * I), 0.05, key + (3,), "bf16")
+    dn = normal((E * I, H), 0.05, key + (4,), "bf16")
+    d_y = normal((N, H), 1.0, key + (5,), "bf16")
+    offs = dev(offsets)
+    gu_saved = torch.empty((N, 2 * I), dtype=torch.bfloat16, device="cuda")
+    y, h = moe.moe_grouped_swiglu_ffn(dev(xp), dev(gu), dev(dn), offs, gu_saved=gu_saved)
+    ry, ra = oracle.expert_rows(xp, offsets, gu, dn, want_act=True)
+    assert rel_err(host(y), ry) <= TOL["bf16"]
+    assert rel_err(host(h), ra) <= TOL["bf16"]
+    y2, h2 = moe.moe_grouped_swiglu_ffn_gather(dev(x), dev(sor), 1, dev(gu), dev(dn), offs, N=N)
+    assert torch.equal(h2, h) and torch.equal(y2, y)
+    d_gu = moe.moe_grouped_gemm_down_bwd(dev(d_y), dev(dn), gu_saved, offs)
+    d_xp = moe.moe_grouped_gemm_gate_up_bwd(d_gu, dev(gu), offs)
+    ref_dx, _ = oracle.expert_rows_bwd(xp, d_y, offsets, gu, dn, want_gu=True)
+    assert rel_err(host(d_xp), ref_dx) <= TOL["bf16"]
