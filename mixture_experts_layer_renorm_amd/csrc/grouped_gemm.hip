@@ -954,7 +954,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_wgrad_kernel(const GemmA
   };
 
   // The whole walk, once per role, so that each role's loop is scheduled on its own. Both roles
-  // meet the same barriers in the same order: one per K step, two per epilogue quarter.
+  // meet the same barriers in the same order: one per K step, nine per epilogue.
   auto walk = [&](auto loader_tag) {
     constexpr bool LOADER = decltype(loader_tag)::value;
     const int lw = wave & (kWgLoaders - 1);
