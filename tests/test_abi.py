@@ -104,6 +104,22 @@ def test_grouped_ffn_rejects(lib):
     assert lib.moe_grouped_swiglu_ffn(*args) == moe.MOE_ERR_INVALID_ARG           # H = 0
 
 
+def test_router_logits_bwd_checks(lib):
+    fake = ctypes.c_void_p(64)  # never dereferenced
+    # nothing to compute, bad dtype, E out of range, null inputs with tokens
+    assert lib.moe_router_logits_bwd(fake, fake, fake, moe.MOE_BF16, 4, 8, 4, None, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert "nothing to compute" in err(lib)
+    assert lib.moe_router_logits_bwd(fake, fake, fake, 7, 4, 8, 4, fake, None, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_logits_bwd(fake, fake, fake, moe.MOE_BF16, 4, 8, 0, fake, None, fake, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_logits_bwd(None, fake, fake, moe.MOE_BF16, 4, 8, 4, fake, None, fake, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert "null" in err(lib)
+    # no tokens and no weight gradient asked for: d_x has no rows, nothing is launched
+    assert lib.moe_router_logits_bwd(None, None, None, moe.MOE_BF16, 0, 8, 4, None, None, fake, None) == moe.MOE_OK
+
+
 def test_combine_rejects(lib):
     assert lib.moe_unpermute_combine(None, moe.MOE_BF16, 4, 8, 33, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_unpermute_combine(None, moe.MOE_BF16, 4, 8, 2, None, None, None, None, None) == moe.MOE_ERR_INVALID_ARG
